@@ -1,0 +1,39 @@
+"""Byte counts for the decode step (pure arithmetic, no device code).
+
+KV bytes per token across the model: 2 (K and V) x layers x KV heads x head
+dim x bytes per element (vLLM's PagedAttention: How Memory Management
+Supports Large Model Inference, "2.1"; Batching and PagedAttention, "Quick
+Reference", bytes per block).  The decode metric counts one layer: every
+valid token's K and V row once per KV head.
+"""
+
+from __future__ import annotations
+
+ELEM_BYTES = {"fp32": 4, "fp16": 2, "bf16": 2}
+
+
+def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
+    return 2 * num_layers * num_kv_heads * head_dim * elem_bytes
+
+
+def block_bytes(block_size: int, num_layers: int, num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
+    return block_size * kv_bytes_per_token(num_layers, num_kv_heads, head_dim, elem_bytes)
+
+
+def decode_kv_bytes(context_lens, num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
+    """Algorithmic K+V bytes one decode launch must read (one layer)."""
+    return int(sum(int(L) for L in context_lens)) * kv_bytes_per_token(1, num_kv_heads, head_dim, elem_bytes)
+
+
+def decode_io_bytes(context_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                    elem_bytes: int, block_size: int = 16) -> int:
+    """KV bytes plus q read, out written, table entries and lengths read."""
+    B = len(context_lens)
+    table = sum(4 * (-(-int(L) // block_size)) for L in context_lens)
+    return (decode_kv_bytes(context_lens, num_kv_heads, head_dim, elem_bytes)
+            + 2 * B * num_q_heads * head_dim * elem_bytes + table + 4 * B)
+
+
+def write_kv_bytes(num_tokens: int, num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
+    """New K/V rows read and written, plus the int64 slots."""
+    return num_tokens * (2 * 2 * num_kv_heads * head_dim * elem_bytes + 8)
