@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark: one paged decode step per iteration on one MI355X.
+
+A step is the whole device path of a decode step for the batch: copy-on-write
+block copies (when the step has any), the write of every sequence's new K/V
+into its slot, then paged decode attention over each sequence's context
+including that token.  The host block-manager work that produces the slots,
+tables and copy pairs runs once per configuration and is timed separately.
+
+HBM honesty: the step rotates over several independent sets of (pools,
+tables, q, out) whose combined size is several times the 256 MB Infinity
+Cache, so each step's KV comes from HBM.
+
+Prints ONE JSON line (rank 0, N=1):
+  value  = algorithmic KV bytes of the step / step time, in GB/s
+  roofline = pa_decode's achieved algorithmic GB/s vs the 8 TB/s HBM peak,
+             per-launch time measured with HIP events on the launch stream
+  cpu_baseline = the fp64 oracle on the host, same algorithmic bytes
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+METRIC = "paged decode attention KV-read GB/s (% of MI355X HBM peak); seq-steps/s"
+WORKLOAD_NAMES = {
+    "c1": "tiny paged decode fp32 (4 seqs, L in {1,5,16,37}, Hq=Hkv=2, D=64)",
+    "c2": "Llama-3.1-8B decode layer bf16 (B=64, Hq=32, Hkv=8, D=128, L~U[128,4096], block 16)",
+    "c3": "OPT-13B MHA decode layer fp16 (B=256, H=40, D=128, L~U[64,2048], block 16)",
+    "c4": "parallel-sampling prefix share bf16 (32 prompts x 8 samples, prefix 1024, tails U[0,512])",
+    "c4b": "fork step bf16 (32 prompts x 8 samples, prefix 1000, copy-on-write of the partial block)",
+    "c5": "Qwen2.5-72B decode layer fp16 (B=128, Hq=64, Hkv=8, D=128, L~U[4096,8192], 512-token partitions)",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = enough for >= 2 GiB)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--placement", choices=["shuffled", "sequential"], default="shuffled")
+    return ap.parse_args()
+
+
+def cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline(w, tables, budget_s):
+    """The oracle as it stands, on whole-batch passes of the same step, for ~budget_s."""
+    import oracle  # test infrastructure: only this leg of the bench uses it
+    from paged_kv_cache_117_amd import metrics
+
+    eb = metrics.ELEM_BYTES[w.dtype]
+    k, v = w.k_pool, w.v_pool
+    # as many leading sequences as fit the budget (one timed probe sequence first)
+    t0 = time.perf_counter()
+    oracle.decode(w.q[:1], k, v, tables[:1], w.context_lens[:1], w.scale, w.dtype)
+    per_tok = (time.perf_counter() - t0) / max(1, int(w.context_lens[0]))
+    total_tok = int(w.context_lens.sum())
+    reps = 1
+    rows = w.num_seqs
+    if per_tok * total_tok > budget_s:
+        acc = 0
+        rows = 0
+        for L in w.context_lens:
+            if (acc + int(L)) * per_tok > budget_s and rows > 0:
+                break
+            acc += int(L)
+            rows += 1
+    else:
+        reps = max(1, int(budget_s / max(per_tok * total_tok, 1e-9)))
+        reps = min(reps, 20)
+    sel = slice(0, rows)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.decode(w.q[sel], k, v, tables[sel], w.context_lens[sel], w.scale, w.dtype)
+    dt = (time.perf_counter() - t0) / reps
+    kvb = metrics.decode_kv_bytes(w.context_lens[sel], w.num_kv_heads, w.head_dim, eb)
+    return {
+        "value": round(kvb / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle decode (gather + two-pass softmax) over the first {rows} of "
+                   f"{w.num_seqs} sequences x {reps} pass(es), {dt:.3f} s per pass; "
+                   f"seq-steps/s {rows / dt:.2f}; host CPU: {cpu_info()}"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path has no "
+              "multi-GPU mode: sequences or KV heads shard across GPUs with no exchange inside "
+              "attention, so run one process per GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_117_amd as pa
+    from paged_kv_cache_117_amd import metrics
+    from workloads import make_workload
+
+    torch.cuda.set_device(0)
+    w = make_workload(args.config)
+    eb = metrics.ELEM_BYTES[w.dtype]
+    tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+
+    # ---- host block-manager work (H0): replay, then this step's appends --------
+    order = w.perm if args.placement == "shuffled" else np.arange(w.num_blocks, dtype=np.int32)
+    bm = pa.BlockManager(w.num_blocks, w.block_size, order)
+    bm.replay(w.ops)
+    t0 = time.perf_counter()
+    slots = bm.append_batch(w.seq_ids)
+    pairs = bm.take_copies_array()
+    tables = bm.tables(w.seq_ids, w.max_blocks_per_seq)
+    host_bm_ms = (time.perf_counter() - t0) * 1e3
+
+    # ---- device buffers: R rotating sets, each a private region of one pool --------
+    nb = w.num_blocks
+    pool_bytes = 2 * nb * w.num_kv_heads * w.block_size * w.head_dim * eb
+    R = args.sets or max(2, min(16, int(np.ceil(2 * 2**30 / pool_bytes))))
+
+    def dev(a, dtype=None):
+        a = np.ascontiguousarray(a)
+        if w.dtype == "bf16" and dtype == "kv":
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    k1 = dev(w.k_pool, "kv")
+    v1 = dev(w.v_pool, "kv")
+    k_pool = torch.empty((R * nb,) + tuple(k1.shape[1:]), dtype=tdt, device="cuda")
+    v_pool = torch.empty_like(k_pool)
+    for r in range(R):
+        k_pool[r * nb:(r + 1) * nb].copy_(k1)
+        v_pool[r * nb:(r + 1) * nb].copy_(v1)
+    del k1, v1
+    q = dev(w.q, "kv")
+    k_new = dev(w.k_new, "kv")
+    v_new = dev(w.v_new, "kv")
+    lens = dev(w.context_lens.astype(np.int32))
+    sets = []
+    for r in range(R):
+        t = np.where(tables >= 0, tables + r * nb, -1).astype(np.int32)
+        sets.append(dict(
+            tables=dev(t),
+            slots=dev(slots + r * nb * w.block_size),
+            pairs=dev((pairs + r * nb).astype(np.int32)) if len(pairs) else None,
+            out=torch.empty_like(q),
+            ws=torch.empty(max(1, pa.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.head_dim,
+                                                            w.max_context_len, args.partition_size)),
+                           dtype=torch.uint8, device="cuda"),
+        ))
+    stream = torch.cuda.current_stream()
+
+    def step(r, ev=None):
+        s = sets[r]
+        if s["pairs"] is not None:
+            pa.copy_blocks(k_pool, v_pool, s["pairs"], stream=stream)
+        pa.write_kv(k_pool, v_pool, k_new, v_new, s["slots"], stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.decode(q, k_pool, v_pool, s["tables"], lens, w.scale, w.max_context_len, out=s["out"],
+                  partition_size=args.partition_size, workspace=s["ws"], stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i % R)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i % R, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_step = total_ms / args.steps
+
+    kv_bytes = metrics.decode_kv_bytes(w.context_lens, w.num_kv_heads, w.head_dim, eb)
+    io_bytes = metrics.decode_io_bytes(w.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, eb)
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+    dec_avg = float(dec_ms.mean())
+    achieved = io_bytes / (dec_avg * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_NAMES[args.config],
+            "key": args.config,
+            "num_seqs": w.num_seqs,
+            "kv_bytes_per_step": kv_bytes,
+            "block_size": w.block_size,
+            "partition_size": args.partition_size or 512,
+            "placement": args.placement,
+            "rotating_sets": R,
+            "copy_pairs": int(len(pairs)),
+        },
+        "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
+        "seq_steps_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
+        "decode_ms": round(dec_avg, 5),
+        "decode_ms_median": round(float(np.median(dec_ms)), 5),
+        "decode_kv_gbps": round(kv_bytes / (dec_avg * 1e-3) / 1e9, 2),
+        "host_block_manager_ms": round(host_bm_ms, 3),
+        "wall_s": round(wall, 3),
+        "roofline": {
+            "kernel": "pa_decode",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, tables, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,215 @@
+/*
+ * pa.h -- C ABI of libpa: paged KV cache decode path for AMD MI355X (gfx950).
+ *
+ * The KV cache is a pool of fixed-size blocks; each sequence reaches its
+ * blocks through a block table that maps logical block j (positions
+ * 16j..16j+15) to a physical block id (PagedAttention and vLLM: Paging the
+ * KV Cache Like an OS, "Step 3: blocks and block tables"; PagedAttention
+ * (tensortonic), "4. Finding Tokens with a Block Table").
+ *
+ * Layouts (all row-major, C order):
+ *   K pool, V pool : [num_blocks][num_kv_heads][block_size][head_dim]  (two tensors)
+ *   q, out         : [num_seqs][num_q_heads][head_dim]
+ *   k_new, v_new   : [num_tokens][num_kv_heads][head_dim]
+ *   block_tables   : int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens   : int32 [num_seqs]
+ *   slot_mapping   : int64 [num_tokens], slot = block * block_size + offset
+ *   block_pairs    : int32 [num_pairs][2] = (src, dst)
+ * q, out, pools and new K/V share one element type (pa_dtype_t).  Query head
+ * h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ * Conventions for every device entry point:
+ *   - Pointers marked "device" are device addresses the caller allocated;
+ *     the library never allocates or frees them and keeps none after return.
+ *     Tensor base pointers must be 16-byte aligned.
+ *   - Work is enqueued on `stream` (a hipStream_t, NULL = the default
+ *     stream) and runs asynchronously.  The return code covers host-side
+ *     argument checks and the launch itself; faults surface at the caller's
+ *     next synchronisation.
+ *   - The contents of index arrays are the caller's contract (the block
+ *     manager below produces them).  The kernels still never access memory
+ *     outside the pools: an out-of-range slot or block pair is skipped, and
+ *     a sequence with an out-of-range length or block id gets NaN outputs.
+ *   - No exception crosses the ABI.  On a non-OK status, pa_last_error()
+ *     returns a message (thread-local, valid until the next call on that
+ *     thread).
+ *   - Arithmetic is float32 for every storage type.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_FP32 = 0, PA_FP16 = 1, PA_BF16 = 2 } pa_dtype_t;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range, misaligned pointer */
+  PA_ERR_UNSUPPORTED = 3, /* block_size != 16, head_dim not 64/128, bad dtype */
+  PA_ERR_WORKSPACE = 4,   /* workspace missing or too small */
+  PA_ERR_LAUNCH = 5,      /* the HIP runtime refused the launch */
+  PA_ERR_NO_BLOCKS = 6,   /* block manager: the free list cannot cover the request */
+  PA_ERR_NOT_FOUND = 7,   /* block manager: unknown sequence id */
+  PA_ERR_EXISTS = 8       /* block manager: sequence id already in use */
+} pa_status_t;
+
+/*
+ * pa_decode -- single-query decode attention through block tables.
+ *
+ * For each sequence s with L = context_lens[s] and each query head h
+ * (KV head j = h / g, g = num_q_heads / num_kv_heads):
+ *   x_t   = scale * q[s][h] . K_j(t)           for positions t = 0..L-1,
+ *   out   = sum_t softmax(x)_t * V_j(t),
+ * where position t lives in physical block block_tables[s][t / 16] at slot
+ * t % 16.  This is ordinary attention over the sequence's valid positions,
+ * the final block truncated at L; only addresses differ (PagedAttention and
+ * vLLM: Paging the KV Cache Like an OS, "Step 5: attention over scattered
+ * blocks"; PagedAttention (tensortonic), "5. Reading the Cache During
+ * Attention"; PagedAttention: Virtual Memory for the KV Cache, "PagedAttention:
+ * attention over non-contiguous blocks").  A decode step writes the step's
+ * own token first (pa_write_kv), so L counts it.
+ *
+ * The context is processed in partitions of `partition_size` positions with
+ * an online (running max / sum) softmax (PagedAttention (tensortonic), "10.
+ * How PagedAttention Fits with FlashAttention"); sequences longer than one
+ * partition are merged by a log-sum-exp weighted reduce, because softmax
+ * must normalise over all valid positions at once (same page, section 5).
+ *
+ *   out              device, [num_seqs][num_q_heads][head_dim], dtype; written
+ *   q                device, [num_seqs][num_q_heads][head_dim], dtype
+ *   k_pool, v_pool   device, [num_blocks][num_kv_heads][block_size][head_dim], dtype
+ *   block_tables     device, int32 [num_seqs][max_blocks_per_seq]; entries at
+ *                    index >= ceil(L/16) are never read
+ *   context_lens     device, int32 [num_seqs]; 0 <= L <= max_context_len
+ *                    (L = 0 writes a zero row)
+ *   max_context_len  host hint >= every context_lens[s]; sizes the launch;
+ *                    must be <= max_blocks_per_seq * block_size
+ *   scale            softmax scale (typically 1/sqrt(head_dim)), finite
+ *   partition_size   positions per partition; 0 = 512; a positive multiple
+ *                    of block_size
+ *   workspace        device scratch of at least pa_decode_workspace_bytes(...)
+ *                    bytes (may be NULL when that is 0); 256-byte aligned;
+ *                    contents need no initialisation and are clobbered
+ *   stream           hipStream_t or NULL
+ * Supported: block_size 16, head_dim 64 or 128, any num_q_heads that is a
+ * multiple of num_kv_heads.  `out` must not alias any input or the workspace.
+ */
+pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, int max_blocks_per_seq,
+                      int max_context_len, float scale, pa_dtype_t dtype, int partition_size,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pa_decode needs for these sizes (0 when every sequence
+ * fits one partition).  partition_size 0 means the default 512.  Returns 0
+ * for invalid sizes as well; pa_decode reports those. */
+size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
+                                 int max_context_len, int partition_size);
+
+/*
+ * pa_write_kv -- store new tokens' K and V rows in their slots
+ * (reshape-and-cache).  For each token i with slot = slot_mapping[i] >= 0:
+ *   k_pool[slot / 16][h][slot % 16][:] = k_new[i][h][:]   for every KV head h,
+ * and the same for V.  One launch covers every token of the step
+ * (PagedAttention (tensortonic), "5. Reading the Cache During Attention";
+ * PagedAttention and vLLM: Paging the KV Cache Like an OS, "Step 5", the
+ * fused write kernel).  Negative slots are skipped; slots >= num_blocks * 16
+ * are skipped too (caller error, never written).  Non-negative slots must be
+ * distinct.  Bytes outside the addressed rows are never touched.
+ *
+ *   k_pool, v_pool   device, [num_blocks][num_kv_heads][block_size][head_dim], dtype
+ *   k_new, v_new     device, [num_tokens][num_kv_heads][head_dim], dtype
+ *   slot_mapping     device, int64 [num_tokens]
+ */
+pa_status_t pa_write_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                        const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                        int head_dim, int block_size, int num_blocks, pa_dtype_t dtype,
+                        void* stream);
+
+/*
+ * pa_copy_blocks -- batched copy-on-write block copies.  For each pair
+ * (src, dst): the whole K block k_pool[dst] = k_pool[src] (every KV head,
+ * every slot) and the same for V, in one launch (PagedAttention and vLLM:
+ * Paging the KV Cache Like an OS, "Step 4" copy-on-write and "Step 5" the
+ * batched copy kernel).  Destinations must be distinct from one another and
+ * from every source (the block manager guarantees this); pairs with an id
+ * outside [0, num_blocks) are skipped.
+ *
+ *   block_pairs      device, int32 [num_pairs][2]
+ */
+pa_status_t pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_pairs,
+                           int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                           int num_blocks, pa_dtype_t dtype, void* stream);
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* ABI version of this header (bumped on incompatible changes). */
+int pa_abi_version(void);
+
+/*
+ * Host block manager (CPU only; no GPU calls).  A FIFO free list of physical
+ * block ids, a reference count per block and one block table per sequence
+ * (PagedAttention and vLLM: Paging the KV Cache Like an OS, "Step 3" and
+ * "Step 4"; vLLM's PagedAttention: How Memory Management Supports Large Model
+ * Inference, "2.2", "2.3" and "7").
+ *   - A block is taken from the front of the free list only when a sequence's
+ *     last block is full (on-demand allocation).
+ *   - fork copies the parent's table and increments each block's count.
+ *   - Appending into a partly filled last block whose count is > 1 first
+ *     copies it (copy-on-write): a fresh block is taken, (src, dst) is queued
+ *     for pa_copy_blocks, the table is repointed and src's count drops.  A
+ *     writer that finds the count at 1 writes in place.  Full blocks are never
+ *     copied.
+ *   - Freeing a sequence decrements its blocks' counts; blocks reaching 0
+ *     return, in table order, to the back of the free list -- except blocks
+ *     named by a queued copy, which are held until pa_bm_take_copies.
+ *   - Appends are all-or-nothing: PA_ERR_NO_BLOCKS leaves every table, count
+ *     and the free list unchanged.
+ * A pa_bm_t is not thread-safe; use one per thread or lock around it.
+ */
+typedef struct pa_bm pa_bm_t;
+
+/* initial_free_order: NULL (0..num_blocks-1) or a permutation of 0..num_blocks-1.
+ * Returns NULL on invalid arguments (message in pa_last_error). */
+pa_bm_t* pa_bm_create(int num_blocks, int block_size, const int32_t* initial_free_order);
+void pa_bm_destroy(pa_bm_t* bm);
+pa_status_t pa_bm_add_seq(pa_bm_t* bm, int64_t seq_id);
+/* Reserve slots for n_tokens more tokens; slots_out (nullable) receives
+ * n_tokens int64 slots. */
+pa_status_t pa_bm_append(pa_bm_t* bm, int64_t seq_id, int n_tokens, int64_t* slots_out);
+/* One token for each of n sequences (distinct ids), all or nothing over the
+ * batch; slots_out receives n slots in order. */
+pa_status_t pa_bm_append_batch(pa_bm_t* bm, const int64_t* seq_ids, int n, int64_t* slots_out);
+pa_status_t pa_bm_fork(pa_bm_t* bm, int64_t parent, int64_t child);
+pa_status_t pa_bm_free_seq(pa_bm_t* bm, int64_t seq_id);
+/* Writes up to cap entries of the table; returns its length (-1: unknown id). */
+int pa_bm_table(const pa_bm_t* bm, int64_t seq_id, int32_t* out, int cap);
+/* Fills out[n][max_blocks] with the tables of seq_ids, padding with pad.
+ * PA_ERR_SHAPE if a table is longer than max_blocks. */
+pa_status_t pa_bm_tables(const pa_bm_t* bm, const int64_t* seq_ids, int n, int32_t* out,
+                         int max_blocks, int32_t pad);
+/* Token count of a sequence (-1: unknown id). */
+int pa_bm_num_tokens(const pa_bm_t* bm, int64_t seq_id);
+/* Number of queued copy-on-write pairs. */
+int pa_bm_num_pending_copies(const pa_bm_t* bm);
+/* Drains the queued (src, dst) pairs into pairs_out[cap][2] and releases held
+ * blocks.  Returns the number of pairs, or -1 (nothing drained) if cap is
+ * smaller than pa_bm_num_pending_copies. */
+int pa_bm_take_copies(pa_bm_t* bm, int32_t* pairs_out, int cap);
+int pa_bm_num_free(const pa_bm_t* bm);
+/* Reference count of a block (-1: out of range). */
+int pa_bm_refcount(const pa_bm_t* bm, int32_t block);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,117 @@
+// pa_write_kv and pa_copy_blocks: byte-exact moves of K/V rows and blocks.
+//
+// Write (reshape-and-cache): every new token's K and V rows go to the slot
+// the block manager assigned, one launch for the whole step (PagedAttention
+// (tensortonic), "5. Reading the Cache During Attention"; PagedAttention and
+// vLLM: Paging the KV Cache Like an OS, "Step 5", the fused write kernel).
+// Copy: whole K and V blocks for copy-on-write, all pairs of a step in one
+// launch (same page, "Step 4" and the batched copy kernel of "Step 5").
+//
+// Both are pure data movement: 16-byte vector loads/stores, one token (write)
+// or one block slice (copy) per workgroup, so each workgroup moves contiguous
+// rows.  Out-of-range slots / block ids are skipped, never dereferenced.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void write_kv_kernel(char* __restrict__ kp, char* __restrict__ vp,
+                                                            const char* __restrict__ kn,
+                                                            const char* __restrict__ vn,
+                                                            const int64_t* __restrict__ slots, int num_kv_heads,
+                                                            int row_bytes, int block_size, int64_t num_slots) {
+  const int i = blockIdx.x;
+  const int64_t slot = slots[i];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / block_size;
+  const int off = (int)(slot % block_size);
+  const int per_row = row_bytes >> 4;  // 16-byte vectors per (token, head) row
+  const int n = num_kv_heads * per_row;
+  for (int v = threadIdx.x; v < n; v += kThreads) {
+    const int h = v / per_row;
+    const int c = v - h * per_row;
+    const size_t dst = (((size_t)blk * num_kv_heads + h) * block_size + off) * (size_t)row_bytes + (size_t)c * 16;
+    const size_t src = ((size_t)i * num_kv_heads + h) * (size_t)row_bytes + (size_t)c * 16;
+    const uint4 kx = *reinterpret_cast<const uint4*>(kn + src);
+    const uint4 vx = *reinterpret_cast<const uint4*>(vn + src);
+    *reinterpret_cast<uint4*>(kp + dst) = kx;
+    *reinterpret_cast<uint4*>(vp + dst) = vx;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(char* __restrict__ kp, char* __restrict__ vp,
+                                                               const int32_t* __restrict__ pairs,
+                                                               size_t block_bytes, int num_blocks) {
+  const int p = blockIdx.x;
+  const int32_t src = pairs[2 * p];
+  const int32_t dst = pairs[2 * p + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  char* pool = blockIdx.z ? vp : kp;
+  const uint4* s = reinterpret_cast<const uint4*>(pool + (size_t)src * block_bytes);
+  uint4* d = reinterpret_cast<uint4*>(pool + (size_t)dst * block_bytes);
+  const size_t n = block_bytes >> 4;
+  for (size_t v = (size_t)blockIdx.y * kThreads + threadIdx.x; v < n; v += (size_t)gridDim.y * kThreads) d[v] = s[v];
+}
+
+int elem_bytes(pa_dtype_t dt) { return dt == PA_FP32 ? 4 : (dt == PA_FP16 || dt == PA_BF16) ? 2 : 0; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+}  // namespace pa
+
+extern "C" pa_status_t pa_write_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                                   const int64_t* slot_mapping, int num_tokens, int num_kv_heads, int head_dim,
+                                   int block_size, int num_blocks, pa_dtype_t dtype, void* stream) {
+  using namespace pa;
+  clear_error();
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return fail(PA_ERR_UNSUPPORTED, "pa_write_kv: unknown dtype %d", (int)dtype);
+  if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "pa_write_kv: block_size %d (only 16)", block_size);
+  if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_write_kv: head_dim %d", head_dim);
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0)
+    return fail(PA_ERR_SHAPE, "pa_write_kv: num_tokens=%d num_kv_heads=%d num_blocks=%d", num_tokens, num_kv_heads,
+                num_blocks);
+  if (num_tokens == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return fail(PA_ERR_NULL, "pa_write_kv: NULL pointer");
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(PA_ERR_SHAPE, "pa_write_kv: tensors must be 16-byte aligned");
+  const int row_bytes = head_dim * eb;
+  hipLaunchKernelGGL(write_kv_kernel, dim3(num_tokens), dim3(kThreads), 0, (hipStream_t)stream, (char*)k_pool,
+                     (char*)v_pool, (const char*)k_new, (const char*)v_new, slot_mapping, num_kv_heads, row_bytes,
+                     block_size, (int64_t)num_blocks * block_size);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "pa_write_kv: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+extern "C" pa_status_t pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_pairs, int num_pairs,
+                                      int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                      pa_dtype_t dtype, void* stream) {
+  using namespace pa;
+  clear_error();
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: unknown dtype %d", (int)dtype);
+  if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: block_size %d (only 16)", block_size);
+  if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: head_dim %d", head_dim);
+  if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks < 0)
+    return fail(PA_ERR_SHAPE, "pa_copy_blocks: num_pairs=%d num_kv_heads=%d num_blocks=%d", num_pairs, num_kv_heads,
+                num_blocks);
+  if (num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !block_pairs) return fail(PA_ERR_NULL, "pa_copy_blocks: NULL pointer");
+  if (!aligned16(k_pool) || !aligned16(v_pool)) return fail(PA_ERR_SHAPE, "pa_copy_blocks: pools must be 16-byte aligned");
+  const size_t block_bytes = (size_t)num_kv_heads * block_size * head_dim * eb;
+  const size_t vecs = block_bytes / 16;
+  unsigned ychunks = (unsigned)((vecs + kThreads - 1) / kThreads);
+  if (ychunks > 64) ychunks = 64;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, ychunks, 2), dim3(kThreads), 0, (hipStream_t)stream,
+                     (char*)k_pool, (char*)v_pool, block_pairs, block_bytes, num_blocks);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "pa_copy_blocks: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}

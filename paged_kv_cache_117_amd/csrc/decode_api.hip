@@ -1,0 +1,98 @@
+// pa_decode / pa_decode_workspace_bytes: argument checks, workspace carving
+// and kernel selection.  The kernels themselves live in decode*.hip.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "decode_kernels.h"
+#include "pa_internal.h"
+
+namespace {
+
+constexpr int kDefaultPartition = 512;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int parts_for(int max_ctx, int psize) { return max_ctx <= 0 ? 1 : (max_ctx + psize - 1) / psize; }
+
+}  // namespace
+
+extern "C" size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int max_context_len,
+                                            int partition_size) {
+  const int psize = partition_size == 0 ? kDefaultPartition : partition_size;
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 || psize <= 0) return 0;
+  return pa::workspace_layout(num_seqs, num_q_heads, head_dim, parts_for(max_context_len, psize)).total;
+}
+
+extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                                 int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                 int max_blocks_per_seq, int max_context_len, float scale, pa_dtype_t dtype,
+                                 int partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace pa;
+  clear_error();
+  if (dtype != PA_FP32 && dtype != PA_FP16 && dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: unknown dtype %d", (int)dtype);
+  if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d (only 16)", block_size);
+  if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d (64 or 128)", head_dim);
+  if (num_seqs < 0 || num_seqs > 65535)
+    return fail(PA_ERR_SHAPE, "pa_decode: num_seqs %d outside [0, 65535]", num_seqs);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_SHAPE, "pa_decode: num_q_heads %d must be a positive multiple of num_kv_heads %d", num_q_heads,
+                num_kv_heads);
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return fail(PA_ERR_SHAPE, "pa_decode: num_blocks %d, max_blocks_per_seq %d", num_blocks, max_blocks_per_seq);
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PA_ERR_SHAPE, "pa_decode: max_context_len %d outside [0, max_blocks_per_seq*16 = %lld]",
+                max_context_len, (long long)max_blocks_per_seq * block_size);
+  const int psize = partition_size == 0 ? kDefaultPartition : partition_size;
+  if (psize <= 0 || psize % block_size != 0)
+    return fail(PA_ERR_SHAPE, "pa_decode: partition_size %d must be a positive multiple of 16", partition_size);
+  if (!isfinite(scale)) return fail(PA_ERR_SHAPE, "pa_decode: scale is not finite");
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
+    return fail(PA_ERR_NULL, "pa_decode: NULL pointer");
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return fail(PA_ERR_SHAPE, "pa_decode: out, q and the pools must be 16-byte aligned");
+
+  const int P = parts_for(max_context_len, psize);
+  const WorkspaceLayout wl = workspace_layout(num_seqs, num_q_heads, head_dim, P);
+  if (wl.total > 0) {
+    if (!workspace) return fail(PA_ERR_WORKSPACE, "pa_decode: needs %zu bytes of workspace, got NULL", wl.total);
+    if (workspace_bytes < wl.total)
+      return fail(PA_ERR_WORKSPACE, "pa_decode: needs %zu bytes of workspace, got %zu", wl.total, workspace_bytes);
+    if (!aligned(workspace, 256)) return fail(PA_ERR_WORKSPACE, "pa_decode: workspace must be 256-byte aligned");
+  }
+
+  DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.kp = static_cast<const char*>(k_pool);
+  a.vp = static_cast<const char*>(v_pool);
+  a.bt = block_tables;
+  a.cl = context_lens;
+  char* ws = static_cast<char*>(workspace);
+  a.ws_o = wl.total ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr;
+  a.ws_m = wl.total ? reinterpret_cast<float*>(ws + wl.m_off) : nullptr;
+  a.ws_l = wl.total ? reinterpret_cast<float*>(ws + wl.l_off) : nullptr;
+  a.B = num_seqs;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.g = num_q_heads / num_kv_heads;
+  a.gmax = a.g >= 8 ? 8 : a.g > 2 ? 4 : a.g;  // 1, 2, 4 or 8 query heads per work item
+  a.nsub = (a.g + a.gmax - 1) / a.gmax;
+  a.D = head_dim;
+  a.num_blocks = num_blocks;
+  a.maxb = max_blocks_per_seq;
+  a.max_ctx = max_context_len;
+  a.psize = psize;
+  a.P = P;
+  a.qscale = scale * 1.4426950408889634f;
+  a.dtype = dtype;
+  if ((int64_t)num_kv_heads * a.nsub > 65535) return fail(PA_ERR_SHAPE, "pa_decode: too many KV heads");
+
+  launch_decode_valu(a, static_cast<hipStream_t>(stream));
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "pa_decode: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}

@@ -1,0 +1,47 @@
+// Internal interface between the pa_decode entry point and its kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const char* kp;
+  const char* vp;
+  const int32_t* bt;
+  const int32_t* cl;
+  float* ws_o;  // [B][Hq][P][D] partition outputs (normalised)
+  float* ws_m;  // [B][Hq][P] running max, base-2 domain
+  float* ws_l;  // [B][Hq][P] running sum
+  int B, Hq, Hkv, g, gmax, nsub, D;
+  int num_blocks, maxb, max_ctx, psize, P;
+  float qscale;  // scale * log2(e)
+  pa_dtype_t dtype;
+};
+
+struct WorkspaceLayout {
+  size_t o_off, m_off, l_off, total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline WorkspaceLayout workspace_layout(size_t B, size_t Hq, size_t D, size_t P) {
+  WorkspaceLayout w{};
+  if (P <= 1) return w;
+  const size_t rows = B * Hq * P;
+  w.o_off = 0;
+  w.m_off = align256(rows * D * sizeof(float));
+  w.l_off = w.m_off + align256(rows * sizeof(float));
+  w.total = w.l_off + align256(rows * sizeof(float));
+  return w;
+}
+
+void launch_decode_valu(const DecodeArgs& a, hipStream_t st);
+
+}  // namespace pa

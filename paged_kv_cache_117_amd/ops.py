@@ -1,0 +1,150 @@
+"""Python binding of the device entry points: argument marshalling only.
+
+Every call checks what the C ABI cannot see (tensor devices, dtypes, shapes,
+contiguity), so that the kernels only ever receive device buffers of the sizes
+the sizes arguments describe, then calls straight into libpa.so.  All work
+runs in the library's HIP kernels on the current (or given) stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import LIB, PA_BF16, PA_ERR_NO_BLOCKS, PA_FP16, PA_FP32, STATUS_NAMES
+
+BLOCK_SIZE = 16
+_DTYPES = {torch.float32: PA_FP32, torch.float16: PA_FP16, torch.bfloat16: PA_BF16}
+
+
+class PaError(RuntimeError):
+    def __init__(self, msg, status):
+        super().__init__(msg)
+        self.status = status
+
+
+class NoFreeBlocks(PaError):
+    pass
+
+
+def check_status(st: int, what: str) -> None:
+    if st != 0:
+        msg = LIB.pa_last_error().decode(errors="replace")
+        cls = NoFreeBlocks if st == PA_ERR_NO_BLOCKS else PaError
+        raise cls(f"{what}: {STATUS_NAMES.get(st, st)}: {msg}", st)
+
+
+def _device_tensor(t, name, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, current device is {torch.cuda.current_device()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    return t
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dtype_code(t):
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_context_len: int,
+                           partition_size: int = 0) -> int:
+    return int(LIB.pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_size))
+
+
+def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_context_len: int,
+           out=None, partition_size: int = 0, workspace=None, stream=None):
+    """Paged decode attention (pa_decode).  Returns ``out`` [B][Hq][D]."""
+    _device_tensor(q, "q", ndim=3)
+    B, Hq, D = q.shape
+    _device_tensor(k_pool, "k_pool", q.dtype, 4)
+    _device_tensor(v_pool, "v_pool", q.dtype, 4)
+    if k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool shapes differ")
+    nb, Hkv, bs, Dk = k_pool.shape
+    if Dk != D:
+        raise ValueError(f"head_dim mismatch: q {D}, pools {Dk}")
+    _device_tensor(block_tables, "block_tables", torch.int32, 2)
+    _device_tensor(context_lens, "context_lens", torch.int32, 1)
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens rows must equal num_seqs")
+    if out is None:
+        out = torch.empty_like(q)
+    _device_tensor(out, "out", q.dtype, 3)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    need = decode_workspace_bytes(B, Hq, D, max_context_len, partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device) if need else None
+    if workspace is not None:
+        _device_tensor(workspace, "workspace")
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = LIB.pa_decode(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                       block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, bs, nb,
+                       block_tables.shape[1], int(max_context_len), float(scale), _dtype_code(q),
+                       int(partition_size), ws_ptr, ws_bytes, _stream_handle(stream))
+    check_status(st, "pa_decode")
+    return out
+
+
+def write_kv(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
+    """Store new tokens' K/V rows at their slots (pa_write_kv)."""
+    _device_tensor(k_pool, "k_pool", ndim=4)
+    _device_tensor(v_pool, "v_pool", k_pool.dtype, 4)
+    if k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool shapes differ")
+    nb, Hkv, bs, D = k_pool.shape
+    _device_tensor(k_new, "k_new", k_pool.dtype, 3)
+    _device_tensor(v_new, "v_new", k_pool.dtype, 3)
+    _device_tensor(slot_mapping, "slot_mapping", torch.int64, 1)
+    T = slot_mapping.shape[0]
+    if tuple(k_new.shape) != (T, Hkv, D) or tuple(v_new.shape) != (T, Hkv, D):
+        raise ValueError(f"k_new/v_new must be [{T}][{Hkv}][{D}]")
+    st = LIB.pa_write_kv(k_pool.data_ptr(), v_pool.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                         slot_mapping.data_ptr(), T, Hkv, D, bs, nb, _dtype_code(k_pool),
+                         _stream_handle(stream))
+    check_status(st, "pa_write_kv")
+
+
+def copy_blocks(k_pool, v_pool, block_pairs, stream=None):
+    """Whole-block copies (src -> dst) for copy-on-write (pa_copy_blocks)."""
+    _device_tensor(k_pool, "k_pool", ndim=4)
+    _device_tensor(v_pool, "v_pool", k_pool.dtype, 4)
+    if k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool shapes differ")
+    nb, Hkv, bs, D = k_pool.shape
+    _device_tensor(block_pairs, "block_pairs", torch.int32, 2)
+    if block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [n][2]")
+    st = LIB.pa_copy_blocks(k_pool.data_ptr(), v_pool.data_ptr(), block_pairs.data_ptr(),
+                            block_pairs.shape[0], Hkv, D, bs, nb, _dtype_code(k_pool),
+                            _stream_handle(stream))
+    check_status(st, "pa_copy_blocks")
+
+
+def abi_version() -> int:
+    return int(LIB.pa_abi_version())
+
+
+def _as_ptr(arr, ctype):
+    return arr.ctypes.data_as(ctypes.POINTER(ctype))

@@ -15,3 +15,12 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_sessionstart(session):
+    # Tests load the in-tree libpa.so; build it only when nothing is built.
+    lib = os.path.join(ROOT, "paged_kv_cache_117_amd", "libpa.so")
+    if not os.path.exists(lib):
+        from paged_kv_cache_117_amd import build_lib
+
+        build_lib.build(verbose=False)

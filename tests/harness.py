@@ -1,0 +1,154 @@
+"""Shared test plumbing: one decode step on the oracle and on the HIP path.
+
+A step is: replay the workload's block-manager operations (pre-step state),
+append one token per sequence, run the copy-on-write copies, write the new
+K/V, then decode.  Before the step, every pool element that does not hold a
+cached token (unused blocks, unfilled slots, the slot the step writes, copy
+destinations) is set to NaN, so an output is finite only if the step filled
+what it had to and the kernels never read an invalid slot.
+
+The oracle side uses only ``oracle`` (its block manager, write, copy and
+decode); the GPU side uses only the library.  They share the seeded
+``workloads`` inputs and nothing else.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+NAN_BITS = {"fp32": None, "fp16": np.float16(np.nan), "bf16": np.uint16(0x7FC0)}
+
+
+def nan_value(dtype):
+    if dtype == "fp32":
+        return np.float32(np.nan)
+    return NAN_BITS[dtype]
+
+
+def tables_of(bm, seq_ids, max_blocks):
+    t = np.full((len(seq_ids), max_blocks), -1, dtype=np.int32)
+    for s, sid in enumerate(seq_ids):
+        row = bm.table(sid)
+        t[s, : len(row)] = row
+    return t
+
+
+def poison_pools(w, pre_tables, pre_ntok):
+    """Copies of the pools with NaN everywhere except cached positions."""
+    keep = np.zeros((w.num_blocks, w.block_size), dtype=bool)
+    for s in range(w.num_seqs):
+        n = int(pre_ntok[s])
+        nb = -(-n // w.block_size)
+        for j in range(nb):
+            cnt = min(w.block_size, n - j * w.block_size)
+            keep[pre_tables[s, j], :cnt] = True
+    k = w.k_pool.copy()
+    v = w.v_pool.copy()
+    mask = ~keep  # [num_blocks][bs] -> broadcast over heads and dims
+    nv = nan_value(w.dtype)
+    k.transpose(0, 2, 1, 3)[mask] = nv
+    v.transpose(0, 2, 1, 3)[mask] = nv
+    return k, v
+
+
+class Step:
+    """Everything one side needs to run (or check) a decode step."""
+
+    def __init__(self, w, bm_factory, poison=True):
+        self.w = w
+        bm = bm_factory(w.num_blocks, w.block_size, w.perm)
+        bm.replay(w.ops)
+        self.pre_ntok = np.array([bm.num_tokens(s) for s in w.seq_ids], dtype=np.int64)
+        assert np.array_equal(self.pre_ntok, w.context_lens.astype(np.int64) - 1)
+        maxb = w.max_blocks_per_seq
+        self.pre_tables = tables_of(bm, w.seq_ids, maxb)
+        self.slots = np.asarray(bm.append_batch(w.seq_ids), dtype=np.int64)
+        self.pairs = np.asarray(bm.take_copies(), dtype=np.int32).reshape(-1, 2)
+        self.tables = tables_of(bm, w.seq_ids, maxb)
+        self.bm = bm
+        if poison:
+            self.k0, self.v0 = poison_pools(w, self.pre_tables, self.pre_ntok)
+        else:
+            self.k0, self.v0 = w.k_pool, w.v_pool
+
+
+def oracle_step(w, poison=True, rows=None):
+    """Oracle result of the step: (pools after copy+write, decode output rows)."""
+    st = Step(w, lambda n, bs, order: oracle.BlockManager(n, bs, order), poison)
+    k, v = oracle.copy_blocks(st.k0, st.v0, st.pairs)
+    k, v = oracle.write_kv(k, v, w.k_new, w.v_new, st.slots, w.block_size)
+    rows = np.arange(w.num_seqs) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = oracle.decode(w.q[rows], k, v, st.tables[rows], w.context_lens[rows], w.scale, w.dtype)
+    return st, k, v, out
+
+
+# ----------------------------------------------------------------------------
+# GPU side
+# ----------------------------------------------------------------------------
+
+def torch_dtype(dtype):
+    import torch
+
+    return {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[dtype]
+
+
+def to_device(a, dtype=None):
+    """Host array -> device tensor; 16-bit storage keeps its exact bits."""
+    import torch
+
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    elif dtype == "fp16":
+        t = torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return t
+
+
+def to_host_storage(t, dtype):
+    """Device tensor -> numpy array in the workload's storage format."""
+    import torch
+
+    if dtype == "bf16":
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def to_f64(t, dtype):
+    return oracle.storage_to_f64(to_host_storage(t, dtype), dtype)
+
+
+class GpuStep:
+    """Upload one step's inputs and run it through the library."""
+
+    def __init__(self, w, poison=True, bm_factory=None):
+        import paged_kv_cache_117_amd as pa
+
+        factory = bm_factory or (lambda n, bs, order: pa.BlockManager(n, bs, order))
+        self.st = Step(w, factory, poison)
+        self.w = w
+        self.k = to_device(self.st.k0, w.dtype)
+        self.v = to_device(self.st.v0, w.dtype)
+        self.q = to_device(w.q, w.dtype)
+        self.k_new = to_device(w.k_new, w.dtype)
+        self.v_new = to_device(w.v_new, w.dtype)
+        self.slots = to_device(self.st.slots)
+        self.pairs = to_device(self.st.pairs)
+        self.tables = to_device(self.st.tables)
+        self.lens = to_device(w.context_lens.astype(np.int32))
+
+    def run(self, partition_size=0, out=None):
+        import paged_kv_cache_117_amd as pa
+
+        w = self.w
+        if len(self.st.pairs):
+            pa.copy_blocks(self.k, self.v, self.pairs)
+        pa.write_kv(self.k, self.v, self.k_new, self.v_new, self.slots)
+        self.out = pa.decode(self.q, self.k, self.v, self.tables, self.lens, w.scale,
+                             w.max_context_len, out=out, partition_size=partition_size)
+        return self.out
+
+
+TOL = {"fp32": 1e-5, "fp16": 1.5e-2, "bf16": 1.5e-2}

@@ -1,0 +1,95 @@
+"""The C ABI: every declared function is exported and bound; host-side checks."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_117_amd as pa
+from paged_kv_cache_117_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = declared_functions()
+    assert len(names) >= 20
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(_lib.SIGNATURES) == names
+
+
+def test_abi_version():
+    assert pa.abi_version() == 1
+
+
+def test_workspace_bytes():
+    # one partition -> no workspace
+    assert pa.decode_workspace_bytes(4, 2, 64, 37, 0) == 0
+    assert pa.decode_workspace_bytes(64, 32, 128, 512, 512) == 0
+    # 8 partitions of 512 for 4096 tokens: o [B][Hq][P][D] + m + l, each 256-aligned
+    rows = 64 * 32 * 8
+    assert pa.decode_workspace_bytes(64, 32, 128, 4096, 0) == rows * 128 * 4 + 2 * rows * 4
+    assert pa.decode_workspace_bytes(0, 32, 128, 4096, 0) == 0
+
+
+L = _lib.LIB
+NULL = None
+
+
+def call_decode(**kw):
+    a = dict(out=16, q=16, k=16, v=16, bt=16, cl=16, B=1, Hq=2, Hkv=2, D=64, bs=16, nb=4, maxb=2,
+             maxctx=20, scale=0.125, dt=0, ps=0, ws=NULL, wsb=0, stream=NULL)
+    a.update(kw)
+    return L.pa_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                       a["bs"], a["nb"], a["maxb"], a["maxctx"], a["scale"], a["dt"], a["ps"], a["ws"], a["wsb"],
+                       a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bs=8), 3), (dict(D=96), 3), (dict(dt=7), 3),
+    (dict(Hq=3, Hkv=2), 2), (dict(maxctx=33), 2), (dict(ps=24), 2), (dict(B=-1), 2),
+    (dict(scale=float("inf")), 2), (dict(q=NULL), 1), (dict(out=8), 2),
+    (dict(maxctx=600, maxb=64), 4),
+])
+def test_decode_host_validation(kw, status):
+    """Rejected before any device work (these calls never reach the GPU)."""
+    assert call_decode(**kw) == status
+    assert L.pa_last_error().decode()
+
+
+def test_decode_zero_sequences_is_a_no_op():
+    assert call_decode(B=0, out=NULL, q=NULL) == 0
+
+
+def test_write_and_copy_host_validation():
+    assert L.pa_write_kv(16, 16, 16, 16, 16, 1, 2, 64, 8, 4, 0, NULL) == 3
+    assert L.pa_write_kv(16, 16, 16, 16, NULL, 1, 2, 64, 16, 4, 0, NULL) == 1
+    assert L.pa_write_kv(16, 16, 8, 16, 16, 1, 2, 64, 16, 4, 0, NULL) == 2
+    assert L.pa_write_kv(NULL, NULL, NULL, NULL, NULL, 0, 2, 64, 16, 4, 0, NULL) == 0
+    assert L.pa_copy_blocks(16, 16, 16, 1, 2, 100, 16, 4, 0, NULL) == 3
+    assert L.pa_copy_blocks(16, 16, NULL, 1, 2, 64, 16, 4, 0, NULL) == 1
+    assert L.pa_copy_blocks(NULL, NULL, NULL, 0, 2, 64, 16, 4, 0, NULL) == 0
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+
+    q = torch.zeros(1, 2, 64)
+    with pytest.raises(ValueError):
+        pa.decode(q, torch.zeros(4, 2, 16, 64), torch.zeros(4, 2, 16, 64),
+                  torch.zeros(1, 2, dtype=torch.int32), torch.ones(1, dtype=torch.int32), 0.125, 1)
+
+
+def test_one_hip_runtime_in_the_process():
+    """libpa binds to torch's HIP runtime; a second copy would not see the device."""
+    maps = [line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line]
+    assert len(set(maps)) == 1, sorted(set(maps))
