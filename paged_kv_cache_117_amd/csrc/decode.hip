@@ -281,23 +281,36 @@ void launch_reduce(const DecodeArgs& a, hipStream_t st) {
 }
 
 template <int DT>
-void launch_all(const DecodeArgs& a, hipStream_t st) {
-  if (a.D == 64) {
+void launch_valu_d(const DecodeArgs& a, hipStream_t st) {
+  if (a.D == 64)
     launch_valu_g<DT, 64>(a, st);
-    if (a.P > 1) launch_reduce<DT, 64>(a, st);
-  } else {
+  else
     launch_valu_g<DT, 128>(a, st);
-    if (a.P > 1) launch_reduce<DT, 128>(a, st);
-  }
+}
+
+template <int DT>
+void launch_reduce_d(const DecodeArgs& a, hipStream_t st) {
+  if (a.D == 64)
+    launch_reduce<DT, 64>(a, st);
+  else
+    launch_reduce<DT, 128>(a, st);
 }
 
 }  // namespace
 
 void launch_decode_valu(const DecodeArgs& a, hipStream_t st) {
   switch (a.dtype) {
-    case PA_FP32: launch_all<PA_FP32>(a, st); break;
-    case PA_FP16: launch_all<PA_FP16>(a, st); break;
-    default: launch_all<PA_BF16>(a, st); break;
+    case PA_FP32: launch_valu_d<PA_FP32>(a, st); break;
+    case PA_FP16: launch_valu_d<PA_FP16>(a, st); break;
+    default: launch_valu_d<PA_BF16>(a, st); break;
+  }
+}
+
+void launch_decode_reduce(const DecodeArgs& a, hipStream_t st) {
+  switch (a.dtype) {
+    case PA_FP32: launch_reduce_d<PA_FP32>(a, st); break;
+    case PA_FP16: launch_reduce_d<PA_FP16>(a, st); break;
+    default: launch_reduce_d<PA_BF16>(a, st); break;
   }
 }
 

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "decode_kernels.h"
 #include "pa_internal.h"
@@ -12,6 +14,16 @@ namespace {
 constexpr int kDefaultPartition = 512;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// PA_DECODE_KERNEL=valu selects the VALU partition kernel for 16-bit KV too
+// (read once; for comparisons).
+bool force_valu() {
+  static const bool v = [] {
+    const char* e = getenv("PA_DECODE_KERNEL");
+    return e && strcmp(e, "valu") == 0;
+  }();
+  return v;
+}
 
 int parts_for(int max_ctx, int psize) { return max_ctx <= 0 ? 1 : (max_ctx + psize - 1) / psize; }
 
@@ -91,7 +103,13 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
   a.dtype = dtype;
   if ((int64_t)num_kv_heads * a.nsub > 65535) return fail(PA_ERR_SHAPE, "pa_decode: too many KV heads");
 
-  launch_decode_valu(a, static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype != PA_FP32 && !force_valu()) {
+    launch_decode_mfma(a, st);
+  } else {
+    launch_decode_valu(a, st);
+    if (a.P > 1) launch_decode_reduce(a, st);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "pa_decode: launch failed: %s", hipGetErrorString(e));
   return PA_OK;

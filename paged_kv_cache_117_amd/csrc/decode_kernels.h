@@ -42,6 +42,9 @@ inline WorkspaceLayout workspace_layout(size_t B, size_t Hq, size_t D, size_t P)
   return w;
 }
 
-void launch_decode_valu(const DecodeArgs& a, hipStream_t st);
+// Partition kernels (the reduce is launched separately when P > 1).
+void launch_decode_valu(const DecodeArgs& a, hipStream_t st);   // any dtype
+void launch_decode_mfma(const DecodeArgs& a, hipStream_t st);   // fp16 / bf16; launches the reduce itself
+void launch_decode_reduce(const DecodeArgs& a, hipStream_t st);
 
 }  // namespace pa
