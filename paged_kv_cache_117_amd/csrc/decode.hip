@@ -47,9 +47,9 @@ __global__ __launch_bounds__(64) void decode_part_valu(void* __restrict__ out, c
                                                       const char* __restrict__ kp, const char* __restrict__ vp,
                                                       const int32_t* __restrict__ bt, const int32_t* __restrict__ cl,
                                                       float* __restrict__ ws_o, float* __restrict__ ws_m,
-                                                      float* __restrict__ ws_l, int Hq, int Hkv, int g, int nsub,
-                                                      int num_blocks, int maxb, int max_ctx, float qscale, int psize,
-                                                      int P) {
+                                                      float* __restrict__ ws_l, int B, int Hq, int Hkv, int g,
+                                                      int nsub, int num_blocks, int maxb, int max_ctx, float qscale,
+                                                      int psize, int P) {
   constexpr int ES = Elem<DT>::kBytes;
   constexpr int ROWB = D * ES;
   constexpr int LPR = ROWB / 16;
@@ -59,10 +59,15 @@ __global__ __launch_bounds__(64) void decode_part_valu(void* __restrict__ out, c
   const int lane = threadIdx.x;
   const int r = lane / LPR;
   const int c = lane % LPR;
-  const int p = blockIdx.x;
-  const int kvh = blockIdx.y / nsub;
-  const int sub = blockIdx.y - kvh * nsub;
-  const int s = blockIdx.z;
+  // 1-D grid: KV head / sub-group fastest, then sequence, then partition, so
+  // the round-robin deal of workgroups to the 8 XCDs balances the work.
+  const int hs = Hkv * nsub;
+  const int idx = blockIdx.x;
+  const int hsub = idx % hs;
+  const int s = (idx / hs) % B;
+  const int p = idx / (hs * B);
+  const int kvh = hsub / nsub;
+  const int sub = hsub - kvh * nsub;
   int L = cl[s];
   const bool bad_len = L < 0 || L > max_ctx;
   if (bad_len) L = 0;
@@ -259,9 +264,10 @@ namespace {
 
 template <int DT, int D, int GMAX>
 void launch_valu(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_part_valu<DT, D, GMAX>), dim3(a.P, a.Hkv * a.nsub, a.B), dim3(64), 0, st, a.out, a.q,
-                     a.kp, a.vp, a.bt, a.cl, a.ws_o, a.ws_m, a.ws_l, a.Hq, a.Hkv, a.g, a.nsub, a.num_blocks, a.maxb,
-                     a.max_ctx, a.qscale, a.psize, a.P);
+  const unsigned grid = (unsigned)a.P * a.Hkv * a.nsub * a.B;
+  hipLaunchKernelGGL((decode_part_valu<DT, D, GMAX>), dim3(grid), dim3(64), 0, st, a.out, a.q, a.kp, a.vp, a.bt,
+                     a.cl, a.ws_o, a.ws_m, a.ws_l, a.B, a.Hq, a.Hkv, a.g, a.nsub, a.num_blocks, a.maxb, a.max_ctx,
+                     a.qscale, a.psize, a.P);
 }
 
 template <int DT, int D>

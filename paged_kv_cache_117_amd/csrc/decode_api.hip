@@ -101,7 +101,9 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
   a.P = P;
   a.qscale = scale * 1.4426950408889634f;
   a.dtype = dtype;
-  if ((int64_t)num_kv_heads * a.nsub > 65535) return fail(PA_ERR_SHAPE, "pa_decode: too many KV heads");
+  if ((int64_t)P * num_kv_heads * a.nsub * num_seqs > 0x7fffffffLL)
+    return fail(PA_ERR_SHAPE, "pa_decode: launch of %lld workgroups is too large",
+                (long long)P * num_kv_heads * a.nsub * num_seqs);
 
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype != PA_FP32 && !force_valu()) {

@@ -62,6 +62,26 @@ __device__ __forceinline__ float row_bcast(float x) {
                             __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xF, 0xF, false));
 }
 
+// The value of lane l combined (`op`) with the value of lane l^16 (resp.
+// l^32): the token groups of the MFMA output layout.  (gfx950's
+// v_permlane16/32_swap would do this on the VALU, but this compiler folds the
+// two results of the swap intrinsic into one when they are combined, so the
+// LDS crossbar permute is used.)
+template <typename Op>
+__device__ __forceinline__ float xor16(float x, Op op) {
+  return op(x, __shfl_xor(x, 16));
+}
+template <typename Op>
+__device__ __forceinline__ float xor32(float x, Op op) {
+  return op(x, __shfl_xor(x, 32));
+}
+struct MaxOp {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct AddOp {
+  __device__ float operator()(float a, float b) const { return a + b; }
+};
+
 template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (N > 0) {
@@ -95,9 +115,9 @@ __global__ __launch_bounds__(256) void decode_part_mfma(void* __restrict__ out, 
                                                        const char* __restrict__ kp, const char* __restrict__ vp,
                                                        const int32_t* __restrict__ bt, const int32_t* __restrict__ cl,
                                                        float* __restrict__ ws_o, float* __restrict__ ws_m,
-                                                       float* __restrict__ ws_l, int Hq, int Hkv, int g, int nsub,
-                                                       int num_blocks, int maxb, int max_ctx, float qscale, int psize,
-                                                       int P) {
+                                                       float* __restrict__ ws_l, int B, int Hq, int Hkv, int g,
+                                                       int nsub, int num_blocks, int maxb, int max_ctx, float qscale,
+                                                       int psize, int P) {
   constexpr int ROWB = D * 2;  // bytes of one token row of one head
   constexpr int KS = D / 32;   // MFMA k-steps over the head dim
   constexpr int DPL = D / 16;  // dims per lane in the PV step
@@ -113,10 +133,17 @@ __global__ __launch_bounds__(256) void decode_part_mfma(void* __restrict__ out, 
   const int lane = tid & 63;
   const int grp = lane >> 4;
   const int col = lane & 15;
-  const int p = blockIdx.x;
-  const int kvh = blockIdx.y / nsub;
-  const int sub = blockIdx.y - kvh * nsub;
-  const int s = blockIdx.z;
+  // 1-D grid, KV head (and query sub-group) fastest, then sequence, then
+  // partition.  Workgroups are dealt round-robin to the 8 XCDs by linear id,
+  // so every XCD gets an equal share of heads of every sequence and every
+  // partition index; the (mostly empty) high partitions come last.
+  const int hs = Hkv * nsub;
+  const int idx = blockIdx.x;
+  const int hsub = idx % hs;
+  const int s = (idx / hs) % B;
+  const int p = idx / (hs * B);
+  const int kvh = hsub / nsub;
+  const int sub = hsub - kvh * nsub;
   int L = cl[s];
   const bool bad_len = L < 0 || L > max_ctx;
   if (bad_len) L = 0;
@@ -181,9 +208,11 @@ __global__ __launch_bounds__(256) void decode_part_mfma(void* __restrict__ out, 
       for (int i = 0; i < 4; ++i) vr[i] = *reinterpret_cast<const VVec*>(vb + v_lane + i * ROWB);
     };
 
-    auto consume = [&](int j, const uint4(&kr)[KS], const VVec(&vr)[4]) {
+    // `valid` false: a padding step of the pipeline; every slot is masked.
+    auto consume = [&](int j, const uint4(&kr)[KS], const VVec(&vr)[4], bool valid) {
       const int blk = b0 + wave + (chunk + j) * kWaves;
-      const bool full = (blk + 1) * 16 <= L;
+      const int lim = valid ? L : 0;
+      const bool full = (blk + 1) * 16 <= lim;
       f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < KS; ++k) sacc = mfma_qk<DT>(kr[k], qop[k], sacc);
@@ -193,11 +222,11 @@ __global__ __launch_bounds__(256) void decode_part_mfma(void* __restrict__ out, 
       if (!full) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
-          if (blk * 16 + grp * 4 + jj >= L) sv[jj] = kNegInf;
+          if (blk * 16 + grp * 4 + jj >= lim) sv[jj] = kNegInf;
       }
       float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      bm = xor16(bm, MaxOp());
+      bm = xor32(bm, MaxOp());
       const float mn = fmaxf(m_run, bm);
       if (__any(mn > m_run)) {
         const float alpha = fast_exp2(m_run - mn);
@@ -218,7 +247,7 @@ __global__ __launch_bounds__(256) void decode_part_mfma(void* __restrict__ out, 
       for (int i = 0; i < 4; ++i) {
         float vf[DPL];
         unpack_v<DT, DPL>(vr[i], vf);
-        if (!full && blk * 16 + grp * 4 + i >= L) {
+        if (!full && blk * 16 + grp * 4 + i >= lim) {
 #pragma unroll
           for (int e = 0; e < DPL; ++e) vf[e] = 0.f;  // unfilled slots may hold NaN
         }
@@ -231,28 +260,26 @@ __global__ __launch_bounds__(256) void decode_part_mfma(void* __restrict__ out, 
       }
     };
 
+    // Two tiles in flight per wave.  Every issue is unconditional (indices
+    // past the end re-read the last tile, an L2 hit) so the loads stay in a
+    // fixed order and each consume waits only for its own tile.
+    const int last = cnt - 1;
     issue(0, kA, vA);
-    if (cnt > 1) issue(1, kB, vB);
+    issue(min(1, last), kB, vB);
     for (int j = 0; j < cnt; j += 2) {
-      consume(j, kA, vA);
-      if (j + 2 < cnt) issue(j + 2, kA, vA);
-      if (j + 1 < cnt) {
-        consume(j + 1, kB, vB);
-        if (j + 3 < cnt) issue(j + 3, kB, vB);
-      }
+      consume(j, kA, vA, true);
+      issue(min(j + 2, last), kA, vA);
+      consume(j + 1, kB, vB, j + 1 < cnt);
+      issue(min(j + 3, last), kB, vB);
     }
   }
 
   // Sum the four token groups of the wave (same head / dims, other tokens).
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = xor32(xor16(l_run, AddOp()), AddOp());
 #pragma unroll
   for (int h = 0; h < GMAX; ++h)
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      acc[h][e] += __shfl_xor(acc[h][e], 16);
-      acc[h][e] += __shfl_xor(acc[h][e], 32);
-    }
+    for (int e = 0; e < DPL; ++e) acc[h][e] = xor32(xor16(acc[h][e], AddOp()), AddOp());
   if (grp == 0) {
     s_m[wave][col] = m_run;
     s_l[wave][col] = l_run;
@@ -295,9 +322,10 @@ __global__ __launch_bounds__(256) void decode_part_mfma(void* __restrict__ out, 
 
 template <int DT, int D, int GMAX>
 void launch(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_part_mfma<DT, D, GMAX>), dim3(a.P, a.Hkv * a.nsub, a.B), dim3(256), 0, st, a.out, a.q,
-                     a.kp, a.vp, a.bt, a.cl, a.ws_o, a.ws_m, a.ws_l, a.Hq, a.Hkv, a.g, a.nsub, a.num_blocks, a.maxb,
-                     a.max_ctx, a.qscale, a.psize, a.P);
+  const unsigned grid = (unsigned)a.P * a.Hkv * a.nsub * a.B;
+  hipLaunchKernelGGL((decode_part_mfma<DT, D, GMAX>), dim3(grid), dim3(256), 0, st, a.out, a.q, a.kp, a.vp, a.bt,
+                     a.cl, a.ws_o, a.ws_m, a.ws_l, a.B, a.Hq, a.Hkv, a.g, a.nsub, a.num_blocks, a.maxb, a.max_ctx,
+                     a.qscale, a.psize, a.P);
 }
 
 template <int DT, int D>
