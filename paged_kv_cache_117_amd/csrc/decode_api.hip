@@ -106,7 +106,9 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
                 (long long)P * num_kv_heads * a.nsub * num_seqs);
 
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dtype != PA_FP32 && !force_valu()) {
+  // MFMA kernel: 16-bit KV, partitions of at most 4096 positions (each of its
+  // 4 waves walks at most 64 blocks).  Everything else: the VALU kernel.
+  if (dtype != PA_FP32 && psize <= 4096 && !force_valu()) {
     launch_decode_mfma(a, st);
   } else {
     launch_decode_valu(a, st);

@@ -58,22 +58,17 @@ __device__ __forceinline__ f32x4 mfma_qk(const uint4& a, const uint4& b, const f
 // Lane N of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
 template <int N>
 __device__ __forceinline__ float row_bcast(float x) {
-  return __builtin_bit_cast(float,
-                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + N, 0xF, 0xF, false));
 }
 
 // The value of lane l combined (`op`) with the value of lane l^16 (resp.
-// l^32): the token groups of the MFMA output layout.  (gfx950's
-// v_permlane16/32_swap would do this on the VALU, but this compiler folds the
-// two results of the swap intrinsic into one when they are combined, so the
-// LDS crossbar permute is used.)
+// l^32), i.e. the other token groups of the MFMA output layout, through the
+// LDS crossbar (ds_bpermute; `addr` is the partner lane times 4).  gfx950's
+// v_permlane16/32_swap would stay on the VALU, but this compiler folds the
+// two results of the swap intrinsic into one when they are combined.
 template <typename Op>
-__device__ __forceinline__ float xor16(float x, Op op) {
-  return op(x, __shfl_xor(x, 16));
-}
-template <typename Op>
-__device__ __forceinline__ float xor32(float x, Op op) {
-  return op(x, __shfl_xor(x, 32));
+__device__ __forceinline__ float xchg(float x, int addr, Op op) {
+  return op(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, x))));
 }
 struct MaxOp {
   __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
@@ -129,10 +124,13 @@ __global__ __launch_bounds__(256) void decode_part_mfma(void* __restrict__ out, 
   __shared__ int s_bad[kWaves];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave-uniform: keep it (and everything derived from it) in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int grp = lane >> 4;
   const int col = lane & 15;
+  const int x16 = (lane ^ 16) << 2;  // ds_bpermute addresses of the partner lanes
+  const int x32 = (lane ^ 32) << 2;
   // 1-D grid, KV head (and query sub-group) fastest, then sequence, then
   // partition.  Workgroups are dealt round-robin to the 8 XCDs by linear id,
   // so every XCD gets an equal share of heads of every sequence and every
@@ -187,10 +185,13 @@ __global__ __launch_bounds__(256) void decode_part_mfma(void* __restrict__ out, 
     for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
   bool bad = false;
 
-  for (int chunk = 0; chunk < nmine; chunk += 64) {
-    const int cnt = min(64, nmine - chunk);
+  // Lane i holds the physical id of this wave's i-th block (at most 64: the
+  // host sends partitions longer than 4096 positions to the VALU kernel).
+  if (nmine > 0) {
+    const int cnt = nmine;
+    constexpr int chunk = 0;
     int myid = 0;
-    if (lane < cnt) myid = btrow[b0 + wave + (chunk + lane) * kWaves];
+    if (lane < cnt) myid = btrow[b0 + wave + lane * kWaves];
     const bool ok = lane >= cnt || (myid >= 0 && myid < num_blocks);
     if (!__all(ok)) bad = true;
     if (!(myid >= 0 && myid < num_blocks)) myid = 0;  // never dereference a bad id
@@ -208,49 +209,51 @@ __global__ __launch_bounds__(256) void decode_part_mfma(void* __restrict__ out, 
       for (int i = 0; i < 4; ++i) vr[i] = *reinterpret_cast<const VVec*>(vb + v_lane + i * ROWB);
     };
 
-    // `valid` false: a padding step of the pipeline; every slot is masked.
+    // One tile: scores (MFMA), online-softmax update, PV (VALU).  Straight-
+    // line code (branches here make the compiler duplicate the accumulator):
+    // slots at or past `lim` (the unfilled end of a final block, or every
+    // slot of a padding step of the pipeline, `valid` false) get score -inf
+    // and their packed V words are zeroed, so garbage there cannot leak.
     auto consume = [&](int j, const uint4(&kr)[KS], const VVec(&vr)[4], bool valid) {
       const int blk = b0 + wave + (chunk + j) * kWaves;
       const int lim = valid ? L : 0;
-      const bool full = (blk + 1) * 16 <= lim;
+      const int tok0 = blk * 16 + grp * 4;  // first token of this lane's group
       f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < KS; ++k) sacc = mfma_qk<DT>(kr[k], qop[k], sacc);
       float sv[4];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) sv[jj] = sacc[jj] * qscale;
-      if (!full) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          if (blk * 16 + grp * 4 + jj >= lim) sv[jj] = kNegInf;
-      }
+      for (int jj = 0; jj < 4; ++jj) sv[jj] = tok0 + jj < lim ? sacc[jj] * qscale : kNegInf;
       float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      bm = xor16(bm, MaxOp());
-      bm = xor32(bm, MaxOp());
+      bm = xchg(bm, x16, MaxOp());
+      bm = xchg(bm, x32, MaxOp());
+      // Rescale by 2^(m_old - m_new): exactly 1 when the max did not grow.
       const float mn = fmaxf(m_run, bm);
-      if (__any(mn > m_run)) {
-        const float alpha = fast_exp2(m_run - mn);
-        l_run *= alpha;
-        static_for<GMAX>([&](auto hc) {
-          constexpr int h = decltype(hc)::value;
-          const float a = row_bcast<h>(alpha);
+      const float alpha = fast_exp2(m_run - mn);
+      m_run = mn;
+      l_run *= alpha;
+      static_for<GMAX>([&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        const float a = row_bcast<h>(alpha);
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) acc[h][e] *= a;
-        });
-        m_run = mn;
-      }
+        for (int e = 0; e < DPL; ++e) acc[h][e] *= a;
+      });
       float pv[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) pv[jj] = fast_exp2(sv[jj] - m_run);
       l_run += (pv[0] + pv[1]) + (pv[2] + pv[3]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float vf[DPL];
-        unpack_v<DT, DPL>(vr[i], vf);
-        if (!full && blk * 16 + grp * 4 + i >= lim) {
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) vf[e] = 0.f;  // unfilled slots may hold NaN
+        const uint32_t keep = tok0 + i < lim ? 0xffffffffu : 0u;
+        VVec vw = vr[i];
+        vw.x &= keep;
+        vw.y &= keep;
+        if constexpr (DPL == 8) {
+          vw.z &= keep;
+          vw.w &= keep;
         }
+        float vf[DPL];
+        unpack_v<DT, DPL>(vw, vf);
         static_for<GMAX>([&](auto hc) {
           constexpr int h = decltype(hc)::value;
           const float ph = row_bcast<h>(pv[i]);
@@ -275,11 +278,11 @@ __global__ __launch_bounds__(256) void decode_part_mfma(void* __restrict__ out, 
   }
 
   // Sum the four token groups of the wave (same head / dims, other tokens).
-  l_run = xor32(xor16(l_run, AddOp()), AddOp());
+  l_run = xchg(xchg(l_run, x16, AddOp()), x32, AddOp());
 #pragma unroll
   for (int h = 0; h < GMAX; ++h)
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[h][e] = xor32(xor16(acc[h][e], AddOp()), AddOp());
+    for (int e = 0; e < DPL; ++e) acc[h][e] = xchg(xchg(acc[h][e], x16, AddOp()), x32, AddOp());
   if (grp == 0) {
     s_m[wave][col] = m_run;
     s_l[wave][col] = l_run;
