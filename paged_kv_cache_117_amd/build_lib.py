@@ -28,6 +28,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs rather than AGPRs: the decode kernel reads its
+    # 4-register score tile straight back, and one register file keeps the
+    # 16-bit GQA<=4 kernel within 128 registers (4 waves per SIMD).
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", INCLUDE, "-I", CSRC,
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]

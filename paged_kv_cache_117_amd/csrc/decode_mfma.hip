@@ -15,10 +15,13 @@
 //    operand layout, so K goes from HBM to the matrix core with no shuffles)
 //    and the query group, padded to 16 heads with zeros, as the B operand.
 //    Lane (G, c) receives S[token 4G+j][head c], j = 0..3.
-//  * PV stays on the VALU in fp32: lane (G, c) loads dims [c*D/16, +D/16) of
-//    tokens 4G..4G+3 of the V tile and needs the weights of those tokens for
-//    every head of the group; they sit in the same 16-lane row (lane h holds
-//    head h), so one DPP row_newbcast per (token, head) delivers them.
+//  * PV stays on the VALU: lane (G, c) loads dims [c*D/16, +D/16) of tokens
+//    4G..4G+3 of the V tile and needs the weights of those tokens for every
+//    head of the group; they sit in the same 16-lane row (lane h holds head
+//    h).  Weights are packed in pairs of tokens to the KV type and delivered
+//    by one DPP row_newbcast per (token pair, head); v_dot2_f32 multiplies a
+//    pair of tokens' V values (interleaved by v_perm_b32) and accumulates in
+//    fp32 -- half the VALU instructions of per-token FMAs.
 //  * The accumulator is rescaled only when some head's running max grows
 //    (a wave-uniform branch); exponentials of unchanged maxima are exactly 1.
 //
@@ -59,6 +62,35 @@ __device__ __forceinline__ f32x4 mfma_qk(const uint4& a, const uint4& b, const f
 template <int N>
 __device__ __forceinline__ float row_bcast(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + N, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ uint32_t row_bcast_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x150 + N, 0xF, 0xF, false);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 weights rounded (nearest even) to the KV type, `a` in the low half.
+template <int DT>
+__device__ __forceinline__ uint32_t pack_pair(float a, float b) {
+  if constexpr (DT == PA_BF16) {
+    const bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    const f16x2 v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+// c + v.lo * p.lo + v.hi * p.hi in fp32 (v_dot2_f32_bf16 / v_dot2_f32_f16).
+template <int DT>
+__device__ __forceinline__ float dot2(uint32_t v, uint32_t p, float c) {
+  if constexpr (DT == PA_BF16) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v), __builtin_bit_cast(bf16x2, p), c, false);
+  } else {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, v), __builtin_bit_cast(f16x2, p), c, false);
+  }
 }
 
 // The value of lane l combined (`op`) with the value of lane l^16 (resp.
@@ -131,33 +163,26 @@ __global__ __launch_bounds__(256) void decode_part_mfma(void* __restrict__ out, 
   const int col = lane & 15;
   const int x16 = (lane ^ 16) << 2;  // ds_bpermute addresses of the partner lanes
   const int x32 = (lane ^ 32) << 2;
-  // 1-D grid, KV head (and query sub-group) fastest, then sequence, then
-  // partition.  Workgroups are dealt round-robin to the 8 XCDs by linear id,
-  // so every XCD gets an equal share of heads of every sequence and every
-  // partition index; the (mostly empty) high partitions come last.
+  // 1-D grid: KV head (and query sub-group) fastest, then sequence, then
+  // partition rank counted from the end of the sequence.  Workgroups are
+  // dealt round-robin to the 8 XCDs by linear id, so every XCD gets an equal
+  // share of heads of every sequence; ranking partitions from the end puts
+  // every sequence's partial last partition (the short work items) at the
+  // end of the dispatch order and the empty ranks at the start.
   const int hs = Hkv * nsub;
   const int idx = blockIdx.x;
   const int hsub = idx % hs;
   const int s = (idx / hs) % B;
-  const int p = idx / (hs * B);
+  const int rank = P - 1 - idx / (hs * B);  // 0 = the sequence's last partition
   const int kvh = hsub / nsub;
   const int sub = hsub - kvh * nsub;
-  int L = cl[s];
-  const bool bad_len = L < 0 || L > max_ctx;
-  if (bad_len) L = 0;
   const int hbase = kvh * g + sub * GMAX;
   const int nh = min(GMAX, g - sub * GMAX);
-  if (L == 0) {
-    if (p == 0) {
-      const float fill = bad_len ? __builtin_nanf("") : 0.f;
-      for (int i = tid; i < nh * D; i += 256) store_elem<DT>(out, ((size_t)s * Hq + hbase) * D + i, fill);
-    }
-    return;
-  }
-  const int nparts = (L + psize - 1) / psize;
-  if (p >= nparts) return;
+  const int32_t* btrow = bt + (size_t)s * maxb;
 
-  // B operand: lane (G, c) holds q[head c][dims 32k + 8G .. +8]; heads >= nh are zero.
+  // The q operand does not depend on the context length: its loads go out
+  // before the length arrives.  B operand: lane (G, c) holds
+  // q[head c][dims 32k + 8G .. +8]; heads >= nh are zero.
   uint4 qop[KS];
   {
     const char* qrow = reinterpret_cast<const char*>(q) + ((size_t)s * Hq + hbase) * ROWB + grp * 16;
@@ -166,11 +191,24 @@ __global__ __launch_bounds__(256) void decode_part_mfma(void* __restrict__ out, 
       qop[k] = col < nh ? *reinterpret_cast<const uint4*>(qrow + (size_t)col * ROWB + k * 64) : make_uint4(0, 0, 0, 0);
   }
 
+  int L = cl[s];
+  const bool bad_len = L < 0 || L > max_ctx;
+  if (bad_len) L = 0;
+  const int nparts = (L + psize - 1) / psize;
+  if (L == 0) {
+    if (rank == 0) {
+      const float fill = bad_len ? __builtin_nanf("") : 0.f;
+      for (int i = tid; i < nh * D; i += 256) store_elem<DT>(out, ((size_t)s * Hq + hbase) * D + i, fill);
+    }
+    return;
+  }
+  if (rank >= nparts) return;
+  const int p = nparts - 1 - rank;
+
   const int nblk = (L + 15) / 16;
   const int b0 = p * (psize / 16);
   const int b1 = min(b0 + psize / 16, nblk);
   const int nmine = b1 - b0 > wave ? (b1 - b0 - wave + kWaves - 1) / kWaves : 0;
-  const int32_t* btrow = bt + (size_t)s * maxb;
   const size_t blk_stride = (size_t)Hkv * 16 * ROWB;
   const size_t head_off = (size_t)kvh * 16 * ROWB;
   const int k_lane = col * ROWB + grp * 16;          // + k * 64
@@ -242,23 +280,39 @@ __global__ __launch_bounds__(256) void decode_part_mfma(void* __restrict__ out, 
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) pv[jj] = fast_exp2(sv[jj] - m_run);
       l_run += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+      // PV on packed pairs: tokens (4G, 4G+1) and (4G+2, 4G+3).  Lane h of
+      // the row packs its two weights into one 16-bit pair; v_perm_b32 puts
+      // the same dim of the two tokens side by side; v_dot2 accumulates the
+      // pair in fp32.  Masked tokens have their V words zeroed.
+      constexpr int NW = DPL / 2;  // 32-bit words per token row in this lane
+      uint32_t vw[4][NW];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t keep = tok0 + i < lim ? 0xffffffffu : 0u;
-        VVec vw = vr[i];
-        vw.x &= keep;
-        vw.y &= keep;
-        if constexpr (DPL == 8) {
-          vw.z &= keep;
-          vw.w &= keep;
+        vw[i][0] = vr[i].x & keep;
+        vw[i][1] = vr[i].y & keep;
+        if constexpr (NW == 4) {
+          vw[i][2] = vr[i].z & keep;
+          vw[i][3] = vr[i].w & keep;
         }
-        float vf[DPL];
-        unpack_v<DT, DPL>(vw, vf);
+      }
+      const uint32_t pk[2] = {pack_pair<DT>(pv[0], pv[1]), pack_pair<DT>(pv[2], pv[3])};
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2) {
+        uint32_t lo[NW], hi[NW];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          lo[w] = __builtin_amdgcn_perm(vw[2 * j2 + 1][w], vw[2 * j2][w], 0x05040100u);
+          hi[w] = __builtin_amdgcn_perm(vw[2 * j2 + 1][w], vw[2 * j2][w], 0x07060302u);
+        }
         static_for<GMAX>([&](auto hc) {
           constexpr int h = decltype(hc)::value;
-          const float ph = row_bcast<h>(pv[i]);
+          const uint32_t ph = row_bcast_u<h>(pk[j2]);
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+          for (int w = 0; w < NW; ++w) {
+            acc[h][2 * w] = dot2<DT>(lo[w], ph, acc[h][2 * w]);
+            acc[h][2 * w + 1] = dot2<DT>(hi[w], ph, acc[h][2 * w + 1]);
+          }
         });
       }
     };
