@@ -21,6 +21,8 @@ Prints ONE JSON line (rank 0, N=1):
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -29,6 +31,11 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+# Sources that define the decode kernels; a traffic record is valid only for these bytes.
+KERNEL_SOURCES = ["paged_kv_cache_117_amd/csrc/decode_mfma.hip", "paged_kv_cache_117_amd/csrc/decode.hip",
+                  "paged_kv_cache_117_amd/csrc/decode_api.hip", "paged_kv_cache_117_amd/build_lib.py"]
 METRIC = "paged decode attention KV-read GB/s (% of MI355X HBM peak); seq-steps/s"
 WORKLOAD_NAMES = {
     "c1": "tiny paged decode fp32 (4 seqs, L in {1,5,16,37}, Hq=Hkv=2, D=64)",
@@ -51,7 +58,83 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--placement", choices=["shuffled", "sequential"], default="shuffled")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 counter CSVs into profiles/decode_<config>_traffic.json")
     return ap.parse_args()
+
+
+def kernel_fingerprint():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(key):
+    path = os.path.join(PROFILES, f"decode_{key}_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    return rec if rec.get("kernel_sha") == kernel_fingerprint() else None
+
+
+def calibrate_copy():
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}))
+
+
+def _counter_means(path, kernel_pred):
+    vals = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if kernel_pred(r["Kernel_Name"]):
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
+
+
+def pmc_summary(args):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the decode partition kernel,
+    scaled by what the same counters read for a 1 GiB device copy."""
+    dec = lambda n: "decode_part" in n
+    copy = lambda n: "copy" in n.lower() or "elementwise" in n.lower()
+    fetch, nf = _counter_means(args.pmc_summary[0], dec)
+    write, _ = _counter_means(args.pmc_summary[1], dec)
+    cfetch, _ = _counter_means(args.pmc_summary[2], copy)
+    cwrite, _ = _counter_means(args.pmc_summary[3], copy)
+    gib = float(1 << 30)
+    f_fetch = gib / (cfetch["FETCH_SIZE"] * 1024)
+    f_write = gib / (cwrite["WRITE_SIZE"] * 1024)
+    rec = {
+        "config": args.config,
+        "kernel": "decode_part_mfma (pa_decode partition kernel)",
+        "kernel_sha": kernel_fingerprint(),
+        "dispatches": nf.get("FETCH_SIZE", 0),
+        "fetch_kib_per_dispatch": round(fetch["FETCH_SIZE"], 1),
+        "write_kib_per_dispatch": round(write["WRITE_SIZE"], 1),
+        "copy_fetch_kib_per_gib": round(cfetch["FETCH_SIZE"], 1),
+        "copy_write_kib_per_gib": round(cwrite["WRITE_SIZE"], 1),
+        "fetch_scale": round(f_fetch, 4),
+        "write_scale": round(f_write, 4),
+        "traffic_bytes_per_launch": int(fetch["FETCH_SIZE"] * 1024 * f_fetch + write["WRITE_SIZE"] * 1024 * f_write),
+    }
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"decode_{args.config}_traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def cpu_info():
@@ -121,6 +204,9 @@ def cpu_baseline(w, tables, budget_s):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path has no "
               "multi-GPU mode: sequences or KV heads shard across GPUs with no exchange inside "
@@ -134,6 +220,9 @@ def main():
     from workloads import make_workload
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     w = make_workload(args.config)
     eb = metrics.ELEM_BYTES[w.dtype]
     tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
@@ -261,8 +350,15 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": None,
         },
+        "traffic_note": None,
         "cpu_baseline": None,
     }
+    rec = traffic_record(args.config)
+    if rec is not None and rec.get("config") == args.config:
+        # counters cover the partition kernel; the reduce adds its partial reads and output writes
+        res["roofline"]["traffic"] = rec["traffic_bytes_per_launch"]
+        res["traffic_note"] = ("HBM bytes per partition-kernel launch from rocprofv3 FETCH_SIZE/WRITE_SIZE "
+                               "scaled by a 1 GiB copy; algorithmic bytes per launch: %d" % io_bytes)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, tables, args.cpu_seconds)
     print(json.dumps(res), flush=True)
