@@ -94,13 +94,8 @@ typedef enum {
  *   partition_size   positions per partition; 0 = 512; a positive multiple
  *                    of block_size
  *   workspace        device scratch of at least pa_decode_workspace_bytes(...)
- *                    bytes, 256-byte aligned, owned by the caller.  Its first
- *                    256 bytes are work-queue counters: they must be zero
- *                    before the workspace's first use, and every pa_decode
- *                    leaves them zero when its kernels finish (allocate it
- *                    zeroed once and reuse it).  The rest needs no
- *                    initialisation and is clobbered.  Calls that overlap in
- *                    time must not share a workspace.
+ *                    bytes (may be NULL when that is 0); 256-byte aligned;
+ *                    contents need no initialisation and are clobbered
  *   stream           hipStream_t or NULL
  * Supported: block_size 16, head_dim 64 or 128, any num_q_heads that is a
  * multiple of num_kv_heads.  `out` must not alias any input or the workspace.
@@ -112,10 +107,9 @@ pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* 
                       int max_context_len, float scale, pa_dtype_t dtype, int partition_size,
                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace pa_decode needs for these sizes: 256 for the counters,
- * plus the partition partials when max_context_len spans more than one
- * partition.  partition_size 0 means the default 512.  Returns 0 for invalid
- * sizes; pa_decode reports those. */
+/* Bytes of workspace pa_decode needs for these sizes (0 when every sequence
+ * fits one partition).  partition_size 0 means the default 512.  Returns 0
+ * for invalid sizes as well; pa_decode reports those. */
 size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
                                  int max_context_len, int partition_size);
 

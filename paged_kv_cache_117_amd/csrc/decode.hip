@@ -234,25 +234,27 @@ __global__ __launch_bounds__(64) void decode_part_valu(void* __restrict__ out, c
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Reduce: one workgroup per (query head, sequence), one thread per dim.
+// Reduce: one workgroup per (query head, sequence), one thread per dim.  A
+// row holds E entries; entry e is the merge of partitions per*e ..
+// per*(e+1)-1 (per = 1: one partition each).
 // ---------------------------------------------------------------------------
 template <int DT, int D>
 __global__ __launch_bounds__(D) void decode_reduce(void* __restrict__ out, const int32_t* __restrict__ cl,
                                                    const float* __restrict__ ws_o, const float* __restrict__ ws_m,
                                                    const float* __restrict__ ws_l, int Hq, int max_ctx, int psize,
-                                                   int P) {
+                                                   int E, int per) {
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int d = threadIdx.x;
   const int L = cl[s];
   if (L < 0 || L > max_ctx) return;
-  const int nparts = (L + psize - 1) / psize;
-  if (nparts <= 1) return;
-  const size_t base = ((size_t)s * Hq + h) * P;
+  const int nent = ((L + psize - 1) / psize + per - 1) / per;  // this sequence's entries
+  if (nent <= 1) return;  // written by the partition kernel
+  const size_t base = ((size_t)s * Hq + h) * E;
   float M = kNegInf;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ws_m[base + p]);
+  for (int p = 0; p < nent; ++p) M = fmaxf(M, ws_m[base + p]);
   float num = 0.f, den = 0.f;
-  for (int p = 0; p < nparts; ++p) {
+  for (int p = 0; p < nent; ++p) {
     const float w = ws_l[base + p] * fast_exp2(ws_m[base + p] - M);
     den += w;
     num = fmaf(w, ws_o[(base + p) * D + d], num);
@@ -283,7 +285,7 @@ void launch_valu_g(const DecodeArgs& a, hipStream_t st) {
 template <int DT, int D>
 void launch_reduce(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((decode_reduce<DT, D>), dim3(a.Hq, a.B), dim3(D), 0, st, a.out, a.cl, a.ws_o, a.ws_m, a.ws_l,
-                     a.Hq, a.max_ctx, a.psize, a.P);
+                     a.Hq, a.max_ctx, a.psize, a.entries, a.per_entry);
 }
 
 template <int DT>

@@ -6,8 +6,6 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include <atomic>
-
 #include "decode_kernels.h"
 #include "pa_internal.h"
 
@@ -17,37 +15,14 @@ constexpr int kDefaultPartition = 512;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// PA_DECODE_KERNEL=valu selects the VALU partition kernel for 16-bit KV too,
-// PA_DECODE_KERNEL=grid the one-workgroup-per-item MFMA kernel instead of the
-// persistent one (read once; for comparisons).
-const char* kernel_override() {
-  static const char* v = getenv("PA_DECODE_KERNEL");
-  return v ? v : "";
-}
-bool force_valu() { return strcmp(kernel_override(), "valu") == 0; }
-bool force_grid() { return strcmp(kernel_override(), "grid") == 0; }
-
-// Resident workgroups of the persistent kernel on the current device: CUs x
-// workgroups per CU (from the kernel's registers and LDS), cached.
-int persistent_slots(pa_dtype_t dtype, int head_dim, int gmax) {
-  static std::atomic<int> occ_cache[2][2][2];
-  static std::atomic<int> cu_cache[64];
-  const void* fn = pa::decode_persist_kernel(dtype, head_dim, gmax);
-  if (!fn) return 0;
-  std::atomic<int>& occ = occ_cache[dtype == PA_FP16][head_dim == 128][gmax == 8];
-  if (occ.load() == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, pa::kPersistThreads, 0) != hipSuccess || n <= 0) return 0;
-    occ.store(n);
-  }
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cu_cache[dev].load() == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
-    cu_cache[dev].store(n);
-  }
-  return occ.load() * cu_cache[dev].load();
+// PA_DECODE_KERNEL=valu selects the VALU partition kernel for 16-bit KV too
+// (read once; for comparisons).
+bool force_valu() {
+  static const bool v = [] {
+    const char* e = getenv("PA_DECODE_KERNEL");
+    return e && strcmp(e, "valu") == 0;
+  }();
+  return v;
 }
 
 int parts_for(int max_ctx, int psize) { return max_ctx <= 0 ? 1 : (max_ctx + psize - 1) / psize; }
@@ -94,10 +69,12 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
 
   const int P = parts_for(max_context_len, psize);
   const WorkspaceLayout wl = workspace_layout(num_seqs, num_q_heads, head_dim, P);
-  if (!workspace) return fail(PA_ERR_WORKSPACE, "pa_decode: needs %zu bytes of workspace, got NULL", wl.total);
-  if (workspace_bytes < wl.total)
-    return fail(PA_ERR_WORKSPACE, "pa_decode: needs %zu bytes of workspace, got %zu", wl.total, workspace_bytes);
-  if (!aligned(workspace, 256)) return fail(PA_ERR_WORKSPACE, "pa_decode: workspace must be 256-byte aligned");
+  if (wl.total > 0) {
+    if (!workspace) return fail(PA_ERR_WORKSPACE, "pa_decode: needs %zu bytes of workspace, got NULL", wl.total);
+    if (workspace_bytes < wl.total)
+      return fail(PA_ERR_WORKSPACE, "pa_decode: needs %zu bytes of workspace, got %zu", wl.total, workspace_bytes);
+    if (!aligned(workspace, 256)) return fail(PA_ERR_WORKSPACE, "pa_decode: workspace must be 256-byte aligned");
+  }
 
   DecodeArgs a{};
   a.out = out;
@@ -107,20 +84,19 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
   a.bt = block_tables;
   a.cl = context_lens;
   char* ws = static_cast<char*>(workspace);
-  a.ctr = reinterpret_cast<uint32_t*>(ws + wl.ctr_off);
-  a.ws_o = P > 1 ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr;
-  a.ws_m = P > 1 ? reinterpret_cast<float*>(ws + wl.m_off) : nullptr;
-  a.ws_l = P > 1 ? reinterpret_cast<float*>(ws + wl.l_off) : nullptr;
+  a.ws_o = wl.total ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr;
+  a.ws_m = wl.total ? reinterpret_cast<float*>(ws + wl.m_off) : nullptr;
+  a.ws_l = wl.total ? reinterpret_cast<float*>(ws + wl.l_off) : nullptr;
   a.B = num_seqs;
   a.Hq = num_q_heads;
   a.Hkv = num_kv_heads;
   a.g = num_q_heads / num_kv_heads;
-  // MFMA kernel: 16-bit KV, partitions of at most 4096 positions (each of its
-  // 4 waves walks at most 64 blocks).  Everything else: the VALU kernel.
+  // MFMA kernels: 16-bit KV, partitions of at most 4096 positions (a wave
+  // holds at most 64 block ids).  Everything else: the VALU kernel.
   const bool mfma = dtype != PA_FP32 && psize <= 4096 && !force_valu();
-  // Query heads per work item: the MFMA kernel takes up to 16 (one matrix
-  // column each, sized 4, 8 or 16 for its merge buffer); the VALU kernel
-  // 1, 2, 4 or 8 (one accumulator set each).
+  // Query heads per work item: the MFMA kernels take up to 16 (one matrix
+  // column each; 4, 8 or 16 sizes their LDS staging), the VALU kernel 1, 2,
+  // 4 or 8 (one accumulator set each).
   if (mfma)
     a.gmax = a.g <= 4 ? 4 : a.g <= 8 ? 8 : 16;
   else
@@ -134,26 +110,21 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
   a.P = P;
   a.qscale = scale * 1.4426950408889634f;
   a.dtype = dtype;
-  if ((int64_t)P * num_kv_heads * a.nsub * num_seqs > 0x7fffffffLL)
+  // Partitions of up to 64 blocks: one wavefront each, and the workgroup's
+  // four partitions merged into one workspace entry.
+  a.wave_part = mfma && psize / block_size <= 64;
+  a.per_entry = a.wave_part ? 4 : 1;
+  a.entries = (P + a.per_entry - 1) / a.per_entry;
+  if ((int64_t)a.entries * num_kv_heads * a.nsub * num_seqs > 0x7fffffffLL)
     return fail(PA_ERR_SHAPE, "pa_decode: launch of %lld workgroups is too large",
-                (long long)P * num_kv_heads * a.nsub * num_seqs);
-
-  // Persistent MFMA kernel: batches whose lengths fit its LDS tables, query
-  // groups of up to 8 heads.  Grid = resident slots, at most one per item.
-  a.persist_grid = 0;
-  if (mfma && num_seqs <= kPersistMaxSeqs && (a.gmax == 4 || a.gmax == 8) && !force_grid()) {
-    const int64_t items = (int64_t)P * num_kv_heads * a.nsub * num_seqs;
-    const int slots = persistent_slots(dtype, head_dim, a.gmax);
-    a.persist_grid = (int)(items < slots ? items : slots);
-  }
+                (long long)a.entries * num_kv_heads * a.nsub * num_seqs);
 
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (mfma) {
+  if (mfma)
     launch_decode_mfma(a, st);
-  } else {
+  else
     launch_decode_valu(a, st);
-    if (a.P > 1) launch_decode_reduce(a, st);
-  }
+  if (a.entries > 1) launch_decode_reduce(a, st);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "pa_decode: launch failed: %s", hipGetErrorString(e));
   return PA_OK;

@@ -24,4 +24,4 @@ void clear_error() { g_msg[0] = '\0'; }
 
 extern "C" const char* pa_last_error(void) { return g_msg; }
 
-extern "C" int pa_abi_version(void) { return 2; }
+extern "C" int pa_abi_version(void) { return 1; }

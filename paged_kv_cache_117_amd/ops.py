@@ -94,8 +94,7 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_cont
         raise ValueError("out must have q's shape")
     need = decode_workspace_bytes(B, Hq, D, max_context_len, partition_size)
     if workspace is None:
-        # zeroed: its first 256 bytes are the kernels' work-queue counters
-        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device) if need else None
     if workspace is not None:
         _device_tensor(workspace, "workspace")
     ws_ptr = workspace.data_ptr() if workspace is not None else None

@@ -28,16 +28,16 @@ def test_every_declared_symbol_is_exported_and_bound():
 
 
 def test_abi_version():
-    assert pa.abi_version() == 2
+    assert pa.abi_version() == 1
 
 
 def test_workspace_bytes():
-    # one partition -> only the 256 bytes of work-queue counters
-    assert pa.decode_workspace_bytes(4, 2, 64, 37, 0) == 256
-    assert pa.decode_workspace_bytes(64, 32, 128, 512, 512) == 256
-    # 8 partitions of 512 for 4096 tokens: counters, then o [B][Hq][P][D] + m + l, each 256-aligned
+    # one partition -> no workspace
+    assert pa.decode_workspace_bytes(4, 2, 64, 37, 0) == 0
+    assert pa.decode_workspace_bytes(64, 32, 128, 512, 512) == 0
+    # 8 partitions of 512 for 4096 tokens: o [B][Hq][P][D] + m + l, each 256-aligned
     rows = 64 * 32 * 8
-    assert pa.decode_workspace_bytes(64, 32, 128, 4096, 0) == 256 + rows * 128 * 4 + 2 * rows * 4
+    assert pa.decode_workspace_bytes(64, 32, 128, 4096, 0) == rows * 128 * 4 + 2 * rows * 4
     assert pa.decode_workspace_bytes(0, 32, 128, 4096, 0) == 0
 
 
@@ -58,7 +58,7 @@ def call_decode(**kw):
     (dict(bs=8), 3), (dict(D=96), 3), (dict(dt=7), 3),
     (dict(Hq=3, Hkv=2), 2), (dict(maxctx=33), 2), (dict(ps=24), 2), (dict(B=-1), 2),
     (dict(scale=float("inf")), 2), (dict(q=NULL), 1), (dict(out=8), 2),
-    (dict(maxctx=600, maxb=64), 4), (dict(), 4),
+    (dict(maxctx=600, maxb=64), 4),
 ])
 def test_decode_host_validation(kw, status):
     """Rejected before any device work (these calls never reach the GPU)."""
