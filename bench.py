@@ -268,7 +268,7 @@ def main():
             slots=dev(slots + r * nb * w.block_size),
             pairs=dev((pairs + r * nb).astype(np.int32)) if len(pairs) else None,
             out=torch.empty_like(q),
-            ws=torch.empty(max(1, pa.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.head_dim,
+            ws=torch.empty(max(1, pa.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                                             w.max_context_len, args.partition_size)),
                            dtype=torch.uint8, device="cuda"),
         ))

@@ -75,11 +75,18 @@ typedef enum {
  * attention over non-contiguous blocks").  A decode step writes the step's
  * own token first (pa_write_kv), so L counts it.
  *
- * The context is processed in partitions of `partition_size` positions with
- * an online (running max / sum) softmax (PagedAttention (tensortonic), "10.
- * How PagedAttention Fits with FlashAttention"); sequences longer than one
- * partition are merged by a log-sum-exp weighted reduce, because softmax
- * must normalise over all valid positions at once (same page, section 5).
+ * The context is processed in pieces with an online (running max / sum)
+ * softmax (PagedAttention (tensortonic), "10. How PagedAttention Fits with
+ * FlashAttention"); a sequence split over several pieces is merged by a
+ * log-sum-exp weighted reduce, because softmax must normalise over all valid
+ * positions at once (same page, section 5).  With partition_size > 0 the
+ * pieces are whole partitions of that many positions (several consecutive
+ * partitions of one sequence may be merged on the fly by the same rule).
+ * With partition_size 0, 16-bit KV and up to 4096 sequences, the batch's
+ * blocks are split evenly over the GPU's wavefronts, cutting sequences at
+ * block boundaries wherever the even split falls; otherwise partitions of
+ * 512 positions are used.  Every choice computes the same attention; results
+ * differ only by fp32 rounding order.
  *
  *   out              device, [num_seqs][num_q_heads][head_dim], dtype; written
  *   q                device, [num_seqs][num_q_heads][head_dim], dtype
@@ -91,8 +98,8 @@ typedef enum {
  *   max_context_len  host hint >= every context_lens[s]; sizes the launch;
  *                    must be <= max_blocks_per_seq * block_size
  *   scale            softmax scale (typically 1/sqrt(head_dim)), finite
- *   partition_size   positions per partition; 0 = 512; a positive multiple
- *                    of block_size
+ *   partition_size   positions per partition, a positive multiple of
+ *                    block_size; 0 = automatic (see above)
  *   workspace        device scratch of at least pa_decode_workspace_bytes(...)
  *                    bytes (may be NULL when that is 0); 256-byte aligned;
  *                    contents need no initialisation and are clobbered
@@ -107,10 +114,13 @@ pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* 
                       int max_context_len, float scale, pa_dtype_t dtype, int partition_size,
                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace pa_decode needs for these sizes (0 when every sequence
- * fits one partition).  partition_size 0 means the default 512.  Returns 0
- * for invalid sizes as well; pa_decode reports those. */
-size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
+/* Bytes of workspace pa_decode needs for these sizes and any dtype: partials
+ * of the partitions (none when every sequence fits one partition) and, for
+ * batches of up to 4096 sequences, the pieces of the even split (a fixed
+ * number of slots of num_q_heads / num_kv_heads rows, at most 16).  The
+ * value does not depend on the device.  Returns 0 for invalid sizes as well;
+ * pa_decode reports those. */
+size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                  int max_context_len, int partition_size);
 
 /*

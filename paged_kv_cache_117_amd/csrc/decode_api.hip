@@ -6,6 +6,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "decode_kernels.h"
 #include "pa_internal.h"
 
@@ -15,25 +17,53 @@ constexpr int kDefaultPartition = 512;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// PA_DECODE_KERNEL=valu selects the VALU partition kernel for 16-bit KV too
-// (read once; for comparisons).
-bool force_valu() {
-  static const bool v = [] {
-    const char* e = getenv("PA_DECODE_KERNEL");
-    return e && strcmp(e, "valu") == 0;
-  }();
-  return v;
+// PA_DECODE_KERNEL=valu selects the VALU partition kernel for 16-bit KV too,
+// PA_DECODE_KERNEL=partition the MFMA partition kernels instead of the
+// balanced split (read once; for comparisons).
+const char* kernel_override() {
+  static const char* v = getenv("PA_DECODE_KERNEL");
+  return v ? v : "";
+}
+bool force_valu() { return strcmp(kernel_override(), "valu") == 0; }
+bool force_partition() { return strcmp(kernel_override(), "partition") == 0; }
+
+// Compute units of the current device (cached per device); 256 if the
+// query fails.
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load();
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n);
+  }
+  return n;
 }
 
 int parts_for(int max_ctx, int psize) { return max_ctx <= 0 ? 1 : (max_ctx + psize - 1) / psize; }
 
+// Upper bound of the balanced split's units (every sequence at max_ctx).
+int64_t stream_units_bound(int B, int Hq, int Hkv, int max_ctx, int unit) {
+  const int g = Hq / Hkv, gmax = pa::mfma_gmax(g), nsub = (g + gmax - 1) / gmax;
+  const int64_t per_seg = ((int64_t)(max_ctx + 15) / 16 + unit - 1) / unit;
+  return (int64_t)B * Hkv * nsub * per_seg;
+}
+
 }  // namespace
 
-extern "C" size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int max_context_len,
-                                            int partition_size) {
+extern "C" size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                            int max_context_len, int partition_size) {
   const int psize = partition_size == 0 ? kDefaultPartition : partition_size;
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 || psize <= 0) return 0;
-  return pa::workspace_layout(num_seqs, num_q_heads, head_dim, parts_for(max_context_len, psize)).total;
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || head_dim <= 0 ||
+      max_context_len < 0 || psize <= 0)
+    return 0;
+  size_t need = pa::workspace_layout(num_seqs, num_q_heads, head_dim, parts_for(max_context_len, psize)).total;
+  if (num_seqs <= pa::kStreamMaxSeqs) {
+    const size_t st = pa::stream_layout(num_seqs, num_q_heads, num_kv_heads, head_dim).total;
+    if (st > need) need = st;
+  }
+  return need;
 }
 
 extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -68,11 +98,25 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
     return fail(PA_ERR_SHAPE, "pa_decode: out, q and the pools must be 16-byte aligned");
 
   const int P = parts_for(max_context_len, psize);
+  const int g = num_q_heads / num_kv_heads;
+  // Balanced split: 16-bit KV, batches whose lengths fit its LDS table.
+  // Units are single blocks unless a partition size is given.
+  const bool half = dtype != PA_FP32 && !force_valu();
+  const int unit = partition_size == 0 ? 1 : psize / block_size;
+  // (its tile descriptors hold block * num_kv_heads + head in 28 bits)
+  const bool use_stream = half && num_seqs <= kStreamMaxSeqs && !force_partition() &&
+                          stream_units_bound(num_seqs, num_q_heads, num_kv_heads, max_context_len, unit) < (1 << 30) &&
+                          (int64_t)num_blocks * num_kv_heads < (1 << 28);
+  // MFMA partition kernels: 16-bit KV, partitions of at most 4096 positions
+  // (a wave holds at most 64 block ids).  Everything else: the VALU kernel.
+  const bool mfma = half && (use_stream || psize <= 4096);
   const WorkspaceLayout wl = workspace_layout(num_seqs, num_q_heads, head_dim, P);
-  if (wl.total > 0) {
-    if (!workspace) return fail(PA_ERR_WORKSPACE, "pa_decode: needs %zu bytes of workspace, got NULL", wl.total);
-    if (workspace_bytes < wl.total)
-      return fail(PA_ERR_WORKSPACE, "pa_decode: needs %zu bytes of workspace, got %zu", wl.total, workspace_bytes);
+  const StreamLayout sl = stream_layout(num_seqs, num_q_heads, num_kv_heads, head_dim);
+  const size_t need = use_stream ? sl.total : wl.total;
+  if (need > 0) {
+    if (!workspace) return fail(PA_ERR_WORKSPACE, "pa_decode: needs %zu bytes of workspace, got NULL", need);
+    if (workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "pa_decode: needs %zu bytes of workspace, got %zu", need, workspace_bytes);
     if (!aligned(workspace, 256)) return fail(PA_ERR_WORKSPACE, "pa_decode: workspace must be 256-byte aligned");
   }
 
@@ -84,23 +128,24 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
   a.bt = block_tables;
   a.cl = context_lens;
   char* ws = static_cast<char*>(workspace);
-  a.ws_o = wl.total ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr;
-  a.ws_m = wl.total ? reinterpret_cast<float*>(ws + wl.m_off) : nullptr;
-  a.ws_l = wl.total ? reinterpret_cast<float*>(ws + wl.l_off) : nullptr;
+  if (use_stream) {
+    a.ws_o = reinterpret_cast<float*>(ws + sl.o_off);
+    a.ws_m = reinterpret_cast<float*>(ws + sl.m_off);
+    a.ws_l = reinterpret_cast<float*>(ws + sl.l_off);
+    a.info = reinterpret_cast<int2*>(ws + sl.info_off);
+  } else if (wl.total) {
+    a.ws_o = reinterpret_cast<float*>(ws + wl.o_off);
+    a.ws_m = reinterpret_cast<float*>(ws + wl.m_off);
+    a.ws_l = reinterpret_cast<float*>(ws + wl.l_off);
+  }
   a.B = num_seqs;
   a.Hq = num_q_heads;
   a.Hkv = num_kv_heads;
-  a.g = num_q_heads / num_kv_heads;
-  // MFMA kernels: 16-bit KV, partitions of at most 4096 positions (a wave
-  // holds at most 64 block ids).  Everything else: the VALU kernel.
-  const bool mfma = dtype != PA_FP32 && psize <= 4096 && !force_valu();
+  a.g = g;
   // Query heads per work item: the MFMA kernels take up to 16 (one matrix
-  // column each; 4, 8 or 16 sizes their LDS staging), the VALU kernel 1, 2,
-  // 4 or 8 (one accumulator set each).
-  if (mfma)
-    a.gmax = a.g <= 4 ? 4 : a.g <= 8 ? 8 : 16;
-  else
-    a.gmax = a.g >= 8 ? 8 : a.g > 2 ? 4 : a.g;
+  // column each; 4, 8 or 16 sizes their buffers), the VALU kernel 1, 2, 4
+  // or 8 (one accumulator set each).
+  a.gmax = mfma ? mfma_gmax(g) : g >= 8 ? 8 : g > 2 ? 4 : g;
   a.nsub = (a.g + a.gmax - 1) / a.gmax;
   a.D = head_dim;
   a.num_blocks = num_blocks;
@@ -110,21 +155,35 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
   a.P = P;
   a.qscale = scale * 1.4426950408889634f;
   a.dtype = dtype;
-  // Partitions of up to 64 blocks: one wavefront each, and the workgroup's
-  // four partitions merged into one workspace entry.
-  a.wave_part = mfma && psize / block_size <= 64;
-  a.per_entry = a.wave_part ? 4 : 1;
-  a.entries = (P + a.per_entry - 1) / a.per_entry;
-  if ((int64_t)a.entries * num_kv_heads * a.nsub * num_seqs > 0x7fffffffLL)
-    return fail(PA_ERR_SHAPE, "pa_decode: launch of %lld workgroups is too large",
-                (long long)a.entries * num_kv_heads * a.nsub * num_seqs);
+  a.stream = use_stream;
+  if (use_stream) {
+    // One workgroup of 4 independent wavefronts per CU (4 wavefronts with
+    // two tiles in flight each keep a CU's share of HBM busy), and never
+    // more wavefronts than units.
+    a.unit = unit;
+    const int64_t units = stream_units_bound(num_seqs, num_q_heads, num_kv_heads, max_context_len, unit);
+    int64_t grid = cu_count();
+    if (grid > kStreamMaxWaves / 4) grid = kStreamMaxWaves / 4;
+    if (grid > (units + 3) / 4) grid = (units + 3) / 4;
+    a.grid = grid < 1 ? 1 : (int)grid;
+    a.entries = 1;
+  } else {
+    // Partitions of up to 64 blocks: one wavefront each, and the
+    // workgroup's four partitions merged into one workspace entry.
+    a.wave_part = mfma && psize / block_size <= 64;
+    a.per_entry = a.wave_part ? 4 : 1;
+    a.entries = (P + a.per_entry - 1) / a.per_entry;
+    if ((int64_t)a.entries * num_kv_heads * a.nsub * num_seqs > 0x7fffffffLL)
+      return fail(PA_ERR_SHAPE, "pa_decode: launch of %lld workgroups is too large",
+                  (long long)a.entries * num_kv_heads * a.nsub * num_seqs);
+  }
 
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (mfma)
     launch_decode_mfma(a, st);
   else
     launch_decode_valu(a, st);
-  if (a.entries > 1) launch_decode_reduce(a, st);
+  if (!a.stream && a.entries > 1) launch_decode_reduce(a, st);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "pa_decode: launch failed: %s", hipGetErrorString(e));
   return PA_OK;

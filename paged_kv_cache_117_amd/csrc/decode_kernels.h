@@ -19,6 +19,10 @@ struct DecodeArgs {
   float* ws_o;  // [B][Hq][entries][D] partition (group) outputs, normalised
   float* ws_m;  // [B][Hq][entries] running max, base-2 domain
   float* ws_l;  // [B][Hq][entries] running sum
+  int2* info;     // balanced split: [B][Hkv * nsub] (first piece slot, piece count) per segment
+  int stream;     // balanced-split kernel (ws_o / ws_m / ws_l hold its pieces)
+  int unit;       // balanced split: blocks per unit of work
+  int grid;       // balanced split: workgroups
   int wave_part;  // MFMA kernels: one wavefront per partition (partitions of <= 64 blocks)
   int entries;    // partial entries per (sequence, query head) row of the workspace actually used
   int per_entry;  // partitions merged into one entry: ceil(nparts / per_entry) entries per sequence
@@ -47,9 +51,35 @@ inline WorkspaceLayout workspace_layout(size_t B, size_t Hq, size_t D, size_t P)
   return w;
 }
 
+// Balanced split: batches up to this many sequences (their lengths are
+// staged in LDS), at most this many wavefronts (two piece slots each).
+constexpr int kStreamMaxSeqs = 4096;
+constexpr int kStreamMaxWaves = 4096;
+
+// Query heads per work item of the MFMA kernels (one matrix column each).
+inline int mfma_gmax(int g) { return g <= 4 ? 4 : g <= 8 ? 8 : 16; }
+
+// Workspace of the balanced split: pieces (o [slot][gmax][D], m and l
+// [slot][gmax]) for 2 * kStreamMaxWaves slots, then the segment records.
+struct StreamLayout {
+  size_t o_off, m_off, l_off, info_off, total;
+};
+
+inline StreamLayout stream_layout(size_t B, size_t Hq, size_t Hkv, size_t D) {
+  const size_t g = Hq / Hkv, gmax = (size_t)mfma_gmax((int)g), nsub = (g + gmax - 1) / gmax;
+  const size_t slots = 2 * (size_t)kStreamMaxWaves;
+  StreamLayout w{};
+  w.o_off = 0;
+  w.m_off = align256(slots * gmax * D * sizeof(float));
+  w.l_off = w.m_off + align256(slots * gmax * sizeof(float));
+  w.info_off = w.l_off + align256(slots * gmax * sizeof(float));
+  w.total = w.info_off + align256(B * Hkv * nsub * 2 * sizeof(int));
+  return w;
+}
+
 // Partition kernels (the reduce is launched separately when P > 1).
 void launch_decode_valu(const DecodeArgs& a, hipStream_t st);   // any dtype
-void launch_decode_mfma(const DecodeArgs& a, hipStream_t st);   // fp16 / bf16
+void launch_decode_mfma(const DecodeArgs& a, hipStream_t st);   // fp16 / bf16; the balanced split launches its own reduce
 void launch_decode_reduce(const DecodeArgs& a, hipStream_t st);
 
 }  // namespace pa

@@ -28,14 +28,21 @@
 // NaN/Inf garbage there never reaches the result.  Block ids outside
 // [0, num_blocks) are never dereferenced: the result is NaN instead.
 //
-// Two kernels share this tile code:
-//  * decode_part_wave (partitions of up to 64 blocks): one wavefront per
-//    partition, four consecutive partitions per workgroup, merged in LDS into
-//    one entry (the final row, or a partial for the reduce) per workgroup.
-//  * decode_part_mfma (partitions of 65..256 blocks): the four wavefronts of
-//    a workgroup share one partition, blocks dealt round-robin.
-// Both stage each wave's (m, l) and normalised rows in LDS and write the
-// workgroup's entry with the same log-sum-exp merge as the reduce kernel.
+// Three kernels share this tile code:
+//  * decode_stream (batches of up to 4096 sequences): a persistent grid whose
+//    wavefronts each stream an equal share of the batch's blocks, cutting
+//    sequences wherever the even split falls; decode_stream_reduce merges
+//    the cut ones.
+//  * decode_part_wave (larger batches, partitions of up to 64 blocks): one
+//    wavefront per partition, four consecutive partitions per workgroup,
+//    merged in LDS into one entry (the final row, or a partial for the
+//    reduce) per workgroup.
+//  * decode_part_mfma (larger batches, partitions of 65..256 blocks): the
+//    four wavefronts of a workgroup share one partition, blocks dealt
+//    round-robin.
+// The partition kernels stage each wave's (m, l) and normalised rows in LDS
+// and write the workgroup's entry with the same log-sum-exp merge as the
+// reduce kernel.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -306,6 +313,20 @@ __device__ __forceinline__ void merge_write(const float (*sm)[16], const float (
   }
 }
 
+// N consecutive output elements (8 or 4 of a 16-bit type: 16 or 8 bytes)
+// from fp32, rounded to nearest even.
+template <int DT, int N>
+__device__ __forceinline__ void store_row(void* out, size_t idx, const float* f) {
+  static_assert(N == 8 || N == 4, "16 or 8 bytes");
+  if constexpr (N == 8) {
+    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(out) + idx * 2) = pack16<DT>(f);
+  } else {
+    const float g8[8] = {f[0], f[1], f[2], f[3], 0.f, 0.f, 0.f, 0.f};
+    const uint4 v = pack16<DT>(g8);
+    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(out) + idx * 2) = make_uint2(v.x, v.y);
+  }
+}
+
 // The rows of a sequence with L = 0: zero (NaN for an invalid length).
 template <int DT, int D>
 __device__ __forceinline__ void fill_rows(void* out, size_t row0, int nh, bool bad_len) {
@@ -540,8 +561,397 @@ __global__ __launch_bounds__(256) void decode_part_mfma(void* __restrict__ out, 
           ws_o, ws_m, ws_l);
 }
 
+// ---------------------------------------------------------------------------
+// Balanced split: every wavefront of a persistent grid streams the same
+// amount of KV.
+//
+// HBM throughput of this gather is set by the whole chip (every CU with a
+// few tiles in flight saturates it), so a launch takes as long as its most
+// loaded CU: with one workgroup per partition, ragged batches leave a long
+// tail of a few busy CUs.  Here the work is cut into units (one block, or
+// one partition when a partition size is given) in (sequence, head group,
+// block) order, and wave w of W takes units [w Q / W, (w+1) Q / W) of the Q
+// in the batch.  A wave's range can start and end inside a (sequence, head
+// group) segment and cross whole segments in between: a segment it covers
+// whole is written as final rows, a cut one as a piece (normalised o, m, l)
+// in slot 2w (the wave's first segment) or 2w+1 (its last), and the reduce
+// merges a cut segment's pieces with the same log-sum-exp weights as the
+// partition reduce.  The wave holding a segment's first unit records where
+// its pieces are.
+//
+// A wave works in chunks of up to kChunkTiles tiles: it first stages the
+// chunk's pieces (portions of segments), one descriptor per tile (physical
+// row of the tile's block and head, last filled slot) and the pieces' query
+// rows in its part of LDS, with all loads in flight at once; then one tile
+// pipeline runs through the whole chunk, across piece boundaries, writing
+// each finished piece from registers.  Workgroups are dealt round-robin to
+// the 8 XCDs: workgroup i takes the (i mod 8)-th eighth of the stream, so
+// each XCD's L2 sees a contiguous run of sequences (shared prefix blocks of
+// neighbouring sequences hit there).
+// ---------------------------------------------------------------------------
+constexpr int kChunkTiles = 512;   // tile descriptors per wave and chunk
+constexpr int kChunkPieces = 32;   // pieces per wave and chunk
+constexpr int kChunkQRows = 48;    // query rows per wave and chunk
+
+struct Piece {
+  int bt0;    // block-table index of the portion's first tile
+  int tb;     // the sequence's block index of that tile
+  int kb;     // chunk tile index of that tile
+  int nt;     // tiles in this chunk
+  int L;      // context length
+  int kvh;    // KV head
+  int qrow;   // first query row in the wave's LDS rows
+  int nh;     // query heads
+  int row0;   // first output row
+  int seg;    // s * hs + hsub
+  int np;     // pieces of the segment (valid with kFirstUnit)
+  int flags;  // kWhole | kEnds | kFirstUnit | kLastSlot | kStarts
+  int bad;    // an invalid block id in this portion
+};
+constexpr int kWhole = 1, kEnds = 2, kFirstUnit = 4, kLastSlot = 8, kStarts = 16;
+
+template <int DT, int D, int GMAX>
+__global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, const void* __restrict__ q,
+                                                    const char* kp, const char* vp, const int32_t* __restrict__ bt,
+                                                    const int32_t* __restrict__ cl, float* __restrict__ pc_o,
+                                                    float* __restrict__ pc_m, float* __restrict__ pc_l,
+                                                    int2* __restrict__ info, int B, int Hq, int Hkv, int g, int nsub,
+                                                    int num_blocks, int maxb, int max_ctx, float qscale, int unit) {
+  using T = Tile<DT, D>;
+  constexpr int KS = T::KS, DPL = T::DPL, ROWB = T::ROWB, QROW = T::QROW, QCH = T::QCH;
+  using VVec = typename T::VVec;
+  static_assert(GMAX <= 16, "one MFMA column per query head");
+  __shared__ int s_len[kStreamMaxSeqs];  // context length, -1 when out of range
+  __shared__ unsigned s_desc[kWaves][kChunkTiles];
+  __shared__ Piece s_pc[kWaves][kChunkPieces];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[kWaves][kChunkQRows + 1][QROW];  // last row: zeros
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uni(tid >> 6);
+  const int grp = lane >> 4;
+  const int col = lane & 15;
+  const int x16 = (lane ^ 16) << 2;
+  const int x32 = (lane ^ 32) << 2;
+  const int hs = Hkv * nsub;  // segments per sequence
+
+  for (int i = tid; i < B; i += 256) {
+    const int L = cl[i];
+    s_len[i] = (L < 0 || L > max_ctx) ? -1 : L;
+  }
+  for (int i = lane; i < QROW / 8; i += 64) *reinterpret_cast<uint4*>(&s_q[wave][kChunkQRows][i * 8]) = make_uint4(0, 0, 0, 0);
+  lds_barrier();
+  // Rows of sequences without positions: zero (NaN for an invalid length),
+  // dealt round-robin to the workgroups.
+  for (int s = blockIdx.x; s < B; s += gridDim.x) {
+    const int L = uni(s_len[s]);
+    if (L > 0) continue;
+    const float fill = L < 0 ? __builtin_nanf("") : 0.f;
+    for (int i = tid; i < Hq * D; i += 256) store_elem<DT>(out, (size_t)s * Hq * D + i, fill);
+  }
+  auto seg_units = [&](int L) { return L <= 0 ? 0 : ((L + 15) / 16 + unit - 1) / unit; };
+
+  // Q, then this wave's range (waves past the first Q have none).  Virtual
+  // workgroup v: the XCD's share of the stream, in order.
+  int qt = 0;
+  for (int i = lane; i < B; i += 64) qt += seg_units(s_len[i]);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) qt += __shfl_xor(qt, d);
+  qt = uni(qt) * hs;
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x & 7, n8 = G >> 3, r8 = G & 7;
+  const int v = xcd * n8 + min(xcd, r8) + (blockIdx.x >> 3);
+  const int W = min(G * kWaves, qt);
+  const int w = v * kWaves + wave;
+  if (w >= W) return;
+  const int u_lo = (int)((long long)w * qt / W);
+  const int u_hi = (int)((long long)(w + 1) * qt / W);
+
+  // The sequence holding unit u_lo: prefix sums of units per sequence, 64
+  // sequences at a time.
+  int s = 0, pre = 0;
+  for (int c0 = 0, base = 0; c0 < B; c0 += 64) {
+    const int i = c0 + lane;
+    const int us = i < B ? seg_units(s_len[i]) * hs : 0;
+    int incl = us;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(incl, d);
+      if (lane >= d) incl += t;
+    }
+    const int excl = base + incl - us;
+    const unsigned long long hit = __ballot(us > 0 && excl <= u_lo && u_lo < excl + us);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      s = c0 + l;
+      pre = __shfl(excl, l);
+      break;
+    }
+    base += __shfl(incl, 63);
+  }
+  s = uni(s);
+  const int off0 = u_lo - uni(pre);  // units of s before u_lo
+  const int us0 = seg_units(uni(s_len[s]));
+  if (us0 <= 0) return;  // (cannot happen: s holds unit u_lo)
+  int hsub = off0 / us0;        // walker: segment within the sequence,
+  int uin = off0 - hsub * us0;  // unit within the segment where the current piece starts,
+  int u = u_lo;                 // its unit in the stream,
+  int tdone = 0;                // and its tiles staged by earlier chunks
+  bool first = true;            // the wave's first piece (slot 2w)
+
+  Piece* pcs = s_pc[wave];
+  unsigned* desc = s_desc[wave];
+  uint16_t (*sq)[QROW] = s_q[wave];
+  uint4 kA[KS], kB[KS];
+  VVec vA[4], vB[4];
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4 acc[DPL];
+  bool bad = false;
+  auto reset = [&]() {
+    m_run = kNegInf;
+    l_run = 0.f;
+#pragma unroll
+    for (int uu = 0; uu < DPL; ++uu) acc[uu] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bad = false;
+  };
+
+  while (u < u_hi) {
+    // ---- Plan the chunk (uniform): pieces until tiles, pieces or query
+    // rows run out; a piece that does not fit continues in the next chunk.
+    int npc = 0, ntc = 0, nqr = 0;
+    while (u < u_hi && npc < kChunkPieces && ntc < kChunkTiles) {
+      const int L = uni(s_len[s]);
+      const int n = (L + 15) / 16;
+      const int us = (n + unit - 1) / unit;
+      const int k = min(us - uin, u_hi - u);
+      const int t0 = uin * unit;
+      const int t1 = min((uin + k) * unit, n);
+      const int kvh = hsub / nsub;
+      const int sub = hsub - kvh * nsub;
+      const int nh = min(GMAX, g - sub * GMAX);
+      if (nqr + nh > kChunkQRows) break;
+      const int tb = t0 + tdone;
+      const int cnt = min(t1 - tb, kChunkTiles - ntc);
+      const bool ends = tb + cnt == t1;
+      const bool whole = uin == 0 && k == us;
+      int flags = (whole ? kWhole : 0) | (ends ? kEnds : 0) | (first ? 0 : kLastSlot) | (tdone == 0 ? kStarts : 0);
+      int np = 1;
+      if (uin == 0) {
+        flags |= kFirstUnit;
+        // the wave holding the segment's last unit
+        const int w_last = (int)(((long long)(u + us) * W - 1) / qt);
+        np = whole ? 1 : w_last - w + 1;
+      }
+      if (lane == 0) {
+        Piece& pc = pcs[npc];
+        pc.bt0 = s * maxb + tb;
+        pc.tb = tb;
+        pc.kb = ntc;
+        pc.nt = cnt;
+        pc.L = L;
+        pc.kvh = kvh;
+        pc.qrow = nqr;
+        pc.nh = nh;
+        pc.row0 = s * Hq + kvh * g + sub * GMAX;
+        pc.seg = s * hs + hsub;
+        pc.np = np;
+        pc.flags = flags;
+        pc.bad = 0;
+      }
+      ++npc;
+      ntc += cnt;
+      nqr += nh;
+      if (!ends) {
+        tdone += cnt;
+        break;
+      }
+      u += k;
+      uin = 0;
+      tdone = 0;
+      first = false;
+      if (++hsub == hs) {
+        hsub = 0;
+        do {
+          ++s;
+        } while (s < B && uni(s_len[s]) <= 0);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- Stage: block ids and query rows, all loads in flight together.
+    constexpr int ND = kChunkTiles / 64;
+    constexpr int NQ = (kChunkQRows * QCH + 63) / 64;
+    int ids[ND], dpc[ND];
+    uint4 qv[NQ];
+    int qrw[NQ];
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      const int kk = lane + 64 * i;
+      int p = 0;
+      ids[i] = 0;
+      if (kk < ntc) {
+        while (p + 1 < npc && kk >= pcs[p + 1].kb) ++p;
+        ids[i] = bt[pcs[p].bt0 + kk - pcs[p].kb];
+      }
+      dpc[i] = p;
+    }
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int c = lane + 64 * i;
+      const int r = c / QCH, cc = c - r * QCH;
+      qv[i] = make_uint4(0, 0, 0, 0);
+      qrw[i] = -1;
+      if (r < nqr) {
+        int p = 0;
+        while (p + 1 < npc && r >= pcs[p + 1].qrow) ++p;
+        qrw[i] = r;
+        qv[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(q) +
+                                                (size_t)(pcs[p].row0 + r - pcs[p].qrow) * ROWB + cc * 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      const int kk = lane + 64 * i;
+      if (kk < ntc) {
+        const Piece& pc = pcs[dpc[i]];
+        int id = ids[i];
+        if (id < 0 || id >= num_blocks) {
+          id = 0;
+          atomicOr(&s_pc[wave][dpc[i]].bad, 1);
+        }
+        const int rmax = min(15, pc.L - 1 - (pc.tb + kk - pc.kb) * 16);
+        desc[kk] = ((unsigned)(id * Hkv + pc.kvh) << 4) | (unsigned)rmax;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int c = lane + 64 * i;
+      if (qrw[i] >= 0) *reinterpret_cast<uint4*>(&sq[qrw[i]][(c - qrw[i] * QCH) * 8]) = qv[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- One pipeline through the chunk.
+    int cp = 0;                    // piece being consumed
+    int cp_end = uni(pcs[0].nt);   // its end (chunk tile index)
+    int cp_nh = uni(pcs[0].nh);
+    int cp_qrow = uni(pcs[0].qrow);
+    if (uni(pcs[0].flags) & kStarts) reset();
+    bad |= uni(pcs[0].bad) != 0;
+    const uint16_t* qsrc = &sq[col < cp_nh ? cp_qrow + col : kChunkQRows][grp * 8];
+    pipeline(
+        ntc, kA, vA, kB, vB,
+        [&](int kk, uint4(&kr)[KS], VVec(&vr)[4]) {
+          const unsigned d = (unsigned)uni((int)desc[kk]);
+          const size_t off = (size_t)(d >> 4) * (16 * ROWB);
+          T::load(kp + off, vp + off, grp, col, (int)(d & 15), kr, vr);
+        },
+        [&](int kk, const uint4(&kr)[KS], const VVec(&vr)[4], bool valid) {
+          asm volatile("" ::: "memory");
+          const int lim = valid ? (int)(((unsigned)uni((int)desc[kk]) & 15) + 1) : 0;
+          T::consume(kr, vr, qsrc, 4 * grp, lim, qscale, x16, x32, m_run, l_run, acc);
+          if (valid && kk + 1 == cp_end) {
+            const int flags = uni(pcs[cp].flags);
+            if (flags & kEnds) {
+              // The piece is complete: final rows, or this wave's piece.
+              const int nh = cp_nh;
+              const size_t row0 = (size_t)uni(pcs[cp].row0);
+              const float l_tot = xchg(xchg(l_run, x16, AddOp()), x32, AddOp());
+              const float inv = bad ? __builtin_nanf("") : 1.f / l_tot;
+              const int slot = 2 * w + ((flags & kLastSlot) ? 1 : 0);
+              if (col < nh) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                  const int d0 = DPL * (4 * grp + jj);
+                  float f[DPL];
+#pragma unroll
+                  for (int uu = 0; uu < DPL; ++uu) f[uu] = acc[uu][jj] * inv;
+                  if (flags & kWhole) {
+                    store_row<DT, DPL>(out, (row0 + col) * D + d0, f);
+                  } else {
+                    float* po = pc_o + ((size_t)slot * GMAX + col) * D + d0;
+#pragma unroll
+                    for (int uu = 0; uu < DPL; uu += 4)
+                      *reinterpret_cast<float4*>(po + uu) = make_float4(f[uu], f[uu + 1], f[uu + 2], f[uu + 3]);
+                  }
+                }
+                if (!(flags & kWhole) && grp == 0) {
+                  pc_m[(size_t)slot * GMAX + col] = bad ? __builtin_nanf("") : m_run;
+                  pc_l[(size_t)slot * GMAX + col] = bad ? __builtin_nanf("") : l_tot;
+                }
+              }
+              if ((flags & kFirstUnit) && lane == 0) info[uni(pcs[cp].seg)] = make_int2(slot, uni(pcs[cp].np));
+              reset();
+            }
+            if (++cp < npc) {
+              cp_end += uni(pcs[cp].nt);
+              cp_nh = uni(pcs[cp].nh);
+              cp_qrow = uni(pcs[cp].qrow);
+              bad |= uni(pcs[cp].bad) != 0;
+              qsrc = &sq[col < cp_nh ? cp_qrow + col : kChunkQRows][grp * 8];
+            }
+          }
+        });
+  }
+}
+
+// Merge of a cut segment's pieces (one workgroup per segment; segments
+// written whole, and sequences without positions, are already final).
+template <int DT, int D, int GMAX>
+__global__ __launch_bounds__(256) void decode_stream_reduce(void* __restrict__ out, const int32_t* __restrict__ cl,
+                                                           const float* __restrict__ pc_o,
+                                                           const float* __restrict__ pc_m,
+                                                           const float* __restrict__ pc_l,
+                                                           const int2* __restrict__ info, int Hq, int g, int nsub,
+                                                           int max_ctx) {
+  const int hsub = blockIdx.x;
+  const int s = blockIdx.y;
+  const int L = cl[s];
+  if (L <= 0 || L > max_ctx) return;
+  const int2 inf = info[(size_t)s * gridDim.x + hsub];
+  const int np = inf.y;
+  if (np <= 1) return;
+  const int w0 = inf.x >> 1;
+  const int kvh = hsub / nsub;
+  const int sub = hsub - kvh * nsub;
+  const int nh = min(GMAX, g - sub * GMAX);
+  const size_t row0 = (size_t)s * Hq + kvh * g + sub * GMAX;
+  for (int c = threadIdx.x; c < nh * (D / 4); c += 256) {
+    const int h = c / (D / 4);
+    const int d = (c - h * (D / 4)) * 4;
+    float M = kNegInf, den = 0.f;
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < np; ++i) {
+      const size_t slot = i == 0 ? (size_t)inf.x : 2 * (size_t)(w0 + i);
+      const float m = pc_m[slot * GMAX + h];
+      const float l = pc_l[slot * GMAX + h];
+      const float4 o = *reinterpret_cast<const float4*>(pc_o + (slot * GMAX + h) * D + d);
+      const float Mn = fmaxf(M, m);
+      const float a = fast_exp2(M - Mn);
+      const float b = l * fast_exp2(m - Mn);
+      den = den * a + b;
+      num = make_float4(num.x * a + b * o.x, num.y * a + b * o.y, num.z * a + b * o.z, num.w * a + b * o.w);
+      M = Mn;
+    }
+    const float inv = 1.f / den;
+    const float f[4] = {num.x * inv, num.y * inv, num.z * inv, num.w * inv};
+    store_row<DT, 4>(out, (row0 + h) * D + d, f);
+  }
+}
+
 template <int DT, int D, int GMAX>
 void launch(const DecodeArgs& a, hipStream_t st) {
+  if (a.stream) {
+    hipLaunchKernelGGL((decode_stream<DT, D, GMAX>), dim3(a.grid), dim3(256), 0, st, a.out, a.q, a.kp, a.vp, a.bt, a.cl,
+                       a.ws_o, a.ws_m, a.ws_l, a.info, a.B, a.Hq, a.Hkv, a.g, a.nsub, a.num_blocks, a.maxb, a.max_ctx,
+                       a.qscale, a.unit);
+    hipLaunchKernelGGL((decode_stream_reduce<DT, D, GMAX>), dim3(a.Hkv * a.nsub, a.B), dim3(256), 0, st, a.out, a.cl,
+                       a.ws_o, a.ws_m, a.ws_l, a.info, a.Hq, a.g, a.nsub, a.max_ctx);
+    return;
+  }
   const unsigned grid = (unsigned)a.entries * a.Hkv * a.nsub * a.B;
   if (a.wave_part)
     hipLaunchKernelGGL((decode_part_wave<DT, D, GMAX>), dim3(grid), dim3(256), 0, st, a.out, a.q, a.kp, a.vp, a.bt,

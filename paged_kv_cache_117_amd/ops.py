@@ -66,9 +66,10 @@ def _dtype_code(t):
         raise TypeError(f"unsupported dtype {t.dtype}") from None
 
 
-def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_context_len: int,
-                           partition_size: int = 0) -> int:
-    return int(LIB.pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_size))
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                           max_context_len: int, partition_size: int = 0) -> int:
+    return int(LIB.pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                                             partition_size))
 
 
 def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_context_len: int,
@@ -92,7 +93,7 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_cont
     _device_tensor(out, "out", q.dtype, 3)
     if out.shape != q.shape:
         raise ValueError("out must have q's shape")
-    need = decode_workspace_bytes(B, Hq, D, max_context_len, partition_size)
+    need = decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, partition_size)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device) if need else None
     if workspace is not None:

@@ -31,14 +31,36 @@ def test_abi_version():
     assert pa.abi_version() == 1
 
 
+def _al(x):
+    return (x + 255) // 256 * 256
+
+
+def _even_split_bytes(B, Hq, Hkv, D):
+    # 2 * 4096 piece slots of gmax rows (o [slot][gmax][D], m, l), then one
+    # (slot, count) record per (sequence, KV head, query sub-group)
+    g = Hq // Hkv
+    gmax = 4 if g <= 4 else 8 if g <= 8 else 16
+    nsub = -(-g // gmax)
+    slots = 2 * 4096
+    return _al(slots * gmax * D * 4) + 2 * _al(slots * gmax * 4) + _al(B * Hkv * nsub * 8)
+
+
 def test_workspace_bytes():
-    # one partition -> no workspace
-    assert pa.decode_workspace_bytes(4, 2, 64, 37, 0) == 0
-    assert pa.decode_workspace_bytes(64, 32, 128, 512, 512) == 0
-    # 8 partitions of 512 for 4096 tokens: o [B][Hq][P][D] + m + l, each 256-aligned
-    rows = 64 * 32 * 8
-    assert pa.decode_workspace_bytes(64, 32, 128, 4096, 0) == rows * 128 * 4 + 2 * rows * 4
-    assert pa.decode_workspace_bytes(0, 32, 128, 4096, 0) == 0
+    # batches of up to 4096 sequences: the even split's pieces (any length)
+    assert pa.decode_workspace_bytes(4, 2, 2, 64, 37, 0) == _even_split_bytes(4, 2, 2, 64)
+    assert pa.decode_workspace_bytes(64, 32, 8, 128, 512, 512) == _even_split_bytes(64, 32, 8, 128)
+    assert pa.decode_workspace_bytes(7, 40, 40, 128, 100, 0) == _even_split_bytes(7, 40, 40, 128)
+    assert pa.decode_workspace_bytes(2, 64, 2, 64, 100, 0) == _even_split_bytes(2, 64, 2, 64)
+    # or the partitions' partials when larger: 8 partitions of 512 for 4096
+    # tokens, o [B][Hq][P][D] + m + l, each 256-aligned
+    rows = 4096 * 32 * 8
+    assert pa.decode_workspace_bytes(4096, 32, 8, 128, 4096, 0) == rows * 128 * 4 + 2 * rows * 4
+    # more than 4096 sequences: partitions only (none when one partition fits)
+    assert pa.decode_workspace_bytes(5000, 32, 8, 128, 512, 0) == 0
+    rows = 5000 * 32 * 2
+    assert pa.decode_workspace_bytes(5000, 32, 8, 128, 1024, 512) == rows * 128 * 4 + 2 * _al(rows * 4)
+    assert pa.decode_workspace_bytes(0, 32, 8, 128, 4096, 0) == 0
+    assert pa.decode_workspace_bytes(4, 32, 5, 128, 4096, 0) == 0
 
 
 L = _lib.LIB
@@ -58,7 +80,7 @@ def call_decode(**kw):
     (dict(bs=8), 3), (dict(D=96), 3), (dict(dt=7), 3),
     (dict(Hq=3, Hkv=2), 2), (dict(maxctx=33), 2), (dict(ps=24), 2), (dict(B=-1), 2),
     (dict(scale=float("inf")), 2), (dict(q=NULL), 1), (dict(out=8), 2),
-    (dict(maxctx=600, maxb=64), 4),
+    (dict(maxctx=600, maxb=64), 4), (dict(dt=2), 4), (dict(dt=1, wsb=64, ws=256), 4),
 ])
 def test_decode_host_validation(kw, status):
     """Rejected before any device work (these calls never reach the GPU)."""

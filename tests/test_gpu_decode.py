@@ -175,7 +175,7 @@ def test_workspace_reuse_across_calls_and_shapes():
     wb = make_custom("wsB", "fp16", [90, 4096, 512, 1], 16, 2, 64, seed=32)
     ga, gb = GpuStep(wa), GpuStep(wb)
     ra, rb = ga.run().clone(), gb.run().clone()
-    need = max(pa.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.head_dim, w.max_context_len)
+    need = max(pa.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_context_len)
                for w in (wa, wb))
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
     for it in range(3):
@@ -199,7 +199,7 @@ def test_max_context_hint_above_real_lengths(psize):
     ref = g.run(partition_size=psize).clone()
     wide = torch.full((w.num_seqs, 1024), -1, dtype=torch.int32, device="cuda")
     wide[:, : g.tables.shape[1]] = g.tables
-    ws = torch.empty(pa.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.head_dim, 16384, psize),
+    ws = torch.empty(pa.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, 16384, psize),
                      dtype=torch.uint8, device="cuda")
     for _ in range(2):
         out = _decode_with(g, ws, max_ctx=16384, tables=wide, partition_size=psize)
@@ -217,17 +217,16 @@ def test_large_batch():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-def test_wave_and_workgroup_partition_kernels_agree(dtype):
-    """Partitions of up to 1024 positions run one wavefront each (four merged
-    per workgroup); longer ones are shared by the four waves of a workgroup.
-    Their fp32 summation orders differ, so both are checked against the
-    oracle and against each other, and each for run-to-run determinism."""
+def test_partition_sizes_agree_and_are_deterministic(dtype):
+    """Each partition size cuts the sequences differently, so the fp32
+    summation orders differ: every size is checked against the oracle and
+    against the automatic split, and for run-to-run determinism."""
     lens = [1, 16, 17, 1023, 1024, 1025, 2047, 2048, 2049, 4095, 4096, 4097, 9000, 15000]
     w = make_custom("twokernels", dtype, lens, 32, 8, 128, seed=35)
     g = GpuStep(w)
     _, _, _, want = oracle_step(w)
     res = {}
-    for ps in (256, 1024, 2048, 4096):
+    for ps in (0, 256, 1024, 2048, 4096):
         print(f"[decode] twokernels {dtype} psize={ps}", flush=True)
         a = g.run(partition_size=ps).clone()
         b = g.run(partition_size=ps).clone()
@@ -235,4 +234,16 @@ def test_wave_and_workgroup_partition_kernels_agree(dtype):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
         res[ps] = to_f64(a, dtype)
         assert max_err(res[ps], want) <= TOL[dtype], ps
-    assert max_err(res[256], res[2048]) <= TOL[dtype]
+    for ps in (256, 1024, 2048, 4096):
+        assert max_err(res[0], res[ps]) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("psize", [0, 2048])
+def test_partition_kernels_for_large_batches(psize):
+    """More than 4096 sequences go to the partition kernels (one wavefront
+    per partition up to 1024 positions, a workgroup per partition above)."""
+    rng = np.random.default_rng(36)
+    lens = list(rng.integers(1, 200, size=4100))
+    lens[0], lens[1], lens[4099] = 5000, 2049, 1100
+    w = make_custom("bigbatch", "bf16", lens, 8, 2, 128, seed=36)
+    check(w, rows=[0, 1, 2, 2048, 4095, 4096, 4099], partition_size=psize)
