@@ -62,7 +62,9 @@ def build(verbose: bool = True, jobs: int = 8) -> str:
     with ThreadPoolExecutor(jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    # --no-undefined: a missing symbol (say, a kernel whose host-side launch
+    # stub was not emitted) fails here instead of when the library loads
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 
