@@ -589,17 +589,28 @@ __global__ __launch_bounds__(256) void decode_part_mfma(void* __restrict__ out, 
 // each XCD's L2 sees a contiguous run of sequences (shared prefix blocks of
 // neighbouring sequences hit there).
 // ---------------------------------------------------------------------------
-constexpr int kChunkTiles = 512;   // tile descriptors per wave and chunk
-constexpr int kChunkPieces = 32;   // pieces per wave and chunk
+constexpr int kChunkTiles = 1024;  // tile descriptors per wave and chunk
+constexpr int kChunkPieces = 64;   // pieces per wave and chunk (one lane each while planning)
 constexpr int kChunkQRows = 48;    // query rows per wave and chunk
 
+// Exclusive prefix sums over the wavefront of three values at once.
+__device__ __forceinline__ int3 wave_excl_scan3(int a, int b, int c) {
+  const int lane = threadIdx.x & 63;
+  int x = a, y = b, z = c;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int tx = __shfl_up(x, d), ty = __shfl_up(y, d), tz = __shfl_up(z, d);
+    if (lane >= d) {
+      x += tx;
+      y += ty;
+      z += tz;
+    }
+  }
+  return make_int3(x - a, y - b, z - c);
+}
+
 struct Piece {
-  int bt0;    // block-table index of the portion's first tile
-  int tb;     // the sequence's block index of that tile
-  int kb;     // chunk tile index of that tile
   int nt;     // tiles in this chunk
-  int L;      // context length
-  int kvh;    // KV head
   int qrow;   // first query row in the wave's LDS rows
   int nh;     // query heads
   int row0;   // first output row
@@ -607,6 +618,10 @@ struct Piece {
   int np;     // pieces of the segment (valid with kFirstUnit)
   int flags;  // kWhole | kEnds | kFirstUnit | kLastSlot | kStarts
   int bad;    // an invalid block id in this portion
+  int bto;    // block-table index of chunk tile kk: bto + kk
+  int kvh;    // KV head
+  int rb;     // last filled slot of chunk tile kk: min(15, rb - 16 kk)
+  int kb;     // first chunk tile
 };
 constexpr int kWhole = 1, kEnds = 2, kFirstUnit = 4, kLastSlot = 8, kStarts = 16;
 
@@ -624,6 +639,8 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
   __shared__ int s_len[kStreamMaxSeqs];  // context length, -1 when out of range
   __shared__ unsigned s_desc[kWaves][kChunkTiles];
   __shared__ Piece s_pc[kWaves][kChunkPieces];
+  __shared__ unsigned char s_own[kWaves][kChunkTiles];   // piece of each chunk tile
+  __shared__ unsigned char s_qown[kWaves][kChunkQRows];  // piece of each query row
   __shared__ __attribute__((aligned(16))) uint16_t s_q[kWaves][kChunkQRows + 1][QROW];  // last row: zeros
 
   const int tid = threadIdx.x;
@@ -716,65 +733,117 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
   };
 
   while (u < u_hi) {
-    // ---- Plan the chunk (uniform): pieces until tiles, pieces or query
-    // rows run out; a piece that does not fit continues in the next chunk.
-    int npc = 0, ntc = 0, nqr = 0;
-    while (u < u_hi && npc < kChunkPieces && ntc < kChunkTiles) {
-      const int L = uni(s_len[s]);
-      const int n = (L + 15) / 16;
-      const int us = (n + unit - 1) / unit;
-      const int k = min(us - uin, u_hi - u);
-      const int t0 = uin * unit;
-      const int t1 = min((uin + k) * unit, n);
-      const int kvh = hsub / nsub;
-      const int sub = hsub - kvh * nsub;
-      const int nh = min(GMAX, g - sub * GMAX);
-      if (nqr + nh > kChunkQRows) break;
-      const int tb = t0 + tdone;
-      const int cnt = min(t1 - tb, kChunkTiles - ntc);
-      const bool ends = tb + cnt == t1;
-      const bool whole = uin == 0 && k == us;
-      int flags = (whole ? kWhole : 0) | (ends ? kEnds : 0) | (first ? 0 : kLastSlot) | (tdone == 0 ? kStarts : 0);
-      int np = 1;
-      if (uin == 0) {
-        flags |= kFirstUnit;
-        // the wave holding the segment's last unit
-        const int w_last = (int)(((long long)(u + us) * W - 1) / qt);
-        np = whole ? 1 : w_last - w + 1;
-      }
-      if (lane == 0) {
-        Piece& pc = pcs[npc];
-        pc.bt0 = s * maxb + tb;
-        pc.tb = tb;
-        pc.kb = ntc;
-        pc.nt = cnt;
-        pc.L = L;
-        pc.kvh = kvh;
-        pc.qrow = nqr;
-        pc.nh = nh;
-        pc.row0 = s * Hq + kvh * g + sub * GMAX;
-        pc.seg = s * hs + hsub;
+    // ---- Plan the chunk, one candidate piece per lane: lane j takes the
+    // j-th segment from the walker's position (empty for sequences without
+    // positions); exclusive sums over the lanes give every candidate's
+    // units, tiles and query rows.  The chunk takes candidates in order
+    // until tiles, query rows or pieces run out; a piece cut by the tile
+    // limit continues in the next chunk.
+    int npc, ntc, nqr;
+    {
+      const int cseg = hsub + lane;
+      const int dq = cseg / hs;
+      const int sj = s + dq;  // the candidate's sequence and segment
+      const int hj = cseg - dq * hs;
+      const int Lj = sj < B ? max(s_len[sj], 0) : 0;
+      const int nj = (Lj + 15) >> 4;
+      const int usj = seg_units(Lj);
+      const int uinj = lane == 0 ? uin : 0;
+      const int tdj = lane == 0 ? tdone : 0;
+      const int avj = max(usj - uinj, 0);
+      const int kvhj = nsub == 1 ? hj : hj / nsub;
+      const int subj = hj - kvhj * nsub;
+      const int Uj = wave_excl_scan3(avj, 0, 0).x;  // units before the candidate
+      const int kj = max(0, min(avj, u_hi - u - Uj));
+      const int t1j = min((uinj + kj) * unit, nj);
+      const int tbj = uinj * unit + tdj;
+      const int cntj = kj > 0 ? t1j - tbj : 0;
+      const int nhj = cntj > 0 ? min(GMAX, g - subj * GMAX) : 0;
+      const unsigned long long ne = __ballot(cntj > 0);
+      const int pidx = __builtin_popcountll(ne & ((1ull << lane) - 1));
+      const int3 ex = wave_excl_scan3(cntj, nhj, 0);
+      const int KBj = ex.x, QRj = ex.y;
+      const bool fit = KBj < kChunkTiles && QRj + nhj <= kChunkQRows && pidx < kChunkPieces;
+      const unsigned long long nofit = __ballot(cntj > 0 && !fit);
+      const int lim = nofit ? __builtin_ctzll(nofit) : 64;
+      const bool take = cntj > 0 && lane < lim;
+      const int ctk = take ? min(cntj, kChunkTiles - KBj) : 0;
+      const unsigned long long tk = __ballot(take);
+      npc = __builtin_popcountll(tk);
+      if (take) {
+        const bool whole = uinj == 0 && kj == usj;
+        const bool firstj = first && pidx == 0;
+        int flags = (whole ? kWhole : 0) | (tbj + ctk == t1j ? kEnds : 0) | (firstj ? 0 : kLastSlot) |
+                    (tdj == 0 ? kStarts : 0);
+        int np = 1;
+        if (uinj == 0) {
+          flags |= kFirstUnit;
+          if (!whole) {
+            // the wave holding the segment's last unit
+            const int w_last = (int)(((long long)(u + Uj + usj) * W - 1) / qt);
+            np = w_last - w + 1;
+          }
+        }
+        Piece& pc = pcs[pidx];
+        pc.nt = ctk;
+        pc.qrow = QRj;
+        pc.nh = nhj;
+        pc.row0 = sj * Hq + kvhj * g + subj * GMAX;
+        pc.seg = sj * hs + hj;
         pc.np = np;
         pc.flags = flags;
         pc.bad = 0;
+        pc.bto = sj * maxb + tbj - KBj;
+        pc.kvh = kvhj;
+        pc.rb = Lj - 1 - (tbj - KBj) * 16;
+        pc.kb = KBj;
+        for (int r = 0; r < nhj; ++r) s_qown[wave][QRj + r] = (unsigned char)pidx;
       }
-      ++npc;
-      ntc += cnt;
-      nqr += nh;
-      if (!ends) {
-        tdone += cnt;
-        break;
+      // Advance the walker: into the piece cut by the tile limit, else to
+      // the first candidate not taken (or past all 64).
+      const int lt = tk ? 63 - __builtin_clzll(tk) : -1;  // last taken
+      const bool cut = lt >= 0 && __shfl(ctk, lt) < __shfl(cntj, lt);
+      if (npc == 0 && lim == 0) break;  // (cannot happen: a first non-empty candidate always fits)
+      if (lt >= 0) {
+        ntc = __shfl(KBj + ctk, lt);
+        nqr = __shfl(QRj + nhj, lt);
+      } else {
+        ntc = nqr = 0;
       }
-      u += k;
-      uin = 0;
-      tdone = 0;
-      first = false;
-      if (++hsub == hs) {
-        hsub = 0;
-        do {
-          ++s;
-        } while (s < B && uni(s_len[s]) <= 0);
+      const int c = cut ? lt : lim;
+      const int Uc = c < 64 ? __shfl(Uj, c) : __shfl(Uj + avj, 63);
+      if (cut) {
+        tdone = __shfl(tdj + ctk, lt);
+        uin = __shfl(uinj, lt);
+        first = first && __shfl(pidx, lt) == 0;
+      } else {
+        tdone = 0;
+        uin = c == 0 ? uin : 0;
+        first = first && npc == 0;
       }
+      const int cs = hsub + c;
+      s = uni(s + cs / hs);
+      hsub = uni(cs - (cs / hs) * hs);
+      uin = uni(uin);
+      tdone = uni(tdone);
+      u = uni(u + Uc);
+      npc = uni(npc);
+      ntc = uni(ntc);
+      nqr = uni(nqr);
+    }
+    if (npc == 0) {
+      if (s >= B) break;  // (cannot happen: units remain, so sequences do)
+      continue;           // 64 candidates without positions
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // The piece of every chunk tile, written piece by piece by the whole
+    // wave (the pieces' first tiles are in the lanes that planned them).
+    for (int p = 0; p < npc; ++p) {
+      const int kb0 = uni(pcs[p].kb), n0 = uni(pcs[p].nt);
+      for (int t = lane; t < n0; t += 64) s_own[wave][kb0 + t] = (unsigned char)p;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -789,13 +858,13 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
       const int kk = lane + 64 * i;
-      int p = 0;
+      dpc[i] = 0;
       ids[i] = 0;
       if (kk < ntc) {
-        while (p + 1 < npc && kk >= pcs[p + 1].kb) ++p;
-        ids[i] = bt[pcs[p].bt0 + kk - pcs[p].kb];
+        const int p = s_own[wave][kk];
+        dpc[i] = p;
+        ids[i] = bt[pcs[p].bto + kk];
       }
-      dpc[i] = p;
     }
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
@@ -804,8 +873,7 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
       qv[i] = make_uint4(0, 0, 0, 0);
       qrw[i] = -1;
       if (r < nqr) {
-        int p = 0;
-        while (p + 1 < npc && r >= pcs[p + 1].qrow) ++p;
+        const int p = s_qown[wave][r];
         qrw[i] = r;
         qv[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(q) +
                                                 (size_t)(pcs[p].row0 + r - pcs[p].qrow) * ROWB + cc * 16);
@@ -821,8 +889,7 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
           id = 0;
           atomicOr(&s_pc[wave][dpc[i]].bad, 1);
         }
-        const int rmax = min(15, pc.L - 1 - (pc.tb + kk - pc.kb) * 16);
-        desc[kk] = ((unsigned)(id * Hkv + pc.kvh) << 4) | (unsigned)rmax;
+        desc[kk] = ((unsigned)(id * Hkv + pc.kvh) << 4) | (unsigned)min(15, pc.rb - 16 * kk);
       }
     }
 #pragma unroll
@@ -924,16 +991,34 @@ __global__ __launch_bounds__(256) void decode_stream_reduce(void* __restrict__ o
     const int d = (c - h * (D / 4)) * 4;
     float M = kNegInf, den = 0.f;
     float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int i = 0; i < np; ++i) {
-      const size_t slot = i == 0 ? (size_t)inf.x : 2 * (size_t)(w0 + i);
-      const float m = pc_m[slot * GMAX + h];
-      const float l = pc_l[slot * GMAX + h];
-      const float4 o = *reinterpret_cast<const float4*>(pc_o + (slot * GMAX + h) * D + d);
-      const float Mn = fmaxf(M, m);
-      const float a = fast_exp2(M - Mn);
-      const float b = l * fast_exp2(m - Mn);
-      den = den * a + b;
-      num = make_float4(num.x * a + b * o.x, num.y * a + b * o.y, num.z * a + b * o.z, num.w * a + b * o.w);
+    // pieces in batches of 8: all loads of a batch in flight together
+    for (int i0 = 0; i0 < np; i0 += 8) {
+      float mv[8], lv[8];
+      float4 ov[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        mv[j] = kNegInf;
+        lv[j] = 0.f;
+        ov[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i0 + j < np) {
+          const size_t slot = i0 + j == 0 ? (size_t)inf.x : 2 * (size_t)(w0 + i0 + j);
+          mv[j] = pc_m[slot * GMAX + h];
+          lv[j] = pc_l[slot * GMAX + h];
+          ov[j] = *reinterpret_cast<const float4*>(pc_o + (slot * GMAX + h) * D + d);
+        }
+      }
+      float Mn = M;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) Mn = fmaxf(Mn, mv[j]);
+      const float a = fast_exp2(M - Mn);  // 0 on the first batch (M = -inf)
+      den *= a;
+      num = make_float4(num.x * a, num.y * a, num.z * a, num.w * a);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float b = lv[j] * fast_exp2(mv[j] - Mn);  // 0 past the last piece
+        den += b;
+        num = make_float4(num.x + b * ov[j].x, num.y + b * ov[j].y, num.z + b * ov[j].z, num.w + b * ov[j].w);
+      }
       M = Mn;
     }
     const float inv = 1.f / den;
