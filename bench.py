@@ -37,6 +37,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["paged_kv_cache_117_amd/csrc/decode_mfma.hip", "paged_kv_cache_117_amd/csrc/decode.hip",
                   "paged_kv_cache_117_amd/csrc/decode_api.hip", "paged_kv_cache_117_amd/build_lib.py"]
 METRIC = "paged decode attention KV-read GB/s (% of MI355X HBM peak); seq-steps/s"
+# partition size a workload states (positions per partition); others use the automatic split
+WORKLOAD_PARTITION = {"c5": 512}
 WORKLOAD_NAMES = {
     "c1": "tiny paged decode fp32 (4 seqs, L in {1,5,16,37}, Hq=Hkv=2, D=64)",
     "c2": "Llama-3.1-8B decode layer bf16 (B=64, Hq=32, Hkv=8, D=128, L~U[128,4096], block 16)",
@@ -53,7 +55,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_NAMES))
-    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="positions per partition; 0 = automatic even split (default: the workload's, "
+                         "512 for c5, automatic otherwise)")
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = enough for >= 2 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -105,10 +109,18 @@ def _counter_means(path, kernel_pred):
     return {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
 
 
+def dominant_kernel_name(path, kernel_pred):
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if kernel_pred(r["Kernel_Name"]):
+                return r["Kernel_Name"]
+    return "?"
+
+
 def pmc_summary(args):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the decode partition kernel,
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dominant decode kernel,
     scaled by what the same counters read for a 1 GiB device copy."""
-    dec = lambda n: "decode_part" in n
+    dec = lambda n: ("decode_stream" in n and "reduce" not in n) or "decode_part" in n
     copy = lambda n: "copy" in n.lower() or "elementwise" in n.lower()
     fetch, nf = _counter_means(args.pmc_summary[0], dec)
     write, _ = _counter_means(args.pmc_summary[1], dec)
@@ -119,7 +131,7 @@ def pmc_summary(args):
     f_write = gib / (cwrite["WRITE_SIZE"] * 1024)
     rec = {
         "config": args.config,
-        "kernel": "decode_part_mfma (pa_decode partition kernel)",
+        "kernel": dominant_kernel_name(args.pmc_summary[0], dec),
         "kernel_sha": kernel_fingerprint(),
         "dispatches": nf.get("FETCH_SIZE", 0),
         "fetch_kib_per_dispatch": round(fetch["FETCH_SIZE"], 1),
@@ -224,6 +236,8 @@ def main():
         calibrate_copy()
         return
     w = make_workload(args.config)
+    if args.partition_size is None:
+        args.partition_size = WORKLOAD_PARTITION.get(args.config, 0)
     eb = metrics.ELEM_BYTES[w.dtype]
     tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
 
@@ -329,7 +343,7 @@ def main():
             "num_seqs": w.num_seqs,
             "kv_bytes_per_step": kv_bytes,
             "block_size": w.block_size,
-            "partition_size": args.partition_size or 512,
+            "partition_size": args.partition_size or "auto (even split over all wavefronts)",
             "placement": args.placement,
             "rotating_sets": R,
             "copy_pairs": int(len(pairs)),
@@ -355,9 +369,9 @@ def main():
     }
     rec = traffic_record(args.config)
     if rec is not None and rec.get("config") == args.config:
-        # counters cover the partition kernel; the reduce adds its partial reads and output writes
+        # counters cover the dominant kernel; the reduce adds its piece reads and output writes
         res["roofline"]["traffic"] = rec["traffic_bytes_per_launch"]
-        res["traffic_note"] = ("HBM bytes per partition-kernel launch from rocprofv3 FETCH_SIZE/WRITE_SIZE "
+        res["traffic_note"] = ("HBM bytes per dominant-kernel launch from rocprofv3 FETCH_SIZE/WRITE_SIZE "
                                "scaled by a 1 GiB copy; algorithmic bytes per launch: %d" % io_bytes)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, tables, args.cpu_seconds)
