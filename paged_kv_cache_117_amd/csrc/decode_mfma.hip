@@ -593,20 +593,23 @@ constexpr int kChunkTiles = 1024;  // tile descriptors per wave and chunk
 constexpr int kChunkPieces = 64;   // pieces per wave and chunk (one lane each while planning)
 constexpr int kChunkQRows = 48;    // query rows per wave and chunk
 
+// Inclusive prefix sum over the wavefront's 64 lanes with DPP: shifts by
+// 1, 2, 4, 8 within each row of 16 lanes (lanes before the row start add
+// 0), then row 0's total into row 1 and row 2's into row 3 (row_bcast:15),
+// then rows 0-1's total into rows 2-3 (row_bcast:31).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // Exclusive prefix sums over the wavefront of three values at once.
 __device__ __forceinline__ int3 wave_excl_scan3(int a, int b, int c) {
-  const int lane = threadIdx.x & 63;
-  int x = a, y = b, z = c;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int tx = __shfl_up(x, d), ty = __shfl_up(y, d), tz = __shfl_up(z, d);
-    if (lane >= d) {
-      x += tx;
-      y += ty;
-      z += tz;
-    }
-  }
-  return make_int3(x - a, y - b, z - c);
+  return make_int3(wave_incl_scan(a) - a, wave_incl_scan(b) - b, wave_incl_scan(c) - c);
 }
 
 struct Piece {
@@ -665,6 +668,7 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
     if (L > 0) continue;
     const float fill = L < 0 ? __builtin_nanf("") : 0.f;
     for (int i = tid; i < Hq * D; i += 256) store_elem<DT>(out, (size_t)s * Hq * D + i, fill);
+    for (int h = tid; h < hs; h += 256) info[(size_t)s * hs + h] = make_int2(0, 0);  // nothing to merge
   }
   auto seg_units = [&](int L) { return L <= 0 ? 0 : ((L + 15) / 16 + unit - 1) / unit; };
 
@@ -672,9 +676,7 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
   // workgroup v: the XCD's share of the stream, in order.
   int qt = 0;
   for (int i = lane; i < B; i += 64) qt += seg_units(s_len[i]);
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) qt += __shfl_xor(qt, d);
-  qt = uni(qt) * hs;
+  qt = __builtin_amdgcn_readlane(wave_incl_scan(qt), 63) * hs;
   const int G = gridDim.x;
   const int xcd = blockIdx.x & 7, n8 = G >> 3, r8 = G & 7;
   const int v = xcd * n8 + min(xcd, r8) + (blockIdx.x >> 3);
@@ -690,12 +692,7 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
   for (int c0 = 0, base = 0; c0 < B; c0 += 64) {
     const int i = c0 + lane;
     const int us = i < B ? seg_units(s_len[i]) * hs : 0;
-    int incl = us;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int t = __shfl_up(incl, d);
-      if (lane >= d) incl += t;
-    }
+    const int incl = wave_incl_scan(us);
     const int excl = base + incl - us;
     const unsigned long long hit = __ballot(us > 0 && excl <= u_lo && u_lo < excl + us);
     if (hit) {
@@ -704,7 +701,7 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
       pre = __shfl(excl, l);
       break;
     }
-    base += __shfl(incl, 63);
+    base += __builtin_amdgcn_readlane(incl, 63);
   }
   s = uni(s);
   const int off0 = u_lo - uni(pre);  // units of s before u_lo
@@ -802,20 +799,20 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
       // Advance the walker: into the piece cut by the tile limit, else to
       // the first candidate not taken (or past all 64).
       const int lt = tk ? 63 - __builtin_clzll(tk) : -1;  // last taken
-      const bool cut = lt >= 0 && __shfl(ctk, lt) < __shfl(cntj, lt);
+      const bool cut = lt >= 0 && __builtin_amdgcn_readlane(ctk, lt) < __builtin_amdgcn_readlane(cntj, lt);
       if (npc == 0 && lim == 0) break;  // (cannot happen: a first non-empty candidate always fits)
       if (lt >= 0) {
-        ntc = __shfl(KBj + ctk, lt);
-        nqr = __shfl(QRj + nhj, lt);
+        ntc = __builtin_amdgcn_readlane(KBj + ctk, lt);
+        nqr = __builtin_amdgcn_readlane(QRj + nhj, lt);
       } else {
         ntc = nqr = 0;
       }
       const int c = cut ? lt : lim;
-      const int Uc = c < 64 ? __shfl(Uj, c) : __shfl(Uj + avj, 63);
+      const int Uc = c < 64 ? __builtin_amdgcn_readlane(Uj, c) : __builtin_amdgcn_readlane(Uj + avj, 63);
       if (cut) {
-        tdone = __shfl(tdj + ctk, lt);
-        uin = __shfl(uinj, lt);
-        first = first && __shfl(pidx, lt) == 0;
+        tdone = __builtin_amdgcn_readlane(tdj + ctk, lt);
+        uin = __builtin_amdgcn_readlane(uinj, lt);
+        first = first && __builtin_amdgcn_readlane(pidx, lt) == 0;
       } else {
         tdone = 0;
         uin = c == 0 ? uin : 0;
@@ -863,7 +860,10 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
       if (kk < ntc) {
         const int p = s_own[wave][kk];
         dpc[i] = p;
-        ids[i] = bt[pcs[p].bto + kk];
+        // (kk is inside piece p by construction; the check keeps a planning
+        // error from reading outside the sequence's table row)
+        if (kk - pcs[p].kb < pcs[p].nt) ids[i] = bt[pcs[p].bto + kk];
+        else ids[i] = -1;
       }
     }
 #pragma unroll
@@ -875,8 +875,9 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
       if (r < nqr) {
         const int p = s_qown[wave][r];
         qrw[i] = r;
-        qv[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(q) +
-                                                (size_t)(pcs[p].row0 + r - pcs[p].qrow) * ROWB + cc * 16);
+        if (r - pcs[p].qrow < pcs[p].nh)
+          qv[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(q) +
+                                                  (size_t)(pcs[p].row0 + r - pcs[p].qrow) * ROWB + cc * 16);
       }
     }
 #pragma unroll
@@ -968,16 +969,14 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
 // Merge of a cut segment's pieces (one workgroup per segment; segments
 // written whole, and sequences without positions, are already final).
 template <int DT, int D, int GMAX>
-__global__ __launch_bounds__(256) void decode_stream_reduce(void* __restrict__ out, const int32_t* __restrict__ cl,
-                                                           const float* __restrict__ pc_o,
+__global__ __launch_bounds__(256) void decode_stream_reduce(void* __restrict__ out, const float* __restrict__ pc_o,
                                                            const float* __restrict__ pc_m,
                                                            const float* __restrict__ pc_l,
-                                                           const int2* __restrict__ info, int Hq, int g, int nsub,
-                                                           int max_ctx) {
+                                                           const int2* __restrict__ info, int Hq, int g, int nsub) {
   const int hsub = blockIdx.x;
   const int s = blockIdx.y;
-  const int L = cl[s];
-  if (L <= 0 || L > max_ctx) return;
+  // every segment's record is written by the stream kernel (count 0 for
+  // sequences without positions, 1 for segments it wrote whole)
   const int2 inf = info[(size_t)s * gridDim.x + hsub];
   const int np = inf.y;
   if (np <= 1) return;
@@ -1033,8 +1032,8 @@ void launch(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((decode_stream<DT, D, GMAX>), dim3(a.grid), dim3(256), 0, st, a.out, a.q, a.kp, a.vp, a.bt, a.cl,
                        a.ws_o, a.ws_m, a.ws_l, a.info, a.B, a.Hq, a.Hkv, a.g, a.nsub, a.num_blocks, a.maxb, a.max_ctx,
                        a.qscale, a.unit);
-    hipLaunchKernelGGL((decode_stream_reduce<DT, D, GMAX>), dim3(a.Hkv * a.nsub, a.B), dim3(256), 0, st, a.out, a.cl,
-                       a.ws_o, a.ws_m, a.ws_l, a.info, a.Hq, a.g, a.nsub, a.max_ctx);
+    hipLaunchKernelGGL((decode_stream_reduce<DT, D, GMAX>), dim3(a.Hkv * a.nsub, a.B), dim3(256), 0, st, a.out,
+                       a.ws_o, a.ws_m, a.ws_l, a.info, a.Hq, a.g, a.nsub);
     return;
   }
   const unsigned grid = (unsigned)a.entries * a.Hkv * a.nsub * a.B;
