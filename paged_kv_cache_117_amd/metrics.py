@@ -25,6 +25,26 @@ def decode_kv_bytes(context_lens, num_kv_heads: int, head_dim: int, elem_bytes: 
     return int(sum(int(L) for L in context_lens)) * kv_bytes_per_token(1, num_kv_heads, head_dim, elem_bytes)
 
 
+def decode_unique_kv_bytes(block_tables, context_lens, num_kv_heads: int, head_dim: int, elem_bytes: int,
+                           block_size: int = 16) -> int:
+    """K+V bytes of the distinct physical blocks one decode launch reads: a
+    block shared by several sequences (a shared prefix) counts once, with
+    the most slots any of them reads from it."""
+    import numpy as np
+
+    slots = {}
+    tables = np.asarray(block_tables)
+    for s, L in enumerate(context_lens):
+        L = int(L)
+        nb = -(-L // block_size)
+        for j in range(nb):
+            b = int(tables[s, j])
+            n = min(block_size, L - j * block_size)
+            if n > slots.get(b, 0):
+                slots[b] = n
+    return sum(slots.values()) * kv_bytes_per_token(1, num_kv_heads, head_dim, elem_bytes)
+
+
 def decode_io_bytes(context_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
                     elem_bytes: int, block_size: int = 16) -> int:
     """KV bytes plus q read, out written, table entries and lengths read."""

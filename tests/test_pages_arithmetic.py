@@ -68,3 +68,25 @@ def test_qwen72b_sizing():
 
 def test_decode_kv_bytes_counts_valid_tokens_once_per_kv_head():
     assert metrics.decode_kv_bytes([1, 5, 16, 37], 2, 64, 4) == 59 * 2 * 2 * 64 * 4 == 60416
+
+
+def test_unique_kv_bytes_count_shared_blocks_once():
+    """Without sharing, unique bytes equal the logical bytes; a prefix block
+    read by several sequences counts once, with its largest fill."""
+    import numpy as np
+
+    per_tok = metrics.kv_bytes_per_token(1, 8, 128, 2)
+    lens = [37, 16, 1]
+    tables = np.array([[4, 9, 2], [7, -1, -1], [3, -1, -1]])
+    assert metrics.decode_unique_kv_bytes(tables, lens, 8, 128, 2) == metrics.decode_kv_bytes(lens, 8, 128, 2)
+    # two sequences sharing block 5 (16 slots each); then block 6 (4 slots)
+    # for the first and block 8 (10 slots) for the second
+    tables = np.array([[5, 6, -1], [5, 8, -1]])
+    lens = [20, 26]
+    assert metrics.decode_unique_kv_bytes(tables, lens, 8, 128, 2) == (16 + 4 + 10) * per_tok
+    # C4-like: 8 samples on one 64-block prefix, each with a private 1-slot block
+    nb = 64
+    tables = np.array([list(range(nb)) + [100 + i] for i in range(8)])
+    lens = [nb * 16 + 1] * 8
+    assert metrics.decode_unique_kv_bytes(tables, lens, 8, 128, 2) == (nb * 16 + 8) * per_tok
+    assert metrics.decode_kv_bytes(lens, 8, 128, 2) == 8 * (nb * 16 + 1) * per_tok
