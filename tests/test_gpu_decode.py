@@ -247,3 +247,39 @@ def test_partition_kernels_for_large_batches(psize):
     lens[0], lens[1], lens[4099] = 5000, 2049, 1100
     w = make_custom("bigbatch", "bf16", lens, 8, 2, 128, seed=36)
     check(w, rows=[0, 1, 2, 2048, 4095, 4096, 4099], partition_size=psize)
+
+
+def test_stream_single_long_sequence_many_pieces():
+    """One 70,000-token sequence over every wavefront: each (sequence, KV
+    head) segment is cut into hundreds of pieces, merged by the reduce in
+    batches."""
+    w = make_custom("onelong", "bf16", [70000], 8, 2, 128, seed=37)
+    check(w)
+
+
+def test_stream_runs_of_empty_sequences():
+    """Sequences without positions in runs longer than one planning window
+    (64 candidates), between and around sequences with positions (lengths
+    zeroed on the device after the step's writes)."""
+    empty = list(range(0, 70)) + list(range(71, 201)) + list(range(203, 268))
+    lens = [1] * 269
+    lens[70], lens[201], lens[202], lens[268] = 300, 17, 5000, 1
+    w = make_custom("emptyruns", "fp16", lens, 8, 4, 64, seed=38)
+    g = GpuStep(w)
+    g.run()
+    dl = g.lens.clone()
+    dl[torch.tensor(empty, device="cuda")] = 0
+    out = pa.decode(g.q, g.k, g.v, g.tables, dl, w.scale, w.max_context_len)
+    torch.cuda.synchronize()
+    o = to_f64(out, "fp16")
+    assert np.all(o[empty] == 0)
+    rows = [70, 201, 202, 268]
+    _, _, _, want = oracle_step(w, rows=rows)
+    assert max_err(o[rows], want) <= TOL["fp16"]
+
+
+def test_stream_query_groups_of_32_heads():
+    """g = 32: each KV head's query heads are two sub-groups of 16 (two
+    segments per KV head in the split)."""
+    w = make_custom("g32", "fp16", [1, 700, 2049, 33], 64, 2, 128, seed=39)
+    check(w)
