@@ -14,6 +14,11 @@ What it computes, each part written as the plain definition from the pages:
   attention over scattered blocks"; PagedAttention (tensortonic), "5. Reading
   the Cache During Attention"; PagedAttention: Virtual Memory for the KV Cache,
   "PagedAttention: attention over non-contiguous blocks").
+* ``attention.prefill`` -- several new tokens per sequence (a prefill
+  chunk): token i of the T new ones sits at position L - T + i and attends
+  causally to positions 0..L-T+i, same two-pass float64 softmax (Batching and
+  PagedAttention, chunked prefill; vLLM's PagedAttention: How Memory
+  Management Supports Large Model Inference, "2.5").
 * ``cache_ops.write_kv`` -- store each new token's K/V at its block+offset
   (PagedAttention (tensortonic), "5. Reading the Cache During Attention";
   Paging the KV Cache Like an OS, "Step 5", the write kernel).
@@ -33,6 +38,6 @@ manager.  Every function here is pinned; none is "parity unpinned".
 """
 
 from . import attention, block_manager, cache_ops  # noqa: F401
-from .attention import decode, storage_to_f64  # noqa: F401
+from .attention import decode, prefill, storage_to_f64  # noqa: F401
 from .block_manager import BlockManager, NoFreeBlocks  # noqa: F401
 from .cache_ops import copy_blocks, write_kv  # noqa: F401

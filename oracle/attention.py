@@ -86,3 +86,66 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale, dtype: str) -> 
             w = np.exp(x - m)
             out[s, h] = (w / w.sum()) @ V[j]
     return out
+
+
+def prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale, dtype: str) -> np.ndarray:
+    """Paged attention for several new tokens per sequence (chunked prefill), float64.
+
+    Definition followed:
+
+    * Batching and PagedAttention, "How continuous batching keeps the GPU
+      saturated" and its FAQ on chunked prefill -- a long prompt is fed over
+      several steps, a chunk of consecutive tokens per step, each chunk filling
+      blocks of the paged cache.
+    * vLLM's PagedAttention: How Memory Management Supports Large Model
+      Inference, "2.5" -- a request keeps the count of tokens already computed
+      and each step computes the next run of tokens, which covers chunked
+      prefill and continuing after a prefix-cache hit alike.
+    * PagedAttention (tensortonic), "5. Reading the Cache During Attention" --
+      where a token sits in memory changes neither its logical position nor
+      the causal mask; softmax normalises over every position the query may
+      see.
+
+    Reading (the pages give no formula for several query tokens): sequence s
+    has ``L = context_lens[s]`` cached positions, of which the last
+    ``T = query_start[s+1] - query_start[s]`` are this step's tokens, already
+    written to the pool.  Its i-th new token sits at position ``p = L - T + i``
+    and attends, causally, to positions ``0..p``.  Query heads map to KV heads
+    as in :func:`decode`.
+
+    q            [N][Hq][D] storage values, N = query_start[-1]; rows of
+                 sequence s are query_start[s] .. query_start[s+1]-1
+    k_pool/v_pool[num_blocks][Hkv][bs][D] storage values
+    block_tables [B][max_blocks] int
+    context_lens [B] int, each >= that sequence's T
+    query_start  [B+1] int, non-decreasing, query_start[0] = 0
+    scale        the fp32 scale, used as its exact float64 value
+    returns      [N][Hq][D] float64
+    """
+    q = np.asarray(q)
+    N, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    assert Hq % Hkv == 0
+    g = Hq // Hkv
+    qs = [int(x) for x in query_start]
+    assert qs[0] == 0 and qs[-1] == N
+    sc = np.float64(np.float32(scale))
+    out = np.zeros((N, Hq, D), dtype=np.float64)
+    for s in range(len(qs) - 1):
+        T = qs[s + 1] - qs[s]
+        L = int(context_lens[s])
+        assert 0 <= T <= L
+        if T == 0:
+            continue
+        K = gather_sequence(k_pool, block_tables[s], L, dtype)
+        V = gather_sequence(v_pool, block_tables[s], L, dtype)
+        qf = storage_to_f64(q[qs[s]:qs[s + 1]], dtype)
+        for i in range(T):
+            p = L - T + i  # position of this token; it sees 0..p
+            for h in range(Hq):
+                j = h // g
+                x = sc * (K[j, :p + 1] @ qf[i, h])
+                m = x.max()
+                w = np.exp(x - m)
+                out[qs[s] + i, h] = (w / w.sum()) @ V[j, :p + 1]
+    return out
