@@ -124,6 +124,54 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads
                                  int max_context_len, int partition_size);
 
 /*
+ * pa_prefill -- paged attention for several new tokens per sequence: a
+ * chunk of a long prompt fed over several steps, or the rest of a prompt
+ * after its first blocks were found in the prefix cache (Batching and
+ * PagedAttention, continuous batching and its chunked-prefill FAQ; vLLM's
+ * PagedAttention: How Memory Management Supports Large Model Inference,
+ * "2.5": each step computes the next run of a request's tokens).
+ *
+ * Sequence s has L = context_lens[s] cached positions; the last
+ * T = query_start[s+1] - query_start[s] of them are this step's tokens,
+ * whose K/V the caller has already written (pa_write_kv).  For the i-th new
+ * token (query row query_start[s] + i, position p = L - T + i) and each query
+ * head h (KV head j = h / g):
+ *   x_t = scale * q[row][h] . K_j(t)            for t = 0..p   (causal),
+ *   out[row][h] = sum_t softmax(x)_t * V_j(t),
+ * with position t read from block block_tables[s][t / 16], slot t % 16.
+ * Where a position lives changes neither its place in the sequence nor the
+ * causal mask (PagedAttention (tensortonic), "5. Reading the Cache During
+ * Attention").  With T = 1 this is pa_decode's attention.
+ *
+ *   out              device, [num_tokens][num_q_heads][head_dim], dtype; rows of
+ *                    every sequence with T > 0 are written, nothing else
+ *   q                device, [num_tokens][num_q_heads][head_dim], dtype
+ *   k_pool, v_pool   device, [num_blocks][num_kv_heads][block_size][head_dim], dtype
+ *   block_tables     device, int32 [num_seqs][max_blocks_per_seq]; entries at
+ *                    index >= ceil(L/16) are never read
+ *   context_lens     device, int32 [num_seqs]
+ *   query_start      device, int32 [num_seqs + 1]: query_start[0] = 0,
+ *                    non-decreasing, query_start[num_seqs] = num_tokens;
+ *                    T = 0 is allowed (no rows)
+ *   max_query_len    host, >= every T (sizes the launch), <= num_tokens
+ *   scale            softmax scale (typically 1/sqrt(head_dim)), finite
+ *   stream           hipStream_t or NULL
+ * Supported: fp16 and bf16 (fp32 returns PA_ERR_UNSUPPORTED), block_size 16,
+ * head_dim 64 or 128, any num_q_heads that is a multiple of num_kv_heads.
+ * Device-side contract violations are never dereferenced: a sequence with
+ * T > L, L > max_blocks_per_seq * 16, T > max_query_len or a row range
+ * outside [0, num_tokens) gets NaN rows (those inside [0, num_tokens)); a
+ * block id outside [0, num_blocks) makes the rows that would read it NaN.
+ * `out` must not alias any input.  Needs no workspace.
+ */
+pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       const int32_t* query_start, int num_seqs, int num_tokens,
+                       int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                       int num_blocks, int max_blocks_per_seq, int max_query_len, float scale,
+                       pa_dtype_t dtype, void* stream);
+
+/*
  * pa_write_kv -- store new tokens' K and V rows in their slots
  * (reshape-and-cache).  For each token i with slot = slot_mapping[i] >= 0:
  *   k_pool[slot / 16][h][slot % 16][:] = k_new[i][h][:]   for every KV head h,

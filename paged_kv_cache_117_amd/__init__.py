@@ -1,10 +1,11 @@
-"""Paged KV cache decode path for AMD MI355X (gfx950).
+"""Paged KV cache decode and chunked-prefill path for AMD MI355X (gfx950).
 
 The device work runs in hand-written HIP kernels inside ``libpa.so`` (C ABI in
 ``include/pa.h``); this package only marshals arguments.  Importing it loads
 the library and fails with ImportError when it has not been built.
 
     decode(q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len)
+    prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale, max_query_len)
     write_kv(k_pool, v_pool, k_new, v_new, slot_mapping)
     copy_blocks(k_pool, v_pool, block_pairs)
     BlockManager(num_blocks, block_size=16, free_order=None)
@@ -19,5 +20,6 @@ from .ops import (  # noqa: F401
     copy_blocks,
     decode,
     decode_workspace_bytes,
+    prefill,
     write_kv,
 )

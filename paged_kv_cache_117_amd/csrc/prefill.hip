@@ -1,0 +1,351 @@
+// pa_prefill kernels: paged attention for several new tokens per sequence
+// (a prefill chunk, or the continuation after a prefix-cache hit), causal
+// inside the paged context, for 16-bit KV on gfx950.
+//
+// Sequence s has L cached positions of which the last T are this step's
+// tokens; new token i sits at position p = L - T + i and attends to
+// positions 0..p.  Query rows are numbered token-major within a KV head's
+// group, rho = i * g + h (h = query head within the group), so one pass over
+// a K/V tile serves every query head that shares it.
+//
+// One workgroup (4 wavefronts) takes one (sequence, KV head, tile of R = 64 *
+// NC rows); each wave owns 16 * NC rows as NC matrix columns groups of 16.
+// The workgroup walks the positions 0..(largest p of its rows) in steps of
+// 32 (two 16-slot blocks):
+//  * K and V of the step go from the pool to a double-buffered LDS tile
+//    (16-byte loads, consecutive threads on consecutive bytes, rows padded
+//    by 16 bytes so the operand reads below are free of bank conflicts); the
+//    next step's loads are in flight while the current one computes.
+//  * Scores S^T = K Q^T with v_mfma_f32_16x16x32: the K rows (A operand,
+//    lane (G, c) reads token c at dims 32k + 8G) come from LDS, the query
+//    rows (B operand) sit in registers for the whole walk.  Lane (G, c) gets
+//    S[token 4G + j][row c] for each 16-token half of the step.
+//  * Online softmax per row in base 2.  The running max is kept in raw score
+//    units, so each weight is one fma and one exp2: p = 2^(s*qs - m*qs),
+//    qs = |scale| * log2(e) (a negative scale flips the query's sign bits,
+//    which is exact).  Only steps that cross a row's causal limit apply the
+//    mask.
+//  * PV transposed, O^T = V^T P^T, again with v_mfma_f32_16x16x32: lane
+//    group G's eight k-slots are tokens 4G..4G+3 of the first half and of
+//    the second half, which are exactly the eight weights the lane holds
+//    from the score layout; the V operand (rows = head dims DPL*c + u) is
+//    built from eight 16-byte LDS reads by v_perm_b32 pair interleaves and
+//    shared by all of the wave's column groups.  The output keeps the query
+//    row in the lane's column, so the rescale by 2^(m_old - m_new) is
+//    lane-local.
+//
+// Positions past L-1 inside the last step re-read position L-1 (finite;
+// masked).  Block ids outside [0, num_blocks) are never dereferenced: the
+// workgroup's rows become NaN.  A sequence whose (T, L) cannot be served
+// (T > L, L past the table, T past max_query_len, bad row range) gets NaN
+// rows instead of a computed result.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "pa_device.h"
+#include "prefill_kernels.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kStep = 32;  // positions per step: two blocks
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma32(const uint4& a, const uint4& b, const f32x4& c) {
+  if constexpr (DT == PA_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  }
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 weights rounded (nearest even) to the KV type, `a` in the low half.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (DT == PA_BF16) {
+    const bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    const f16x2 v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+// x combined with the value of lane (l ^ 16) and then (l ^ 32): the four
+// token groups of the MFMA output layout.
+__device__ __forceinline__ float max_groups(float x, int x16, int x32) {
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x16, __builtin_bit_cast(int, x))));
+  return fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, x))));
+}
+__device__ __forceinline__ float sum_groups(float x, int x16, int x32) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x16, __builtin_bit_cast(int, x)));
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, x)));
+}
+
+// NaN into every element of query heads [h0, h0 + nh) of rows [r0, r1).
+template <int DT>
+__device__ void nan_rows(void* out, int r0, int r1, int Hq, int h0, int nh, int D) {
+  const float nan = __builtin_nanf("");
+  const int per_row = nh * D;
+  for (long i = threadIdx.x; i < (long)(r1 - r0) * per_row; i += blockDim.x) {
+    const int r = r0 + (int)(i / per_row);
+    const int e = (int)(i % per_row);
+    store_elem<DT>(out, ((size_t)r * Hq + h0) * D + e, nan);
+  }
+}
+
+template <int DT, int D, int NC>
+__global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
+  constexpr int ROW = D + 8;                 // LDS row stride, elements (16 bytes of padding)
+  constexpr int KS = D / 32;                 // QK k-steps over the head dim
+  constexpr int DPL = D / 16;                // output dims per lane per row = PV MFMAs per column group
+  constexpr int CH = D / 8;                  // 16-byte chunks per token row
+  constexpr int LOADS = kStep * CH / 256;    // chunks of K (and of V) per thread per step
+  constexpr int R = kWaves * 16 * NC;        // rows per workgroup
+  static_assert(LOADS >= 1 && kStep * CH % 256 == 0, "step must split evenly over the threads");
+  using VVec = typename std::conditional<DPL == 8, uint4, uint2>::type;
+
+  __shared__ __align__(16) uint16_t sK[2][kStep][ROW];
+  __shared__ __align__(16) uint16_t sV[2][kStep][ROW];
+  __shared__ int s_bad;
+
+  // XCD-aware numbering: the hardware deals workgroups round-robin over the
+  // 8 XCDs; give each XCD a contiguous range of work items so the tiles of
+  // one (sequence, KV head) share that XCD's L2.
+  const int per_xcd = a.grid >> 3;
+  const int vid = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  const int tile = a.tiles - 1 - vid % a.tiles;  // latest rows (longest walks) first
+  const int rest = vid / a.tiles;
+  const int kvh = rest % a.Hkv;
+  const int s = rest / a.Hkv;
+  if (s >= a.B) return;
+
+  const int q0 = a.qs[s], q1 = a.qs[s + 1], L = a.cl[s];
+  const int T = q1 - q0;
+  const int g = a.g;
+  if (q0 < 0 || q1 < q0 || q1 > a.N || T > L || L > a.maxb * 16 || T > a.max_q) {
+    // Unservable sequence: NaN over whatever part of its row range exists.
+    if (tile == a.tiles - 1) {
+      const int r0 = min(max(q0, 0), a.N), r1 = min(max(q1, r0), a.N);
+      nan_rows<DT>(a.out, r0, r1, a.Hq, kvh * g, g, D);
+    }
+    return;
+  }
+  const int rows = T * g;
+  if (tile * R >= rows) return;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int G = lane >> 4, c = lane & 15;
+  const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;
+  const int base = L - T;  // position of new token 0
+
+  // WG and wave row ranges; positions the workgroup must walk.
+  const int rho_wg_last = min(tile * R + R, rows) - 1;
+  const int nsteps = (base + rho_wg_last / g) / kStep + 1;
+  const int rho_w0 = tile * R + wave * 16 * NC;
+  const bool wave_on = rho_w0 < rows;
+  const int lim_w_lo = base + min(rho_w0, rows - 1) / g;
+  const int lim_w_hi = base + (min(rho_w0 + 16 * NC, rows) - 1) / g;
+
+  // This lane's rows (one per column group) and their causal limits.
+  const bool neg = a.neg_scale != 0;
+  const float qs = a.qscale;  // |scale| * log2(e)
+  int lim[NC];
+  uint4 qr[NC][KS];
+  const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q);
+#pragma unroll
+  for (int n = 0; n < NC; ++n) {
+    const int rho = min(rho_w0 + 16 * n + c, rows - 1);
+    const int i = rho / g, h = rho - i * g;
+    lim[n] = base + i;
+    const uint16_t* src = qp + ((size_t)(q0 + i) * a.Hq + kvh * g + h) * D + 8 * G;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      uint4 v = *reinterpret_cast<const uint4*>(src + 32 * k);
+      if (neg) v = make_uint4(v.x ^ 0x80008000u, v.y ^ 0x80008000u, v.z ^ 0x80008000u, v.w ^ 0x80008000u);
+      qr[n][k] = v;
+    }
+  }
+
+  // Cooperative load of one step's K and V chunks into registers.
+  const int32_t* btrow = a.bt + (size_t)s * a.maxb;
+  const size_t head_off = (size_t)kvh * 16 * D;
+  const size_t blk_stride = (size_t)a.Hkv * 16 * D;
+  const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.kp);
+  const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.vp);
+  bool bad = false;
+  uint4 kreg[LOADS], vreg[LOADS];
+  auto issue = [&](int step) {
+#pragma unroll
+    for (int m = 0; m < LOADS; ++m) {
+      const int u = tid + 256 * m;
+      const int tt = u / CH, ch = u - tt * CH;
+      const int pos = min(step * kStep + tt, L - 1);
+      int id = btrow[pos >> 4];
+      if ((unsigned)id >= (unsigned)a.num_blocks) {
+        bad = true;
+        id = 0;
+      }
+      const size_t off = (size_t)id * blk_stride + head_off + (size_t)(pos & 15) * D + ch * 8;
+      kreg[m] = *reinterpret_cast<const uint4*>(kp + off);
+      vreg[m] = *reinterpret_cast<const uint4*>(vp + off);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int m = 0; m < LOADS; ++m) {
+      const int u = tid + 256 * m;
+      const int tt = u / CH, ch = u - tt * CH;
+      *reinterpret_cast<uint4*>(&sK[buf][tt][ch * 8]) = kreg[m];
+      *reinterpret_cast<uint4*>(&sV[buf][tt][ch * 8]) = vreg[m];
+    }
+  };
+
+  float m_run[NC], l_run[NC];
+  f32x4 acc[NC][DPL];
+#pragma unroll
+  for (int n = 0; n < NC; ++n) {
+    m_run[n] = -__FLT_MAX__;  // finite, so a zero scale gives 2^0, not NaN
+    l_run[n] = 0.f;
+#pragma unroll
+    for (int u = 0; u < DPL; ++u) acc[n][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  if (tid == 0) s_bad = 0;
+  issue(0);
+  stash(0);
+  __syncthreads();
+
+  for (int step = 0; step < nsteps; ++step) {
+    const int buf = step & 1;
+    const bool more = step + 1 < nsteps;
+    if (more) issue(step + 1);
+    const int t0 = step * kStep;
+    if (wave_on && t0 <= lim_w_hi) {
+      // Scores for both 16-token halves of the step.
+      f32x4 sc[NC][2];
+#pragma unroll
+      for (int n = 0; n < NC; ++n) sc[n][0] = sc[n][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          const uint4 ka = *reinterpret_cast<const uint4*>(&sK[buf][16 * half + c][32 * k + 8 * G]);
+#pragma unroll
+          for (int n = 0; n < NC; ++n) sc[n][half] = mfma32<DT>(ka, qr[n][k], sc[n][half]);
+        }
+      }
+      // Online softmax; weights packed as the PV B operand (k-slot e of
+      // lane group G is token 16*(e/4) + 4G + e%4 of the step).
+      const bool diag = t0 + kStep - 1 > lim_w_lo;
+      uint4 pb[NC];
+#pragma unroll
+      for (int n = 0; n < NC; ++n) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = sc[n][e >> 2][e & 3];
+        bool keep[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) keep[e] = !diag || t0 + 16 * (e >> 2) + 4 * G + (e & 3) <= lim[n];
+        float bm = -__builtin_huge_valf();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bm = fmaxf(bm, keep[e] ? x[e] : -__builtin_huge_valf());
+        bm = max_groups(bm, x16, x32);
+        const float mn = fmaxf(m_run[n], bm);  // finite: position 0 is in every row's first step
+        const float alpha = fast_exp2((m_run[n] - mn) * qs);
+        m_run[n] = mn;
+        const float moff = -mn * qs;
+        float p[8];
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = keep[e] ? fast_exp2(fmaf(x[e], qs, moff)) : 0.f;
+          ps += p[e];
+        }
+        l_run[n] = fmaf(l_run[n], alpha, ps);
+#pragma unroll
+        for (int u = 0; u < DPL; ++u) acc[n][u] *= alpha;
+        pb[n] = make_uint4(pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3]), pack2<DT>(p[4], p[5]),
+                           pack2<DT>(p[6], p[7]));
+      }
+      // V rows of the lane's eight k-slot tokens at dims [DPL*c, DPL*c + DPL).
+      VVec vr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vr[e] = *reinterpret_cast<const VVec*>(&sV[buf][16 * (e >> 2) + 4 * G + (e & 3)][DPL * c]);
+#pragma unroll
+      for (int u = 0; u < DPL; ++u) {
+        const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;
+        const int w = u >> 1;
+        const uint4 va = make_uint4(__builtin_amdgcn_perm((&vr[1].x)[w], (&vr[0].x)[w], sel),
+                                    __builtin_amdgcn_perm((&vr[3].x)[w], (&vr[2].x)[w], sel),
+                                    __builtin_amdgcn_perm((&vr[5].x)[w], (&vr[4].x)[w], sel),
+                                    __builtin_amdgcn_perm((&vr[7].x)[w], (&vr[6].x)[w], sel));
+#pragma unroll
+        for (int n = 0; n < NC; ++n) acc[n][u] = mfma32<DT>(va, pb[n], acc[n][u]);
+      }
+    }
+    if (more) stash(buf ^ 1);
+    __syncthreads();
+  }
+  if (bad) s_bad = 1;
+  __syncthreads();
+  const bool wg_bad = s_bad != 0;
+
+  // Epilogue: lane (G, c) holds dims [4*DPL*G, 4*DPL*G + 4*DPL) of row c of
+  // each column group (acc[n][u][j] is dim DPL*(4G + j) + u).
+  if (!wave_on) return;
+#pragma unroll
+  for (int n = 0; n < NC; ++n) {
+    const float lt = sum_groups(l_run[n], x16, x32);
+    const int rho = rho_w0 + 16 * n + c;
+    if (rho >= rows) continue;
+    const int i = rho / g, h = rho - i * g;
+    const float inv = wg_bad ? __builtin_nanf("") : 1.f / lt;
+    float f[4 * DPL];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int u = 0; u < DPL; ++u) f[j * DPL + u] = acc[n][u][j] * inv;
+    char* dst = reinterpret_cast<char*>(a.out) + (((size_t)(q0 + i) * a.Hq + kvh * g + h) * D + 4 * DPL * G) * 2;
+#pragma unroll
+    for (int v = 0; v < DPL / 2; ++v) *reinterpret_cast<uint4*>(dst + 16 * v) = pack16<DT>(f + 8 * v);
+  }
+}
+
+template <int DT, int D>
+void launch_nc(const PrefillArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC>), dim3(a.grid), dim3(256), 0, st, a);
+}
+
+template <int DT>
+void launch_d(const PrefillArgs& a, hipStream_t st) {
+  if (a.D == 64)
+    launch_nc<DT, 64>(a, st);
+  else
+    launch_nc<DT, 128>(a, st);
+}
+
+}  // namespace
+
+void launch_prefill_mfma(const PrefillArgs& a, hipStream_t st) {
+  if (a.dtype == PA_FP16)
+    launch_d<PA_FP16>(a, st);
+  else
+    launch_d<PA_BF16>(a, st);
+}
+
+}  // namespace pa

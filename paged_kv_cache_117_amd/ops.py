@@ -108,6 +108,41 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_cont
     return out
 
 
+def prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale: float, max_query_len: int,
+            out=None, stream=None):
+    """Paged attention for a chunk of new tokens per sequence (pa_prefill).
+
+    ``q`` is [N][Hq][D] with sequence s owning rows query_start[s] ..
+    query_start[s+1]-1; returns ``out`` of q's shape.
+    """
+    _device_tensor(q, "q", ndim=3)
+    N, Hq, D = q.shape
+    _device_tensor(k_pool, "k_pool", q.dtype, 4)
+    _device_tensor(v_pool, "v_pool", q.dtype, 4)
+    if k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool shapes differ")
+    nb, Hkv, bs, Dk = k_pool.shape
+    if Dk != D:
+        raise ValueError(f"head_dim mismatch: q {D}, pools {Dk}")
+    _device_tensor(block_tables, "block_tables", torch.int32, 2)
+    _device_tensor(context_lens, "context_lens", torch.int32, 1)
+    _device_tensor(query_start, "query_start", torch.int32, 1)
+    B = context_lens.shape[0]
+    if block_tables.shape[0] != B or query_start.shape[0] != B + 1:
+        raise ValueError("block_tables rows must equal num_seqs and query_start must have num_seqs + 1 entries")
+    if out is None:
+        out = torch.empty_like(q)
+    _device_tensor(out, "out", q.dtype, 3)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    st = LIB.pa_prefill(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                        block_tables.data_ptr(), context_lens.data_ptr(), query_start.data_ptr(), B, N, Hq,
+                        Hkv, D, bs, nb, block_tables.shape[1], int(max_query_len), float(scale),
+                        _dtype_code(q), _stream_handle(stream))
+    check_status(st, "pa_prefill")
+    return out
+
+
 def write_kv(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
     """Store new tokens' K/V rows at their slots (pa_write_kv)."""
     _device_tensor(k_pool, "k_pool", ndim=4)

@@ -115,3 +115,27 @@ def test_one_hip_runtime_in_the_process():
     """libpa binds to torch's HIP runtime; a second copy would not see the device."""
     maps = [line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line]
     assert len(set(maps)) == 1, sorted(set(maps))
+
+
+def call_prefill(**kw):
+    a = dict(out=16, q=16, k=16, v=16, bt=16, cl=16, qs=16, B=1, N=4, Hq=2, Hkv=2, D=64, bs=16, nb=4, maxb=2,
+             maxq=4, scale=0.125, dt=2, stream=NULL)
+    a.update(kw)
+    return L.pa_prefill(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["qs"], a["B"], a["N"], a["Hq"],
+                        a["Hkv"], a["D"], a["bs"], a["nb"], a["maxb"], a["maxq"], a["scale"], a["dt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bs=8), 3), (dict(D=96), 3), (dict(dt=7), 3), (dict(dt=0), 3),
+    (dict(Hq=3, Hkv=2), 2), (dict(maxq=5), 2), (dict(N=-1), 2), (dict(B=-1), 2), (dict(nb=0), 2),
+    (dict(scale=float("nan")), 2), (dict(qs=NULL), 1), (dict(q=NULL), 1), (dict(out=8), 2),
+])
+def test_prefill_host_validation(kw, status):
+    """Rejected before any device work (these calls never reach the GPU)."""
+    assert call_prefill(**kw) == status
+    assert L.pa_last_error().decode()
+
+
+def test_prefill_without_rows_is_a_no_op():
+    assert call_prefill(N=0, maxq=0, out=NULL, q=NULL, qs=NULL) == 0
+    assert call_prefill(B=0, out=NULL, q=NULL) == 0

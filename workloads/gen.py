@@ -247,3 +247,133 @@ def make_workload(key: str) -> Workload:
             "c5", "fp16", lambda r: r.integers(4096, 8192, size=128, endpoint=True),
             64, 8, 128, seed=5, partition_size=512)
     raise KeyError(key)
+
+
+# ----------------------------------------------------------------------------
+# Chunked-prefill steps
+# ----------------------------------------------------------------------------
+
+@dataclass
+class PrefillWorkload:
+    """One chunked-prefill step's inputs, as host arrays.
+
+    Sequence s holds ``prior_lens[s]`` cached tokens before the step; the
+    step appends ``chunk_lens[s]`` new tokens (their K/V in ``k_new`` /
+    ``v_new``, their queries in ``q``, rows ``query_start[s]`` ..
+    ``query_start[s+1]-1``) and attends over ``context_lens = prior + chunk``
+    positions.  ``ops`` builds the pre-step state.
+    """
+
+    name: str
+    dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    num_blocks: int
+    scale: float
+    prior_lens: np.ndarray  # int32 [B]
+    chunk_lens: np.ndarray  # int32 [B]
+    perm: np.ndarray  # int32 [num_blocks]
+    q: np.ndarray  # storage [N][Hq][D]
+    k_pool: np.ndarray  # storage [num_blocks][Hkv][bs][D]
+    v_pool: np.ndarray
+    k_new: np.ndarray  # storage [N][Hkv][D]
+    v_new: np.ndarray
+    ops: list
+    seq_ids: list
+    block_size: int = BLOCK_SIZE
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.seq_ids)
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.chunk_lens.sum())
+
+    @property
+    def context_lens(self) -> np.ndarray:
+        return (self.prior_lens + self.chunk_lens).astype(np.int32)
+
+    @property
+    def query_start(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.chunk_lens)]).astype(np.int32)
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.chunk_lens.max()) if len(self.chunk_lens) else 0
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if len(self.chunk_lens) else 0
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return max(1, -(-self.max_context_len // self.block_size))
+
+
+PREFILL_CONFIGS = {
+    "p0": "tiny bf16: 6 seqs, chunks {1,7,16,33,130,0}, priors {0,20,5,64,100,9}, Hq=8, Hkv=2, D=64",
+    "p1": "Llama-3.1-8B layer, bf16: 8 seqs x 512-token chunks, prior context U[0,3584], Hq=32, Hkv=8, D=128",
+    "p2": "Qwen2.5-72B layer, fp16: 4 seqs x 1024-token chunks, prior context U[0,7168], Hq=64, Hkv=8, D=128",
+    "p3": "mixed step, Llama shapes, bf16: 4 chunks of 512 (prior U[0,3584]) + 60 single tokens (prior U[127,4095])",
+}
+
+
+def make_prefill_custom(name, dtype, prior_lens, chunk_lens, num_q_heads, num_kv_heads, head_dim, seed,
+                        pool_factor: float = 1.25) -> PrefillWorkload:
+    """Independent sequences: each holds its prior tokens, then one chunk is appended.
+
+    ``prior_lens`` / ``chunk_lens`` may be lists or one callable
+    ``rng -> (prior, chunk)`` drawn from the lengths stream.
+    """
+    if callable(prior_lens):
+        prior, chunk = prior_lens(_rng(seed, _S_LENS))
+    else:
+        prior, chunk = prior_lens, chunk_lens
+    prior = np.asarray(prior, dtype=np.int32)
+    chunk = np.asarray(chunk, dtype=np.int32)
+    assert prior.shape == chunk.shape and (prior >= 0).all() and (chunk >= 0).all()
+    need, nb = _pool_blocks(prior + chunk, pool_factor)
+    nb = max(nb, need, 1)
+    B, N = len(prior), int(chunk.sum())
+    D, Hq, Hkv = head_dim, num_q_heads, num_kv_heads
+    perm = _rng(seed, _S_PERM).permutation(nb).astype(np.int32)
+    q = _normal_storage(seed, _S_Q, (N, Hq, D), dtype)
+    k_pool = _normal_storage(seed, _S_K, (nb, Hkv, BLOCK_SIZE, D), dtype)
+    v_pool = _normal_storage(seed, _S_V, (nb, Hkv, BLOCK_SIZE, D), dtype)
+    k_new = _normal_storage(seed, _S_KNEW, (N, Hkv, D), dtype)
+    v_new = _normal_storage(seed, _S_VNEW, (N, Hkv, D), dtype)
+    ops = []
+    for s in range(B):
+        ops.append(("add", s))
+        if prior[s] > 0:
+            ops.append(("append", s, int(prior[s])))
+    return PrefillWorkload(
+        name=name, dtype=dtype, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, num_blocks=nb,
+        scale=float(np.float32(1.0) / np.sqrt(np.float32(D))), prior_lens=prior, chunk_lens=chunk,
+        perm=perm, q=q, k_pool=k_pool, v_pool=v_pool, k_new=k_new, v_new=v_new, ops=ops,
+        seq_ids=list(range(B)), meta={"seed": seed, "pool_need": need})
+
+
+def make_prefill_workload(key: str) -> PrefillWorkload:
+    """The named chunked-prefill workloads (see PREFILL_CONFIGS)."""
+    key = key.lower()
+    if key == "p0":
+        return make_prefill_custom("p0", "bf16", [0, 20, 5, 64, 100, 9], [1, 7, 16, 33, 130, 0], 8, 2, 64, seed=10)
+    if key == "p1":
+        return make_prefill_custom(
+            "p1", "bf16", lambda r: (r.integers(0, 3584, size=8, endpoint=True), np.full(8, 512)),
+            None, 32, 8, 128, seed=11)
+    if key == "p2":
+        return make_prefill_custom(
+            "p2", "fp16", lambda r: (r.integers(0, 7168, size=4, endpoint=True), np.full(4, 1024)),
+            None, 64, 8, 128, seed=12)
+    if key == "p3":
+        def lens(r):
+            pri = np.concatenate([r.integers(0, 3584, size=4, endpoint=True),
+                                  r.integers(127, 4095, size=60, endpoint=True)])
+            return pri, np.concatenate([np.full(4, 512), np.ones(60, np.int64)])
+        return make_prefill_custom("p3", "bf16", lens, None, 32, 8, 128, seed=13)
+    raise KeyError(key)
