@@ -49,12 +49,24 @@ WORKLOAD_NAMES = {
 }
 
 
+# Chunked-prefill workloads (pa_write_kv of the chunk + pa_prefill per step)
+PREFILL_METRIC = "paged chunked-prefill attention TFLOP/s (% of MI355X dense 16-bit MFMA peak); tokens/s"
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}  # MI355X dense, vendor figure
+PREFILL_NAMES = {
+    "p1": "Llama-3.1-8B prefill chunk layer bf16 (8 seqs x 512-token chunks, prior context U[0,3584], "
+          "Hq=32, Hkv=8, D=128, block 16)",
+    "p2": "Qwen2.5-72B prefill chunk layer fp16 (4 seqs x 1024-token chunks, prior context U[0,7168], "
+          "Hq=64, Hkv=8, D=128, block 16)",
+    "p3": "mixed chunked-prefill step bf16, Llama shapes (4 chunks of 512 + 60 single tokens)",
+}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_NAMES) + sorted(PREFILL_NAMES))
     ap.add_argument("--partition-size", type=int, default=None,
                     help="positions per partition; 0 = automatic even split (default: the workload's, "
                          "512 for c5, automatic otherwise)")
@@ -260,6 +272,166 @@ def cpu_baseline(w, tables, budget_s):
     }
 
 
+def prefill_cpu_baseline(w, tables, budget_s):
+    """The oracle's prefill on the first rows of the first sequence: those
+    rows of the real workload, computed as a chunk of their own (same
+    positions), as many as fit the budget; TFLOP/s of those rows."""
+    import oracle  # test infrastructure: only this leg of the bench uses it
+    from paged_kv_cache_117_amd import metrics
+
+    P = int(w.prior_lens[0])
+
+    def run(n):
+        t0 = time.perf_counter()
+        oracle.prefill(w.q[:n], w.k_pool, w.v_pool, tables[:1], [P + n], [0, n], w.scale, w.dtype)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    t4 = run(4)
+    per_row = max((t4 - t1) / 3, 1e-6)
+    n = max(1, min(int(w.chunk_lens[0]), int((budget_s - max(t1 - per_row, 0.0)) / per_row)))
+    dt = run(n)
+    fl = metrics.prefill_flops([P], [n], w.num_q_heads, w.head_dim)
+    return {
+        "value": round(fl / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle prefill (gather + two-pass softmax per row) over the first {n} of "
+                   f"{int(w.chunk_lens[0])} chunk tokens of sequence 0 (prior {P}), {dt:.3f} s; "
+                   f"tokens/s {n / dt:.2f}; host CPU: {cpu_info()}"),
+    }
+
+
+def main_prefill(args):
+    """One chunked-prefill step per iteration: write the chunk's K/V, then
+    pa_prefill over every sequence's context."""
+    import torch
+
+    import paged_kv_cache_117_amd as pa
+    from paged_kv_cache_117_amd import metrics
+    from workloads import make_prefill_workload
+
+    w = make_prefill_workload(args.config)
+    eb = metrics.ELEM_BYTES[w.dtype]
+    tdt = {"fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    order = w.perm if args.placement == "shuffled" else np.arange(w.num_blocks, dtype=np.int32)
+    bm = pa.BlockManager(w.num_blocks, w.block_size, order)
+    bm.replay(w.ops)
+    t0 = time.perf_counter()
+    slots = []
+    for s, sid in enumerate(w.seq_ids):
+        if w.chunk_lens[s]:
+            slots.extend(bm.append(sid, int(w.chunk_lens[s])))
+    slots = np.asarray(slots, dtype=np.int64)
+    tables = bm.tables(w.seq_ids, w.max_blocks_per_seq)
+    host_bm_ms = (time.perf_counter() - t0) * 1e3
+
+    def dev(a, kv=False):
+        a = np.ascontiguousarray(a)
+        if kv and w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    nb = w.num_blocks
+    pool_bytes = 2 * nb * w.num_kv_heads * w.block_size * w.head_dim * eb
+    R = args.sets or max(2, min(16, int(np.ceil(2**30 / pool_bytes))))
+    k1, v1 = dev(w.k_pool, True), dev(w.v_pool, True)
+    k_pool = torch.empty((R * nb,) + tuple(k1.shape[1:]), dtype=tdt, device="cuda")
+    v_pool = torch.empty_like(k_pool)
+    for r in range(R):
+        k_pool[r * nb:(r + 1) * nb].copy_(k1)
+        v_pool[r * nb:(r + 1) * nb].copy_(v1)
+    del k1, v1
+    q = dev(w.q, True)
+    k_new, v_new = dev(w.k_new, True), dev(w.v_new, True)
+    lens = dev(w.context_lens.astype(np.int32))
+    qstart = dev(w.query_start.astype(np.int32))
+    sets = []
+    for r in range(R):
+        t = np.where(tables >= 0, tables + r * nb, -1).astype(np.int32)
+        sets.append(dict(tables=dev(t), slots=dev(slots + r * nb * w.block_size), out=torch.empty_like(q)))
+    stream = torch.cuda.current_stream()
+
+    def step(r, ev=None):
+        s = sets[r]
+        pa.write_kv(k_pool, v_pool, k_new, v_new, s["slots"], stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.prefill(q, k_pool, v_pool, s["tables"], lens, qstart, w.scale, w.max_query_len, out=s["out"],
+                   stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i % R)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i % R, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    pf_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    pf_avg = float(pf_ms.mean())
+    flops = metrics.prefill_flops(w.prior_lens, w.chunk_lens, w.num_q_heads, w.head_dim)
+    io = metrics.prefill_io_bytes(w.prior_lens, w.chunk_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, eb)
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (pf_avg * 1e-3) / 1e12
+    res = {
+        "metric": PREFILL_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": PREFILL_NAMES[args.config],
+            "key": args.config,
+            "num_seqs": w.num_seqs,
+            "num_tokens": w.num_tokens,
+            "flops_per_step": flops,
+            "io_bytes_per_step": io,
+            "block_size": w.block_size,
+            "placement": args.placement,
+            "rotating_sets": R,
+        },
+        "mfma_peak_frac": round(value / peak, 4),
+        "tokens_per_s": round(w.num_tokens / (ms_step * 1e-3), 1),
+        "prefill_ms": round(pf_avg, 5),
+        "prefill_ms_median": round(float(np.median(pf_ms)), 5),
+        "prefill_io_gbps": round(io / (pf_avg * 1e-3) / 1e9, 2),
+        "host_block_manager_ms": round(host_bm_ms, 3),
+        "wall_s": round(wall, 3),
+        "roofline": {
+            "kernel": "pa_prefill",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = prefill_cpu_baseline(w, tables, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -270,6 +442,13 @@ def main():
               "multi-GPU mode: sequences or KV heads shard across GPUs with no exchange inside "
               "attention, so run one process per GPU.", file=sys.stderr)
         sys.exit(2)
+
+    if args.config in PREFILL_NAMES:
+        import torch
+
+        torch.cuda.set_device(0)
+        main_prefill(args)
+        return
 
     import torch
 

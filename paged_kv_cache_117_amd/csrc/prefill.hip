@@ -53,9 +53,12 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
-constexpr int kStep = 32;  // positions per step: two blocks
+constexpr int kPair = 32;                 // positions per compute pass: two blocks
+constexpr int kPairs = 2;                 // passes per step (one barrier, one load batch)
+constexpr int kStep = kPair * kPairs;     // positions per step
 
 template <int DT>
 __device__ __forceinline__ f32x4 mfma32(const uint4& a, const uint4& b, const f32x4& c) {
@@ -82,6 +85,10 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
   }
 }
+
+// 32-bit word w (a compile-time constant after unrolling) of a vector.
+__device__ __forceinline__ uint32_t word(const uint4& v, int w) { return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w; }
+__device__ __forceinline__ uint32_t word(const uint2& v, int w) { return w == 0 ? v.x : v.y; }
 
 // x combined with the value of lane (l ^ 16) and then (l ^ 32): the four
 // token groups of the MFMA output layout.
@@ -187,30 +194,45 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.kp);
   const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.vp);
   bool bad = false;
-  uint4 kreg[LOADS], vreg[LOADS];
-  auto issue = [&](int step) {
+  // (plain vector types: HIP's uint4 is copied by memcpy, which keeps these
+  // arrays in scratch memory)
+  u32x4 kreg[LOADS], vreg[LOADS];
+  // Block id behind each of this thread's loads of a step, fetched one step
+  // ahead of the K/V loads that use it.  These are per-lane vector loads on
+  // purpose: a scalar load would share its wait counter with the LDS operand
+  // reads, and since scalar loads complete out of order the first operand
+  // wait of every step would then also wait for the table lookup.
+  // Positions past L-1 read position L-1.
+  auto load_ids = [&](int step, int (&ids)[LOADS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < LOADS; ++m) {
+      const int tt = (tid + 256 * m) / CH;
+      ids[m] = btrow[min(step * kStep + tt, L - 1) >> 4];
+    }
+  };
+  auto issue = [&](int step, const int (&ids)[LOADS]) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < LOADS; ++m) {
       const int u = tid + 256 * m;
       const int tt = u / CH, ch = u - tt * CH;
       const int pos = min(step * kStep + tt, L - 1);
-      int id = btrow[pos >> 4];
+      int id = ids[m];
       if ((unsigned)id >= (unsigned)a.num_blocks) {
         bad = true;
         id = 0;
       }
       const size_t off = (size_t)id * blk_stride + head_off + (size_t)(pos & 15) * D + ch * 8;
-      kreg[m] = *reinterpret_cast<const uint4*>(kp + off);
-      vreg[m] = *reinterpret_cast<const uint4*>(vp + off);
+      kreg[m] = *reinterpret_cast<const u32x4*>(kp + off);
+      vreg[m] = *reinterpret_cast<const u32x4*>(vp + off);
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < LOADS; ++m) {
       const int u = tid + 256 * m;
       const int tt = u / CH, ch = u - tt * CH;
-      *reinterpret_cast<uint4*>(&sK[buf][tt][ch * 8]) = kreg[m];
-      *reinterpret_cast<uint4*>(&sV[buf][tt][ch * 8]) = vreg[m];
+      *reinterpret_cast<u32x4*>(&sK[buf][tt][ch * 8]) = kreg[m];
+      *reinterpret_cast<u32x4*>(&sV[buf][tt][ch * 8]) = vreg[m];
     }
   };
 
@@ -225,17 +247,24 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   }
 
   if (tid == 0) s_bad = 0;
-  issue(0);
+  int ids[LOADS];
+  load_ids(0, ids);
+  issue(0, ids);
   stash(0);
+  load_ids(1, ids);  // ids of the next step are always one step ahead of its loads
   __syncthreads();
 
   for (int step = 0; step < nsteps; ++step) {
     const int buf = step & 1;
     const bool more = step + 1 < nsteps;
-    if (more) issue(step + 1);
-    const int t0 = step * kStep;
-    if (wave_on && t0 <= lim_w_hi) {
-      // Scores for both 16-token halves of the step.
+    if (more) issue(step + 1, ids);
+    if (step + 2 < nsteps) load_ids(step + 2, ids);
+#pragma unroll
+    for (int pp = 0; pp < kPairs; ++pp) {
+      const int t0 = step * kStep + pp * kPair;
+      const int r0 = pp * kPair;  // LDS row of the pass's first token
+      if (!(wave_on && t0 <= lim_w_hi)) continue;
+      // Scores for both 16-token halves of the pass.
       f32x4 sc[NC][2];
 #pragma unroll
       for (int n = 0; n < NC; ++n) sc[n][0] = sc[n][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -243,14 +272,14 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
       for (int half = 0; half < 2; ++half) {
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
-          const uint4 ka = *reinterpret_cast<const uint4*>(&sK[buf][16 * half + c][32 * k + 8 * G]);
+          const uint4 ka = *reinterpret_cast<const uint4*>(&sK[buf][r0 + 16 * half + c][32 * k + 8 * G]);
 #pragma unroll
           for (int n = 0; n < NC; ++n) sc[n][half] = mfma32<DT>(ka, qr[n][k], sc[n][half]);
         }
       }
       // Online softmax; weights packed as the PV B operand (k-slot e of
-      // lane group G is token 16*(e/4) + 4G + e%4 of the step).
-      const bool diag = t0 + kStep - 1 > lim_w_lo;
+      // lane group G is token 16*(e/4) + 4G + e%4 of the pass).
+      const bool diag = t0 + kPair - 1 > lim_w_lo;
       uint4 pb[NC];
 #pragma unroll
       for (int n = 0; n < NC; ++n) {
@@ -264,7 +293,7 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) bm = fmaxf(bm, keep[e] ? x[e] : -__builtin_huge_valf());
         bm = max_groups(bm, x16, x32);
-        const float mn = fmaxf(m_run[n], bm);  // finite: position 0 is in every row's first step
+        const float mn = fmaxf(m_run[n], bm);  // finite: position 0 is in every row's first pass
         const float alpha = fast_exp2((m_run[n] - mn) * qs);
         m_run[n] = mn;
         const float moff = -mn * qs;
@@ -285,15 +314,15 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
       VVec vr[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        vr[e] = *reinterpret_cast<const VVec*>(&sV[buf][16 * (e >> 2) + 4 * G + (e & 3)][DPL * c]);
+        vr[e] = *reinterpret_cast<const VVec*>(&sV[buf][r0 + 16 * (e >> 2) + 4 * G + (e & 3)][DPL * c]);
 #pragma unroll
       for (int u = 0; u < DPL; ++u) {
         const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;
         const int w = u >> 1;
-        const uint4 va = make_uint4(__builtin_amdgcn_perm((&vr[1].x)[w], (&vr[0].x)[w], sel),
-                                    __builtin_amdgcn_perm((&vr[3].x)[w], (&vr[2].x)[w], sel),
-                                    __builtin_amdgcn_perm((&vr[5].x)[w], (&vr[4].x)[w], sel),
-                                    __builtin_amdgcn_perm((&vr[7].x)[w], (&vr[6].x)[w], sel));
+        const uint4 va = make_uint4(__builtin_amdgcn_perm(word(vr[1], w), word(vr[0], w), sel),
+                                    __builtin_amdgcn_perm(word(vr[3], w), word(vr[2], w), sel),
+                                    __builtin_amdgcn_perm(word(vr[5], w), word(vr[4], w), sel),
+                                    __builtin_amdgcn_perm(word(vr[7], w), word(vr[6], w), sel));
 #pragma unroll
         for (int n = 0; n < NC; ++n) acc[n][u] = mfma32<DT>(va, pb[n], acc[n][u]);
       }

@@ -1,4 +1,4 @@
-"""Byte counts for the decode step (pure arithmetic, no device code).
+"""Byte and flop counts for the decode and chunked-prefill steps (pure arithmetic, no device code).
 
 KV bytes per token across the model: 2 (K and V) x layers x KV heads x head
 dim x bytes per element (vLLM's PagedAttention: How Memory Management
@@ -57,3 +57,30 @@ def decode_io_bytes(context_lens, num_q_heads: int, num_kv_heads: int, head_dim:
 def write_kv_bytes(num_tokens: int, num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
     """New K/V rows read and written, plus the int64 slots."""
     return num_tokens * (2 * 2 * num_kv_heads * head_dim * elem_bytes + 8)
+
+
+def prefill_pairs(prior_lens, chunk_lens) -> int:
+    """(query token, key position) pairs of one chunked-prefill launch per
+    query head: token i of a chunk of T after P cached tokens sees P + i + 1
+    positions."""
+    n = 0
+    for P, T in zip(prior_lens, chunk_lens):
+        P, T = int(P), int(T)
+        n += T * P + T * (T + 1) // 2
+    return n
+
+
+def prefill_flops(prior_lens, chunk_lens, num_q_heads: int, head_dim: int) -> int:
+    """Algorithmic flops of one chunked-prefill attention launch: per (query
+    head, query token, visible position) 2*D for the score and 2*D for the
+    weighted V row (the softmax itself is not counted)."""
+    return 4 * head_dim * num_q_heads * prefill_pairs(prior_lens, chunk_lens)
+
+
+def prefill_io_bytes(prior_lens, chunk_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                     elem_bytes: int) -> int:
+    """Each sequence's K+V rows read once, q read and out written once."""
+    ctx = sum(int(P) + int(T) for P, T in zip(prior_lens, chunk_lens))
+    toks = sum(int(T) for T in chunk_lens)
+    return (ctx * kv_bytes_per_token(1, num_kv_heads, head_dim, elem_bytes)
+            + 2 * toks * num_q_heads * head_dim * elem_bytes)

@@ -90,3 +90,15 @@ def test_unique_kv_bytes_count_shared_blocks_once():
     lens = [nb * 16 + 1] * 8
     assert metrics.decode_unique_kv_bytes(tables, lens, 8, 128, 2) == (nb * 16 + 8) * per_tok
     assert metrics.decode_kv_bytes(lens, 8, 128, 2) == 8 * (nb * 16 + 1) * per_tok
+
+
+def test_prefill_pairs_count_the_causal_mask():
+    """Pairs = ones of the [T][P+T] causal mask tril(diagonal=P), by brute force."""
+    import numpy as np
+
+    prior = [0, 3, 17, 100, 5]
+    chunk = [9, 1, 0, 33, 64]
+    want = sum(int(np.tril(np.ones((T, P + T)), k=P).sum()) for P, T in zip(prior, chunk))
+    assert metrics.prefill_pairs(prior, chunk) == want
+    assert metrics.prefill_flops(prior, chunk, 32, 128) == 4 * 128 * 32 * want
+    assert metrics.prefill_io_bytes([10], [6], 4, 2, 64, 2) == 16 * 2 * 2 * 64 * 2 + 2 * 6 * 4 * 64 * 2
