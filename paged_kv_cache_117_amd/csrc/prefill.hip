@@ -246,6 +246,92 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
     for (int u = 0; u < DPL; ++u) acc[n][u] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // One pass over 32 positions starting at t0 (LDS rows r0..r0+31).
+  // Lazy rescaling: the weights use a reference max m_run that is raised
+  // only when some row of the wave sees a score more than 2^kSlack above it
+  // (then every row moves to its true running max); otherwise the weights
+  // may exceed 1, by at most 2^kSlack, and the accumulators keep their
+  // scale.  l and acc always share the reference, so o = acc / l is exact.
+  constexpr float kSlack = 8.f;
+  auto pass = [&](auto masked, int buf, int r0, int t0) __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked)::value;
+    f32x4 sc[NC][2];
+#pragma unroll
+    for (int n = 0; n < NC; ++n) sc[n][0] = sc[n][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(&sK[buf][r0 + 16 * half + c][32 * k + 8 * G]);
+#pragma unroll
+        for (int n = 0; n < NC; ++n) sc[n][half] = mfma32<DT>(ka, qr[n][k], sc[n][half]);
+      }
+    }
+    // Scores of the lane's eight k-slots (k-slot e of lane group G is token
+    // 16*(e/4) + 4G + e%4 of the pass), masked past each row's limit.
+    float x[NC][8];
+    float bm[NC];
+    bool grow = false;
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[n][e] = sc[n][e >> 2][e & 3];
+        if constexpr (kMasked)
+          if (t0 + 16 * (e >> 2) + 4 * G + (e & 3) > lim[n]) x[n][e] = -__builtin_huge_valf();
+      }
+      float b = fmaxf(fmaxf(fmaxf(x[n][0], x[n][1]), fmaxf(x[n][2], x[n][3])),
+                      fmaxf(fmaxf(x[n][4], x[n][5]), fmaxf(x[n][6], x[n][7])));
+      bm[n] = max_groups(b, x16, x32);
+      grow |= (bm[n] - m_run[n]) * qs > kSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int n = 0; n < NC; ++n) {
+        const float mn = fmaxf(m_run[n], bm[n]);
+        const float alpha = fast_exp2((m_run[n] - mn) * qs);
+        m_run[n] = mn;
+        l_run[n] *= alpha;
+#pragma unroll
+        for (int u = 0; u < DPL; ++u) acc[n][u] *= alpha;
+      }
+    }
+    uint4 pb[NC];
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+      const float moff = -m_run[n] * qs;
+      float p[8];
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // a masked score is -inf: 2^-inf = 0 (a zero scale never reaches a
+        // masked pass with a finite weight: 0 * -inf is NaN, so select)
+        p[e] = fast_exp2(fmaf(x[n][e], qs, moff));
+        if constexpr (kMasked) p[e] = x[n][e] == -__builtin_huge_valf() ? 0.f : p[e];
+        ps += p[e];
+      }
+      l_run[n] += ps;
+      pb[n] = make_uint4(pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3]), pack2<DT>(p[4], p[5]),
+                         pack2<DT>(p[6], p[7]));
+    }
+    // V rows of the lane's eight k-slot tokens at dims [DPL*c, DPL*c + DPL).
+    VVec vr[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      vr[e] = *reinterpret_cast<const VVec*>(&sV[buf][r0 + 16 * (e >> 2) + 4 * G + (e & 3)][DPL * c]);
+#pragma unroll
+    for (int u = 0; u < DPL; ++u) {
+      const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;
+      const int w = u >> 1;
+      const uint4 va = make_uint4(__builtin_amdgcn_perm(word(vr[1], w), word(vr[0], w), sel),
+                                  __builtin_amdgcn_perm(word(vr[3], w), word(vr[2], w), sel),
+                                  __builtin_amdgcn_perm(word(vr[5], w), word(vr[4], w), sel),
+                                  __builtin_amdgcn_perm(word(vr[7], w), word(vr[6], w), sel));
+#pragma unroll
+      for (int n = 0; n < NC; ++n) acc[n][u] = mfma32<DT>(va, pb[n], acc[n][u]);
+    }
+  };
+
   if (tid == 0) s_bad = 0;
   int ids[LOADS];
   load_ids(0, ids);
@@ -262,70 +348,12 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
 #pragma unroll
     for (int pp = 0; pp < kPairs; ++pp) {
       const int t0 = step * kStep + pp * kPair;
-      const int r0 = pp * kPair;  // LDS row of the pass's first token
       if (!(wave_on && t0 <= lim_w_hi)) continue;
-      // Scores for both 16-token halves of the pass.
-      f32x4 sc[NC][2];
-#pragma unroll
-      for (int n = 0; n < NC; ++n) sc[n][0] = sc[n][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-#pragma unroll
-        for (int k = 0; k < KS; ++k) {
-          const uint4 ka = *reinterpret_cast<const uint4*>(&sK[buf][r0 + 16 * half + c][32 * k + 8 * G]);
-#pragma unroll
-          for (int n = 0; n < NC; ++n) sc[n][half] = mfma32<DT>(ka, qr[n][k], sc[n][half]);
-        }
-      }
-      // Online softmax; weights packed as the PV B operand (k-slot e of
-      // lane group G is token 16*(e/4) + 4G + e%4 of the pass).
-      const bool diag = t0 + kPair - 1 > lim_w_lo;
-      uint4 pb[NC];
-#pragma unroll
-      for (int n = 0; n < NC; ++n) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = sc[n][e >> 2][e & 3];
-        bool keep[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) keep[e] = !diag || t0 + 16 * (e >> 2) + 4 * G + (e & 3) <= lim[n];
-        float bm = -__builtin_huge_valf();
-#pragma unroll
-        for (int e = 0; e < 8; ++e) bm = fmaxf(bm, keep[e] ? x[e] : -__builtin_huge_valf());
-        bm = max_groups(bm, x16, x32);
-        const float mn = fmaxf(m_run[n], bm);  // finite: position 0 is in every row's first pass
-        const float alpha = fast_exp2((m_run[n] - mn) * qs);
-        m_run[n] = mn;
-        const float moff = -mn * qs;
-        float p[8];
-        float ps = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = keep[e] ? fast_exp2(fmaf(x[e], qs, moff)) : 0.f;
-          ps += p[e];
-        }
-        l_run[n] = fmaf(l_run[n], alpha, ps);
-#pragma unroll
-        for (int u = 0; u < DPL; ++u) acc[n][u] *= alpha;
-        pb[n] = make_uint4(pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3]), pack2<DT>(p[4], p[5]),
-                           pack2<DT>(p[6], p[7]));
-      }
-      // V rows of the lane's eight k-slot tokens at dims [DPL*c, DPL*c + DPL).
-      VVec vr[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vr[e] = *reinterpret_cast<const VVec*>(&sV[buf][r0 + 16 * (e >> 2) + 4 * G + (e & 3)][DPL * c]);
-#pragma unroll
-      for (int u = 0; u < DPL; ++u) {
-        const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;
-        const int w = u >> 1;
-        const uint4 va = make_uint4(__builtin_amdgcn_perm(word(vr[1], w), word(vr[0], w), sel),
-                                    __builtin_amdgcn_perm(word(vr[3], w), word(vr[2], w), sel),
-                                    __builtin_amdgcn_perm(word(vr[5], w), word(vr[4], w), sel),
-                                    __builtin_amdgcn_perm(word(vr[7], w), word(vr[6], w), sel));
-#pragma unroll
-        for (int n = 0; n < NC; ++n) acc[n][u] = mfma32<DT>(va, pb[n], acc[n][u]);
-      }
+      // Only passes that reach past a row's causal limit need the mask.
+      if (t0 + kPair - 1 > lim_w_lo)
+        pass(std::true_type{}, buf, pp * kPair, t0);
+      else
+        pass(std::false_type{}, buf, pp * kPair, t0);
     }
     if (more) stash(buf ^ 1);
     __syncthreads();
