@@ -128,15 +128,20 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   __shared__ __align__(16) uint16_t sV[2][kStep][ROW];
   __shared__ int s_bad;
 
-  // XCD-aware numbering: the hardware deals workgroups round-robin over the
-  // 8 XCDs; give each XCD a contiguous range of work items so the tiles of
-  // one (sequence, KV head) share that XCD's L2.
-  const int per_xcd = a.grid >> 3;
-  const int vid = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  const int tile = a.tiles - 1 - vid % a.tiles;  // latest rows (longest walks) first
-  const int rest = vid / a.tiles;
-  const int kvh = rest % a.Hkv;
-  const int s = rest / a.Hkv;
+  // XCD-aware numbering.  The hardware deals workgroups round-robin over the
+  // 8 XCDs (workgroup b runs on XCD b % 8).  Work item (sequence, KV head)
+  // number i goes to XCD i % 8, so all row tiles of one item share that
+  // XCD's L2 while the items -- and with 8 KV heads, one head of every
+  // sequence -- are spread evenly over the XCDs.  Within an XCD the tiles
+  // are ordered latest rows (longest walks) first, across all its items.
+  const int items = a.B * a.Hkv;
+  const int per_xcd = (items + 7) >> 3;  // items per XCD (upper bound)
+  const int xcd = (int)(blockIdx.x & 7), local = (int)(blockIdx.x >> 3);
+  const int item = (local % per_xcd) * 8 + xcd;
+  const int tile = a.tiles - 1 - local / per_xcd;
+  if (item >= items) return;
+  const int kvh = item % a.Hkv;
+  const int s = item / a.Hkv;
   if (s >= a.B) return;
 
   const int q0 = a.qs[s], q1 = a.qs[s + 1], L = a.cl[s];

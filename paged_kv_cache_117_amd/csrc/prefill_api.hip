@@ -68,9 +68,11 @@ extern "C" pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, 
   a.neg_scale = scale < 0.f;
   a.qscale = fabsf(scale) * 1.4426950408889634f;
   a.dtype = dtype;
+  // Grid: 8 XCDs x ceil(items / 8) work items x row tiles (the kernel maps
+  // each workgroup to an item and tile; see prefill.hip).
   const int64_t tiles = ((int64_t)max_query_len * a.g + kPrefillRows - 1) / kPrefillRows;
-  const int64_t items = tiles * num_kv_heads * num_seqs;
-  const int64_t grid = (items + 7) / 8 * 8;
+  const int64_t items = (int64_t)num_kv_heads * num_seqs;
+  const int64_t grid = 8 * ((items + 7) / 8) * tiles;
   if (grid > 0x7fffffffLL)
     return fail(PA_ERR_SHAPE, "pa_prefill: launch of %lld workgroups is too large", (long long)grid);
   a.tiles = (int)tiles;

@@ -25,7 +25,7 @@ struct PrefillArgs {
   int B, N, Hq, Hkv, g, D;
   int num_blocks, maxb, max_ctx, max_q;
   int tiles;      // row tiles per (sequence, KV head) in the launch
-  int grid;       // workgroups launched (a multiple of 8)
+  int grid;       // workgroups launched: 8 * ceil(B * Hkv / 8) * tiles
   int neg_scale;  // scale < 0: the kernel flips the query's sign
   float qscale;   // |scale| * log2(e)
   pa_dtype_t dtype;
