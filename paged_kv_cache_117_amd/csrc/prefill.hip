@@ -90,15 +90,11 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 __device__ __forceinline__ uint32_t word(const uint4& v, int w) { return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w; }
 __device__ __forceinline__ uint32_t word(const uint2& v, int w) { return w == 0 ? v.x : v.y; }
 
-// x combined with the value of lane (l ^ 16) and then (l ^ 32): the four
-// token groups of the MFMA output layout.
+// Max of x over lanes l, l ^ 16, l ^ 32 and l ^ 48: the four token groups
+// of the MFMA output layout.
 __device__ __forceinline__ float max_groups(float x, int x16, int x32) {
   x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x16, __builtin_bit_cast(int, x))));
   return fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, x))));
-}
-__device__ __forceinline__ float sum_groups(float x, int x16, int x32) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x16, __builtin_bit_cast(int, x)));
-  return x + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, x)));
 }
 
 // NaN into every element of query heads [h0, h0 + nh) of rows [r0, r1).
@@ -241,12 +237,13 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
     }
   };
 
-  float m_run[NC], l_run[NC];
+  float m_run[NC];
+  f32x4 l_acc[NC];  // row sums of the rounded weights, from the matrix core (all four entries equal)
   f32x4 acc[NC][DPL];
 #pragma unroll
   for (int n = 0; n < NC; ++n) {
     m_run[n] = -__FLT_MAX__;  // finite, so a zero scale gives 2^0, not NaN
-    l_run[n] = 0.f;
+    l_acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < DPL; ++u) acc[n][u] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -258,6 +255,8 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   // may exceed 1, by at most 2^kSlack, and the accumulators keep their
   // scale.  l and acc always share the reference, so o = acc / l is exact.
   constexpr float kSlack = 8.f;
+  constexpr uint32_t kOne2 = DT == PA_BF16 ? 0x3F803F80u : 0x3C003C00u;  // two 1.0s of the KV type
+  const uint4 ones = make_uint4(kOne2, kOne2, kOne2, kOne2);
   auto pass = [&](auto masked, int buf, int r0, int t0) __attribute__((always_inline)) {
     constexpr bool kMasked = decltype(masked)::value;
     f32x4 sc[NC][2];
@@ -273,9 +272,12 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
       }
     }
     // Scores of the lane's eight k-slots (k-slot e of lane group G is token
-    // 16*(e/4) + 4G + e%4 of the pass), masked past each row's limit.
+    // 16*(e/4) + 4G + e%4 of the pass), masked past each row's limit.  Each
+    // lane checks its own scores against the reference; only when some lane
+    // of the wave sees growth past the slack are the rows' maxima gathered
+    // across the four lane groups and the accumulators rescaled.
     float x[NC][8];
-    float bm[NC];
+    float lm[NC];
     bool grow = false;
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
@@ -285,18 +287,17 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
         if constexpr (kMasked)
           if (t0 + 16 * (e >> 2) + 4 * G + (e & 3) > lim[n]) x[n][e] = -__builtin_huge_valf();
       }
-      float b = fmaxf(fmaxf(fmaxf(x[n][0], x[n][1]), fmaxf(x[n][2], x[n][3])),
-                      fmaxf(fmaxf(x[n][4], x[n][5]), fmaxf(x[n][6], x[n][7])));
-      bm[n] = max_groups(b, x16, x32);
-      grow |= (bm[n] - m_run[n]) * qs > kSlack;
+      lm[n] = fmaxf(fmaxf(fmaxf(x[n][0], x[n][1]), fmaxf(x[n][2], x[n][3])),
+                    fmaxf(fmaxf(x[n][4], x[n][5]), fmaxf(x[n][6], x[n][7])));
+      grow |= (lm[n] - m_run[n]) * qs > kSlack;
     }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
       for (int n = 0; n < NC; ++n) {
-        const float mn = fmaxf(m_run[n], bm[n]);
+        const float mn = fmaxf(m_run[n], max_groups(lm[n], x16, x32));
         const float alpha = fast_exp2((m_run[n] - mn) * qs);
         m_run[n] = mn;
-        l_run[n] *= alpha;
+        l_acc[n] *= alpha;
 #pragma unroll
         for (int u = 0; u < DPL; ++u) acc[n][u] *= alpha;
       }
@@ -306,18 +307,17 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
     for (int n = 0; n < NC; ++n) {
       const float moff = -m_run[n] * qs;
       float p[8];
-      float ps = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        // a masked score is -inf: 2^-inf = 0 (a zero scale never reaches a
-        // masked pass with a finite weight: 0 * -inf is NaN, so select)
+        // a masked score is -inf: 2^-inf = 0 (with a zero scale 0 * -inf
+        // would be NaN, hence the select)
         p[e] = fast_exp2(fmaf(x[n][e], qs, moff));
         if constexpr (kMasked) p[e] = x[n][e] == -__builtin_huge_valf() ? 0.f : p[e];
-        ps += p[e];
       }
-      l_run[n] += ps;
       pb[n] = make_uint4(pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3]), pack2<DT>(p[4], p[5]),
                          pack2<DT>(p[6], p[7]));
+      // row sums of the rounded weights: an all-ones A operand
+      l_acc[n] = mfma32<DT>(ones, pb[n], l_acc[n]);
     }
     // V rows of the lane's eight k-slot tokens at dims [DPL*c, DPL*c + DPL).
     VVec vr[8];
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   if (!wave_on) return;
 #pragma unroll
   for (int n = 0; n < NC; ++n) {
-    const float lt = sum_groups(l_run[n], x16, x32);
+    const float lt = l_acc[n][0];
     const int rho = rho_w0 + 16 * n + c;
     if (rho >= rows) continue;
     const int i = rho / g, h = rho - i * g;
