@@ -61,12 +61,22 @@ PREFILL_NAMES = {
 }
 
 
+# Preemption by swapping (pa_swap_blocks out to pinned host memory and back)
+SWAP_METRIC = "paged KV swap-out + swap-in GB/s over the host link (pinned host pool)"
+HOST_LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction, vendor figure
+SWAP_NAMES = {
+    "s1": "swap of 8 Llama-3.1-8B sequences x 2048 tokens, one layer bf16 (1024 blocks of 8 KV heads x 16 x 128, "
+          "64 MiB K+V) to pinned host memory and back into other blocks",
+}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_NAMES) + sorted(PREFILL_NAMES))
+    ap.add_argument("--config", default="c2",
+                    choices=sorted(WORKLOAD_NAMES) + sorted(PREFILL_NAMES) + sorted(SWAP_NAMES))
     ap.add_argument("--partition-size", type=int, default=None,
                     help="positions per partition; 0 = automatic even split (default: the workload's, "
                          "512 for c5, automatic otherwise)")
@@ -432,6 +442,98 @@ def main_prefill(args):
     print(json.dumps(res), flush=True)
 
 
+def main_swap(args):
+    """One step = swap 1024 blocks out to a pinned host pool, then back in."""
+    import torch
+
+    import paged_kv_cache_117_amd as pa
+    import oracle  # test infrastructure: the cpu_baseline leg only
+
+    nblk, hkv, D = 1024, 8, 128
+    rng = np.random.default_rng(21)
+    dev_blocks = 4 * nblk
+    k = torch.randn(dev_blocks, hkv, 16, D, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn_like(k)
+    hk = torch.empty((nblk, hkv, 16, D), dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    src = rng.permutation(dev_blocks)[:nblk]
+    dst = rng.permutation(np.setdiff1d(np.arange(dev_blocks), src))[:nblk]
+    out_pairs = torch.from_numpy(np.stack([src, rng.permutation(nblk)], 1).astype(np.int32)).cuda()
+    in_pairs = torch.from_numpy(np.stack([out_pairs[:, 1].cpu().numpy(), dst], 1).astype(np.int32)).cuda()
+    stream = torch.cuda.current_stream()
+    moved = 2 * nblk * hkv * 16 * D * 2  # K and V bytes each way
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        pa.swap_blocks(hk, hv, k, v, out_pairs, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        pa.swap_blocks(k, v, hk, hv, in_pairs, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    out_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in evs]))
+    in_ms = float(np.mean([b.elapsed_time(c) for _, b, c in evs]))
+    # reference: the DMA engines copying one contiguous buffer of the same size each way
+    dbuf = torch.empty(moved // 2, dtype=torch.bfloat16, device="cuda")
+    hbuf = torch.empty(moved // 2, dtype=torch.bfloat16, pin_memory=True)
+    for _ in range(3):
+        hbuf.copy_(dbuf, non_blocking=True)
+        dbuf.copy_(hbuf, non_blocking=True)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record(stream)
+    for _ in range(5):
+        hbuf.copy_(dbuf, non_blocking=True)
+    e[1].record(stream)
+    for _ in range(5):
+        dbuf.copy_(hbuf, non_blocking=True)
+    e[2].record(stream)
+    torch.cuda.synchronize()
+    d2h = moved / (e[0].elapsed_time(e[1]) / 5 * 1e-3) / 1e9
+    h2d = moved / (e[1].elapsed_time(e[2]) / 5 * 1e-3) / 1e9
+    out_gbps = moved / (out_ms * 1e-3) / 1e9
+    in_gbps = moved / (in_ms * 1e-3) / 1e9
+    res = {
+        "metric": SWAP_METRIC, "value": round(2 * moved / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": SWAP_NAMES[args.config], "key": args.config, "blocks": nblk,
+                   "bytes_each_way": moved},
+        "swap_out_gbps": round(out_gbps, 2), "swap_in_gbps": round(in_gbps, 2),
+        "dma_contiguous_d2h_gbps": round(d2h, 2), "dma_contiguous_h2d_gbps": round(h2d, 2),
+        "roofline": {"kernel": "pa_swap_blocks (swap-out)", "bound": "host link", "achieved": round(out_gbps, 2),
+                     "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s", "frac": round(out_gbps / HOST_LINK_PEAK_GBPS, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        hk_np = np.zeros((nblk, hkv, 16, D), np.uint16)
+        k_np = rng.integers(0, 1 << 16, size=(dev_blocks // 4, hkv, 16, D), dtype=np.uint16)
+        pairs = np.stack([np.arange(dev_blocks // 4), np.arange(dev_blocks // 4)], 1)
+        t = time.perf_counter()
+        oracle.swap_blocks(hk_np, hk_np, k_np, k_np, pairs)
+        dt = time.perf_counter() - t
+        res["cpu_baseline"] = {"value": round(2 * k_np.nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"oracle swap_blocks of {dev_blocks // 4} blocks (K and V) between host "
+                                         f"arrays, {dt:.3f} s; host CPU: {cpu_info()}"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -443,6 +545,12 @@ def main():
               "attention, so run one process per GPU.", file=sys.stderr)
         sys.exit(2)
 
+    if args.config in SWAP_NAMES:
+        import torch
+
+        torch.cuda.set_device(0)
+        main_swap(args)
+        return
     if args.config in PREFILL_NAMES:
         import torch
 

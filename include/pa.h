@@ -206,6 +206,32 @@ pa_status_t pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_pair
                            int num_pairs, int num_kv_heads, int head_dim, int block_size,
                            int num_blocks, pa_dtype_t dtype, void* stream);
 
+/*
+ * pa_swap_blocks -- batched whole-block copies between two pools of the same
+ * block shape, for preemption by swapping: evicted blocks go from the device
+ * pool to a pool in host memory and come back later, possibly to other block
+ * ids (PagedAttention: Virtual Memory for the KV Cache, "Scheduling and
+ * preemption"; Batching and PagedAttention, FAQ on running out of blocks).
+ * For each pair (src, dst):
+ *   dst_k[dst] = src_k[src] and dst_v[dst] = src_v[src]  (every KV head, every slot).
+ * Swap-out: dst = host pool, src = device pool; swap-in the reverse; both
+ * device pools also work.  One launch; the GPU reads or writes the host pool
+ * directly over the host link.
+ *
+ *   dst_k, dst_v     [num_dst_blocks][num_kv_heads][block_size][head_dim], dtype
+ *   src_k, src_v     [num_src_blocks][num_kv_heads][block_size][head_dim], dtype
+ *   block_pairs      int32 [num_pairs][2] = (src id, dst id)
+ * Every pointer must be device memory or pinned, device-mapped host memory
+ * (hipHostMalloc, or a torch tensor made with pin_memory=True); anything else
+ * (pageable memory) returns PA_ERR_SHAPE before any launch.  Pairs with an id
+ * outside its pool are skipped.  Destinations must be distinct and must not
+ * overlap a source block of the same call.
+ */
+pa_status_t pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                           const int32_t* block_pairs, int num_pairs, int num_kv_heads, int head_dim,
+                           int block_size, int num_src_blocks, int num_dst_blocks, pa_dtype_t dtype,
+                           void* stream);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* pa_last_error(void);
 

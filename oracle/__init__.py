@@ -24,6 +24,9 @@ What it computes, each part written as the plain definition from the pages:
   Paging the KV Cache Like an OS, "Step 5", the write kernel).
 * ``cache_ops.copy_blocks`` -- whole-block copies for copy-on-write (Paging
   the KV Cache Like an OS, "Step 4" and the copy kernel of "Step 5").
+* ``cache_ops.swap_blocks`` -- whole blocks between the device pool and a
+  host pool, out and back, for preemption by swapping (PagedAttention:
+  Virtual Memory for the KV Cache, "Scheduling and preemption").
 * ``block_manager.BlockManager`` -- free list, reference counts, on-demand
   allocation, fork and copy-on-write (Paging the KV Cache Like an OS, "Step 3"
   and "Step 4"; PagedAttention (tensortonic), "7. Sharing a Prefix Without
@@ -40,4 +43,4 @@ manager.  Every function here is pinned; none is "parity unpinned".
 from . import attention, block_manager, cache_ops  # noqa: F401
 from .attention import decode, prefill, storage_to_f64  # noqa: F401
 from .block_manager import BlockManager, NoFreeBlocks  # noqa: F401
-from .cache_ops import copy_blocks, write_kv  # noqa: F401
+from .cache_ops import copy_blocks, swap_blocks, write_kv  # noqa: F401

@@ -9,7 +9,12 @@
   "Step 5" (one kernel batches many small block copies).  The whole block is
   copied: every KV head, every slot.
 
-Both return new arrays and leave the inputs untouched.
+* ``swap_blocks`` -- PagedAttention: Virtual Memory for the KV Cache,
+  "Scheduling and preemption": an evicted sequence's blocks are copied to
+  CPU memory and brought back later.  Whole blocks again, from one pool to
+  another pool of the same block shape (the block ids may differ).
+
+All return new arrays and leave the inputs untouched.
 """
 
 from __future__ import annotations
@@ -37,4 +42,16 @@ def copy_blocks(k_pool, v_pool, pairs):
     for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2).tolist():
         k[dst] = k[src]
         v[dst] = v[src]
+    return k, v
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, pairs):
+    """dst[d] = src[s] for every (s, d) in pairs; ids outside a pool are skipped."""
+    k = np.array(dst_k, copy=True)
+    v = np.array(dst_v, copy=True)
+    ns, nd = len(src_k), len(dst_k)
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2).tolist():
+        if 0 <= src < ns and 0 <= dst < nd:
+            k[dst] = src_k[src]
+            v[dst] = src_v[src]
     return k, v

@@ -8,6 +8,7 @@ the library and fails with ImportError when it has not been built.
     prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale, max_query_len)
     write_kv(k_pool, v_pool, k_new, v_new, slot_mapping)
     copy_blocks(k_pool, v_pool, block_pairs)
+    swap_blocks(dst_k, dst_v, src_k, src_v, block_pairs)   # device <-> pinned host pool
     BlockManager(num_blocks, block_size=16, free_order=None)
 """
 
@@ -21,5 +22,6 @@ from .ops import (  # noqa: F401
     decode,
     decode_workspace_bytes,
     prefill,
+    swap_blocks,
     write_kv,
 )

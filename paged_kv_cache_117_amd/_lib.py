@@ -30,6 +30,7 @@ SIGNATURES = {
                           _f32, _i32, _vp]),
     "pa_write_kv": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_swap_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_last_error": (_c.c_char_p, []),
     "pa_abi_version": (_i32, []),
     "pa_bm_create": (_vp, [_i32, _i32, _pi32]),

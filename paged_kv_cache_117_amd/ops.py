@@ -178,6 +178,44 @@ def copy_blocks(k_pool, v_pool, block_pairs, stream=None):
     check_status(st, "pa_copy_blocks")
 
 
+def _pool_tensor(t, name, dtype=None):
+    """A pool on the GPU or in pinned host memory (the library checks which)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.is_cuda:
+        if t.device.index != torch.cuda.current_device():
+            raise ValueError(f"{name} is on {t.device}, current device is {torch.cuda.current_device()}")
+    elif not t.is_pinned():
+        raise ValueError(f"{name} lives in pageable host memory; allocate it with pin_memory=True")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must have 4 dims, got shape {tuple(t.shape)}")
+    return t
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, block_pairs, stream=None):
+    """Whole-block copies src[pair[0]] -> dst[pair[1]] between a device pool
+    and a pinned host pool (pa_swap_blocks): swap-out or swap-in."""
+    _pool_tensor(src_k, "src_k")
+    for n, t in (("src_v", src_v), ("dst_k", dst_k), ("dst_v", dst_v)):
+        _pool_tensor(t, n, src_k.dtype)
+    if src_k.shape != src_v.shape or dst_k.shape != dst_v.shape or src_k.shape[1:] != dst_k.shape[1:]:
+        raise ValueError("pools must share the block shape (K and V alike)")
+    if not isinstance(block_pairs, torch.Tensor) or block_pairs.dtype != torch.int32 or block_pairs.dim() != 2 \
+            or block_pairs.shape[1] != 2 or not block_pairs.is_contiguous():
+        raise ValueError("block_pairs must be a contiguous int32 [n][2] tensor")
+    if not block_pairs.is_cuda and not block_pairs.is_pinned():
+        raise ValueError("block_pairs must be on the GPU or in pinned host memory")
+    ns, Hkv, bs, D = src_k.shape
+    st = LIB.pa_swap_blocks(dst_k.data_ptr(), dst_v.data_ptr(), src_k.data_ptr(), src_v.data_ptr(),
+                            block_pairs.data_ptr(), block_pairs.shape[0], Hkv, D, bs, ns, dst_k.shape[0],
+                            _dtype_code(src_k), _stream_handle(stream))
+    check_status(st, "pa_swap_blocks")
+
+
 def abi_version() -> int:
     return int(LIB.pa_abi_version())
 

@@ -139,3 +139,23 @@ def test_prefill_host_validation(kw, status):
 def test_prefill_without_rows_is_a_no_op():
     assert call_prefill(N=0, maxq=0, out=NULL, q=NULL, qs=NULL) == 0
     assert call_prefill(B=0, out=NULL, q=NULL) == 0
+
+
+def test_swap_host_validation():
+    """Checks that come before any pointer query or launch."""
+    sw = L.pa_swap_blocks
+    assert sw(16, 16, 16, 16, 16, 1, 2, 64, 16, 4, 4, 7, NULL) == 3   # dtype
+    assert sw(16, 16, 16, 16, 16, 1, 2, 64, 8, 4, 4, 2, NULL) == 3    # block size
+    assert sw(16, 16, 16, 16, 16, 1, 2, 96, 16, 4, 4, 2, NULL) == 3   # head dim
+    assert sw(16, 16, 16, 16, 16, -1, 2, 64, 16, 4, 4, 2, NULL) == 2  # negative count
+    assert sw(16, 16, NULL, 16, 16, 1, 2, 64, 16, 4, 4, 2, NULL) == 1
+    assert sw(16, 16, 8, 16, 16, 1, 2, 64, 16, 4, 4, 2, NULL) == 2    # misaligned
+    assert sw(NULL, NULL, NULL, NULL, NULL, 0, 2, 64, 16, 4, 4, 2, NULL) == 0
+
+
+def test_swap_binding_refuses_pageable_host_pools():
+    import torch
+
+    pool = torch.zeros(4, 2, 16, 64)
+    with pytest.raises(ValueError):
+        pa.swap_blocks(pool, pool.clone(), pool.clone(), pool.clone(), torch.zeros(1, 2, dtype=torch.int32))

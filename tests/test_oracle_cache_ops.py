@@ -69,3 +69,43 @@ def test_copy_blocks_whole_block_all_heads_bitwise():
     untouched = [b for b in range(10) if b not in (7, 8, 9)]
     assert np.array_equal(k2[untouched], k[untouched])
     assert np.array_equal(v2[untouched], v[untouched])
+
+
+def test_swap_matches_fancy_indexing_and_skips_bad_ids():
+    rng = np.random.default_rng(4)
+    src_k = rng.standard_normal((10, 2, 16, 8))
+    src_v = rng.standard_normal((10, 2, 16, 8))
+    dst_k = np.zeros((6, 2, 16, 8))
+    dst_v = np.zeros((6, 2, 16, 8))
+    pairs = np.array([[3, 0], [9, 5], [0, 2], [12, 1], [4, -1]])  # last two skipped
+    k, v = oracle.swap_blocks(dst_k, dst_v, src_k, src_v, pairs)
+    want_k = dst_k.copy()
+    want_v = dst_v.copy()
+    want_k[[0, 5, 2]] = src_k[[3, 9, 0]]
+    want_v[[0, 5, 2]] = src_v[[3, 9, 0]]
+    assert np.array_equal(k, want_k) and np.array_equal(v, want_v)
+    assert np.all(dst_k == 0)  # inputs untouched
+
+
+def test_swap_out_and_back_to_other_blocks_keeps_attention():
+    """Preemption by swapping (PagedAttention: Virtual Memory for the KV Cache,
+    "Scheduling and preemption"): a sequence's blocks go to a host pool and
+    come back into different device blocks; with its table repointed, its
+    attention output is unchanged, bit for bit."""
+    rng = np.random.default_rng(5)
+    nb, hkv, d, L = 12, 2, 16, 45
+    k = rng.standard_normal((nb, hkv, 16, d))
+    v = rng.standard_normal((nb, hkv, 16, d))
+    table = np.array([[7, 2, 9]], np.int32)
+    q = rng.standard_normal((1, 4, d))
+    before = oracle.decode(q, k, v, table, [L], 0.25, "fp32")
+    host_k = np.full((5, hkv, 16, d), np.nan)
+    host_v = np.full_like(host_k, np.nan)
+    out_pairs = [(7, 4), (2, 0), (9, 3)]
+    host_k, host_v = oracle.swap_blocks(host_k, host_v, k, v, out_pairs)
+    k[[7, 2, 9]] = np.nan  # the device blocks are reused meanwhile
+    v[[7, 2, 9]] = np.nan
+    in_pairs = [(4, 1), (0, 10), (3, 5)]
+    k, v = oracle.swap_blocks(k, v, host_k, host_v, in_pairs)
+    after = oracle.decode(q, k, v, np.array([[1, 10, 5]], np.int32), [L], 0.25, "fp32")
+    assert np.array_equal(before, after)
