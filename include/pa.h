@@ -292,6 +292,74 @@ int pa_bm_num_free(const pa_bm_t* bm);
 /* Reference count of a block (-1: out of range). */
 int pa_bm_refcount(const pa_bm_t* bm, int32_t block);
 
+/*
+ * Swapping (PagedAttention: Virtual Memory for the KV Cache, "Scheduling and
+ * preemption": a group -- e.g. the beams of one request -- is evicted whole,
+ * its blocks copied to CPU memory and brought back later).  The host pool
+ * has its own FIFO free list of host block ids 0..num_host_blocks-1 and its
+ * own counts.
+ *   - swap_out(group): every distinct block of the group's tables goes to a
+ *     host block popped from the host free list, in order of first
+ *     appearance (sequence order, then table order); pairs_out receives
+ *     (device block, host block) for pa_swap_blocks; the device blocks return
+ *     to the back of the free list; tables now hold host ids.  Refused
+ *     (nothing changes) if a block is shared with a sequence outside the
+ *     group (PA_ERR_SHAPE), copy-on-write pairs are pending (PA_ERR_SHAPE:
+ *     take and run them first), or the host pool is short (PA_ERR_NO_BLOCKS).
+ *   - swap_in(group): the reverse, into device blocks popped from the free
+ *     list; pairs_out receives (host block, device block).
+ *   - A swapped-out sequence cannot be appended to, forked or exported with
+ *     pa_bm_tables; pa_bm_free_seq releases its host blocks.
+ * pairs_out must hold cap >= the number of distinct blocks (at most the sum
+ * of the group's table lengths) pairs of int32.
+ */
+pa_status_t pa_bm_set_host_blocks(pa_bm_t* bm, int num_host_blocks);
+pa_status_t pa_bm_swap_out(pa_bm_t* bm, const int64_t* seq_ids, int n, int32_t* pairs_out, int cap,
+                           int* num_pairs_out);
+pa_status_t pa_bm_swap_in(pa_bm_t* bm, const int64_t* seq_ids, int n, int32_t* pairs_out, int cap,
+                          int* num_pairs_out);
+/* 1 swapped out, 0 on the device, -1 unknown id. */
+int pa_bm_is_swapped(const pa_bm_t* bm, int64_t seq_id);
+int pa_bm_num_host_free(const pa_bm_t* bm);
+/* Count of a host block (-1: out of range). */
+int pa_bm_host_refcount(const pa_bm_t* bm, int32_t host_block);
+
+/*
+ * Prefix cache (vLLM's PagedAttention: How Memory Management Supports Large
+ * Model Inference, "2.4" and "7"; PagedAttention (tensortonic), "8. Reusing
+ * Work Across Separate Requests").  A manager made by pa_bm_create_cached
+ * keys every full block by a chained hash
+ *   h_j = SHA-256(h_{j-1} || tokens of block j as int32 little-endian || extra_key),
+ * h_{-1} = 32 zero bytes, and keeps a map from hash to block.
+ *   - pa_bm_add_seq_cached starts a sequence from its prompt: it walks the
+ *     prompt's full blocks and takes each matching cached block (count + 1)
+ *     until the first miss.  *num_cached_out = the tokens whose K/V are
+ *     already in those blocks, except that a prompt found whole still
+ *     computes its last token (n_tokens - 1).  The caller then appends the
+ *     rest with pa_bm_append_tokens.
+ *   - pa_bm_append_tokens appends like pa_bm_append and enters each block
+ *     that fills into the map (the first block with a given hash keeps the
+ *     entry).  pa_bm_append / pa_bm_append_batch also work but leave the
+ *     sequence's later blocks unhashed (no token ids).
+ *   - Freed blocks keep their entries and go to the back of the free list,
+ *     a sequence's last blocks first; a block taken from the front loses its
+ *     entry.  The free list is thus the eviction order (least recently freed
+ *     first), and a block in use is never evicted.
+ * pa_bm_add_seq_cached / pa_bm_append_tokens return PA_ERR_UNSUPPORTED on a
+ * manager made by pa_bm_create.
+ */
+pa_bm_t* pa_bm_create_cached(int num_blocks, int block_size, const int32_t* initial_free_order);
+pa_status_t pa_bm_add_seq_cached(pa_bm_t* bm, int64_t seq_id, const int32_t* tokens, int n_tokens,
+                                 const void* extra_key, int extra_len, int* num_cached_out);
+pa_status_t pa_bm_append_tokens(pa_bm_t* bm, int64_t seq_id, const int32_t* tokens, int n_tokens,
+                                int64_t* slots_out);
+/* Entries in the hash map. */
+int pa_bm_num_cached_blocks(const pa_bm_t* bm);
+/* The chained hash of a sequence's j-th full block into out32 (0), or -1. */
+int pa_bm_block_hash(const pa_bm_t* bm, int64_t seq_id, int j, uint8_t* out32);
+/* The block the map holds for a 32-byte hash, or -1. */
+int pa_bm_cached_block(const pa_bm_t* bm, const uint8_t* hash32);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,12 +22,21 @@ Rules, each from the pages:
 * All or nothing: an append that cannot get every block it needs changes
   nothing (Paging the KV Cache Like an OS, "Step 2", fourth difference).
 
-Two choices of this implementation, where the pages are silent:
+* Swapping: a group of sequences (e.g. the beams of one request) is evicted
+  whole; each distinct block of the group moves to a host block and back
+  into a fresh device block later, blocks shared inside the group staying
+  shared (PagedAttention: Virtual Memory for the KV Cache, "Scheduling and
+  preemption").  A group whose blocks are shared outside it is refused.
+
+Choices of this implementation, where the pages are silent:
 
 * A freed sequence returns its blocks in table order to the back of the queue.
 * A block named by a copy that has not been handed out yet (``take_copies``)
   is held back from the free list until that hand-out, so no block is reused
   as a copy destination (or overwritten) before its pending copy runs.
+* Swap pairs are listed in order of first appearance (sequence order, then
+  table order); host blocks come from their own FIFO list; a swap-out waits
+  for pending copy-on-write copies to be taken.
 """
 
 from __future__ import annotations
@@ -51,6 +60,9 @@ class BlockManager:
         self.ntok: dict[int, int] = {}
         self.pending: list[tuple[int, int]] = []
         self.held: list[int] = []
+        self.swapped: set = set()
+        self.host_free: deque = deque()
+        self.host_ref: list[int] = []
 
     # -- queries -------------------------------------------------------------
     def num_free(self) -> int:
@@ -77,6 +89,8 @@ class BlockManager:
 
     def append(self, seq, n: int) -> list[int]:
         """Reserve slots for n more tokens; returns their slots (block*bs+off)."""
+        if seq in self.swapped:
+            raise ValueError(f"sequence {seq} is swapped out")
         table = self.tables[seq]
         T = self.ntok[seq]
         bs = self.block_size
@@ -86,7 +100,7 @@ class BlockManager:
             raise NoFreeBlocks(f"need {new_blocks + int(cow)}, have {len(self.free)}")
         if cow:
             src = table[-1]
-            dst = self.free.popleft()
+            dst = self._pop_free()
             self.pending.append((src, dst))
             self.ref[src] -= 1
             self.ref[dst] = 1
@@ -94,7 +108,7 @@ class BlockManager:
         slots = []
         for _ in range(n):
             if T % bs == 0:
-                b = self.free.popleft()
+                b = self._pop_free()
                 self.ref[b] = 1
                 table.append(b)
             slots.append(table[T // bs] * bs + T % bs)
@@ -107,6 +121,8 @@ class BlockManager:
         seqs = list(seqs)
         if len(set(seqs)) != len(seqs):
             raise ValueError("a sequence appears twice in the batch")
+        if any(q in self.swapped for q in seqs):
+            raise ValueError("a sequence of the batch is swapped out")
         need = 0
         bs = self.block_size
         ref = {}
@@ -127,6 +143,8 @@ class BlockManager:
     def fork(self, parent, child) -> None:
         if child in self.tables:
             raise KeyError(f"sequence {child} exists")
+        if parent in self.swapped:
+            raise ValueError(f"sequence {parent} is swapped out")
         table = self.tables[parent]
         for b in table:
             self.ref[b] += 1
@@ -136,24 +154,117 @@ class BlockManager:
     def _in_pending(self, b: int) -> bool:
         return any(b == s or b == d for s, d in self.pending)
 
+    def _pop_free(self) -> int:
+        return self.free.popleft()
+
+    def _release(self, b: int) -> None:
+        if self._in_pending(b):
+            self.held.append(b)
+        else:
+            self.free.append(b)
+
+    def _release_order(self, table):
+        return table
+
     def free_seq(self, seq) -> None:
         table = self.tables.pop(seq)
         del self.ntok[seq]
-        for b in table:
+        if seq in self.swapped:
+            self.swapped.discard(seq)
+            for h in table:
+                self.host_ref[h] -= 1
+                if self.host_ref[h] == 0:
+                    self.host_free.append(h)
+            return
+        for b in self._release_order(table):
             self.ref[b] -= 1
             if self.ref[b] == 0:
-                if self._in_pending(b):
-                    self.held.append(b)
-                else:
-                    self.free.append(b)
+                self._release(b)
 
     def take_copies(self) -> list[tuple[int, int]]:
         pairs = self.pending
         self.pending = []
         for b in self.held:
-            self.free.append(b)
+            if self.ref[b] == 0:
+                self.free.append(b)
         self.held = []
         return pairs
+
+    # -- swapping (PagedAttention: Virtual Memory for the KV Cache, "Scheduling
+    # and preemption": a group is evicted whole; its blocks go to CPU memory and
+    # come back later) ----------------------------------------------------------
+    def set_host_blocks(self, n: int) -> None:
+        assert not self.swapped
+        self.host_free = deque(range(n))
+        self.host_ref = [0] * n
+
+    def _group(self, seqs, want_swapped):
+        seqs = list(seqs)
+        if len(set(seqs)) != len(seqs):
+            raise ValueError("a sequence appears twice in the group")
+        uses: dict[int, int] = {}
+        order: list[int] = []
+        for q in seqs:
+            if q not in self.tables:
+                raise KeyError(q)
+            if (q in self.swapped) != want_swapped:
+                raise ValueError(f"sequence {q} is in the wrong place for this swap")
+            for b in self.tables[q]:
+                if b not in uses:
+                    order.append(b)
+                uses[b] = uses.get(b, 0) + 1
+        return seqs, order, uses
+
+    def swap_out(self, seqs) -> list[tuple[int, int]]:
+        seqs, order, uses = self._group(seqs, False)
+        if self.pending:
+            raise ValueError("copy-on-write pairs pending")
+        if any(self.ref[b] != uses[b] for b in order):
+            raise ValueError("a block is shared outside the group")
+        if len(self.host_free) < len(order):
+            raise NoFreeBlocks("host pool")
+        pairs, where = [], {}
+        for b in order:
+            h = self.host_free.popleft()
+            self.host_ref[h] = self.ref[b]
+            self.ref[b] = 0
+            self._on_swap_out(b)
+            self.free.append(b)
+            where[b] = h
+            pairs.append((b, h))
+        for q in seqs:
+            self.tables[q] = [where[b] for b in self.tables[q]]
+            self.swapped.add(q)
+        return pairs
+
+    def swap_in(self, seqs) -> list[tuple[int, int]]:
+        seqs, order, uses = self._group(seqs, True)
+        if any(self.host_ref[h] != uses[h] for h in order):
+            raise ValueError("a host block is shared outside the group")
+        if len(self.free) < len(order):
+            raise NoFreeBlocks("device pool")
+        pairs, where = [], {}
+        for h in order:
+            b = self._pop_free()
+            self.ref[b] = self.host_ref[h]
+            self.host_ref[h] = 0
+            self.host_free.append(h)
+            where[h] = b
+            pairs.append((h, b))
+        for q in seqs:
+            self.tables[q] = [where[h] for h in self.tables[q]]
+            self.swapped.discard(q)
+            self._on_swap_in(q)
+        return pairs
+
+    def _on_swap_out(self, b: int) -> None:
+        pass
+
+    def _on_swap_in(self, seq) -> None:
+        pass
+
+    def is_swapped(self, seq) -> bool:
+        return seq in self.swapped
 
     # -- helpers for tests ------------------------------------------------------
     def replay(self, ops) -> None:

@@ -47,6 +47,18 @@ SIGNATURES = {
     "pa_bm_take_copies": (_i32, [_vp, _pi32, _i32]),
     "pa_bm_num_free": (_i32, [_vp]),
     "pa_bm_refcount": (_i32, [_vp, _c.c_int32]),
+    "pa_bm_set_host_blocks": (_i32, [_vp, _i32]),
+    "pa_bm_swap_out": (_i32, [_vp, _pi64, _i32, _pi32, _i32, _c.POINTER(_c.c_int)]),
+    "pa_bm_swap_in": (_i32, [_vp, _pi64, _i32, _pi32, _i32, _c.POINTER(_c.c_int)]),
+    "pa_bm_is_swapped": (_i32, [_vp, _i64]),
+    "pa_bm_num_host_free": (_i32, [_vp]),
+    "pa_bm_host_refcount": (_i32, [_vp, _c.c_int32]),
+    "pa_bm_create_cached": (_vp, [_i32, _i32, _pi32]),
+    "pa_bm_add_seq_cached": (_i32, [_vp, _i64, _pi32, _i32, _c.c_char_p, _i32, _c.POINTER(_c.c_int)]),
+    "pa_bm_append_tokens": (_i32, [_vp, _i64, _pi32, _i32, _pi64]),
+    "pa_bm_num_cached_blocks": (_i32, [_vp]),
+    "pa_bm_block_hash": (_i32, [_vp, _i64, _i32, _c.c_char_p]),
+    "pa_bm_cached_block": (_i32, [_vp, _c.c_char_p]),
 }
 
 

@@ -14,18 +14,21 @@ _I64P = ctypes.POINTER(ctypes.c_int64)
 
 
 class BlockManager:
-    """Free list + reference counts + copy-on-write, implemented in C++ (libpa)."""
+    """Free list + reference counts + copy-on-write, swapping to a host pool
+    and (``prefix_cache=True``) a chained-hash prefix cache, in C++ (libpa)."""
 
-    def __init__(self, num_blocks: int, block_size: int = 16, free_order=None):
+    def __init__(self, num_blocks: int, block_size: int = 16, free_order=None, prefix_cache: bool = False):
         order = None
         if free_order is not None:
             self._order = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
             if self._order.shape != (num_blocks,):
                 raise ValueError("free_order must list every block once")
             order = self._order.ctypes.data_as(_I32P)
-        h = LIB.pa_bm_create(int(num_blocks), int(block_size), order)
+        create = LIB.pa_bm_create_cached if prefix_cache else LIB.pa_bm_create
+        h = create(int(num_blocks), int(block_size), order)
         if not h:
             raise PaError("pa_bm_create: " + LIB.pa_last_error().decode(), 2)
+        self.prefix_cache = bool(prefix_cache)
         self._h = ctypes.c_void_p(h)
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
@@ -99,6 +102,67 @@ class BlockManager:
 
     def refcount(self, block: int) -> int:
         return int(LIB.pa_bm_refcount(self._h, int(block)))
+
+    # swapping
+    def set_host_blocks(self, n: int) -> None:
+        check_status(LIB.pa_bm_set_host_blocks(self._h, int(n)), "pa_bm_set_host_blocks")
+
+    def _swap(self, fn, name, seqs) -> np.ndarray:
+        ids = np.ascontiguousarray(np.asarray(list(seqs), dtype=np.int64))
+        cap = sum(max(0, LIB.pa_bm_table(self._h, int(q), None, 0)) for q in ids)
+        out = np.empty((max(cap, 1), 2), dtype=np.int32)
+        n = ctypes.c_int(0)
+        check_status(fn(self._h, ids.ctypes.data_as(_I64P), len(ids), out.ctypes.data_as(_I32P), cap,
+                        ctypes.byref(n)), name)
+        return out[: n.value]
+
+    def swap_out(self, seqs) -> np.ndarray:
+        """(device block, host block) pairs; the group's tables now name host blocks."""
+        return self._swap(LIB.pa_bm_swap_out, "pa_bm_swap_out", seqs)
+
+    def swap_in(self, seqs) -> np.ndarray:
+        """(host block, device block) pairs; the group is back on the device."""
+        return self._swap(LIB.pa_bm_swap_in, "pa_bm_swap_in", seqs)
+
+    def is_swapped(self, seq: int) -> bool:
+        r = LIB.pa_bm_is_swapped(self._h, int(seq))
+        if r < 0:
+            raise KeyError(seq)
+        return bool(r)
+
+    def num_host_free(self) -> int:
+        return int(LIB.pa_bm_num_host_free(self._h))
+
+    def host_refcount(self, block: int) -> int:
+        return int(LIB.pa_bm_host_refcount(self._h, int(block)))
+
+    # prefix cache
+    def add_seq_cached(self, seq: int, tokens, extra: bytes = b"") -> int:
+        """Start ``seq`` from its prompt; returns how many tokens the cache already holds."""
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        n = ctypes.c_int(0)
+        check_status(LIB.pa_bm_add_seq_cached(self._h, int(seq), t.ctypes.data_as(_I32P), len(t), bytes(extra),
+                                              len(extra), ctypes.byref(n)), "pa_bm_add_seq_cached")
+        return n.value
+
+    def append_tokens(self, seq: int, tokens) -> list:
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        slots = np.empty(max(len(t), 1), dtype=np.int64)
+        check_status(LIB.pa_bm_append_tokens(self._h, int(seq), t.ctypes.data_as(_I32P), len(t),
+                                             slots.ctypes.data_as(_I64P)), "pa_bm_append_tokens")
+        return slots[: len(t)].tolist()
+
+    def num_cached_blocks(self) -> int:
+        return int(LIB.pa_bm_num_cached_blocks(self._h))
+
+    def block_hash(self, seq: int, j: int) -> bytes:
+        buf = ctypes.create_string_buffer(32)
+        if LIB.pa_bm_block_hash(self._h, int(seq), int(j), buf) != 0:
+            raise KeyError((seq, j))
+        return buf.raw
+
+    def cached_block(self, h: bytes) -> int:
+        return int(LIB.pa_bm_cached_block(self._h, bytes(h)))
 
     def replay(self, ops) -> None:
         for op in ops:

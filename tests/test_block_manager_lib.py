@@ -109,3 +109,100 @@ def test_error_codes():
         bm.append(1, 33)
     with pytest.raises(pa.PaError):
         pa.BlockManager(3, 16, [0, 0, 1])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_cache_and_swap_agree_with_oracle_on_random_operations(seed):
+    """Prefix-cached manager with a host pool: prompts drawn from a few shared
+    stems, token appends, forks, frees, swaps out and in, copies taken -- the
+    library and the oracle give identical results and state throughout."""
+    from oracle.prefix_cache import CachingBlockManager
+
+    rng = np.random.default_rng(100 + seed)
+    n, bs, nh = 48, int(rng.choice([4, 16])), 24
+    order = rng.permutation(n).tolist()
+    a, b = CachingBlockManager(n, bs, order), pa.BlockManager(n, bs, order, prefix_cache=True)
+    a.set_host_blocks(nh), b.set_host_blocks(nh)
+    stems = [list(rng.integers(0, 50, size=5 * bs)) for _ in range(3)]
+    live, swapped, nxt = [], [], 0
+
+    def both(fa, fb):
+        ra = rb = None
+        try:
+            ra = fa()
+        except (oracle.NoFreeBlocks, ValueError) as e:
+            ra = type(e).__name__ == "NoFreeBlocks" and "dry" or "refused"
+        try:
+            rb = fb()
+        except pa.NoFreeBlocks:
+            rb = "dry"
+        except pa.PaError:
+            rb = "refused"
+        if isinstance(ra, list):
+            ra = [tuple(x) if isinstance(x, (list, tuple)) else x for x in ra]
+        if isinstance(rb, np.ndarray):
+            rb = [tuple(x) for x in rb.tolist()]
+        assert ra == rb, (ra, rb)
+        return ra
+
+    for _ in range(1200):
+        op = int(rng.integers(0, 10))
+        if op == 0 or not live:
+            stem = stems[int(rng.integers(len(stems)))]
+            cut = int(rng.integers(0, len(stem) + 1))
+            prompt = stem[:cut] + list(rng.integers(0, 50, size=int(rng.integers(0, 2 * bs))))
+            extra = b"" if rng.random() < 0.8 else b"x"
+            ra = a.add_seq_cached(nxt, prompt, extra)
+            rb = b.add_seq_cached(nxt, prompt, extra)
+            assert ra == rb
+            both(lambda: a.append_tokens(nxt, prompt[ra:]), lambda: b.append_tokens(nxt, prompt[rb:]))
+            if nxt in a.tables:
+                live.append(nxt)
+            nxt += 1
+            continue
+        s = live[int(rng.integers(len(live)))] if live else None
+        if op in (1, 2) and s is not None:
+            toks = list(rng.integers(0, 50, size=int(rng.integers(0, 2 * bs))))
+            both(lambda: a.append_tokens(s, toks), lambda: b.append_tokens(s, toks))
+        elif op == 3 and s is not None:
+            a.fork(s, nxt), b.fork(s, nxt)
+            live.append(nxt)
+            nxt += 1
+        elif op == 4 and s is not None:
+            live.remove(s)
+            a.free_seq(s), b.free_seq(s)
+        elif op == 5:
+            ca, cb = a.take_copies(), b.take_copies()
+            assert [tuple(x) for x in ca] == [tuple(x) for x in cb]
+        elif op == 6 and live:
+            grp = list(rng.choice(live, size=min(len(live), int(rng.integers(1, 4))), replace=False))
+            r = both(lambda: a.swap_out(grp), lambda: b.swap_out(grp))
+            if isinstance(r, list):
+                for q in grp:
+                    live.remove(q)
+                swapped.append(grp)
+        elif op == 7 and swapped:
+            grp = swapped[int(rng.integers(len(swapped)))]
+            r = both(lambda: a.swap_in(grp), lambda: b.swap_in(grp))
+            if isinstance(r, list):
+                swapped.remove(grp)
+                live.extend(grp)
+        elif op == 8 and s is not None:
+            k = int(rng.integers(0, 3 * bs))
+            both(lambda: a.append(s, k), lambda: b.append(s, k))
+        elif op == 9 and swapped:
+            grp = swapped.pop(int(rng.integers(len(swapped))))
+            for q in grp:
+                a.free_seq(q), b.free_seq(q)
+        # full state comparison
+        assert a.num_free() == b.num_free()
+        assert a.num_cached_blocks() == b.num_cached_blocks()
+        assert len(a.host_free) == b.num_host_free()
+        for q in live + [q for g in swapped for q in g]:
+            assert a.table(q) == b.table(q)
+            assert a.num_tokens(q) == b.num_tokens(q)
+            assert a.is_swapped(q) == b.is_swapped(q)
+            for j in range(len(a.hashes[q])):
+                assert a.block_hash(q, j) == b.block_hash(q, j)
+        assert [a.refcount(x) for x in range(n)] == [b.refcount(x) for x in range(n)]
+        assert [a.host_ref[x] for x in range(nh)] == [b.host_refcount(x) for x in range(nh)]
