@@ -70,13 +70,20 @@ SWAP_NAMES = {
 }
 
 
+# Host block manager with the prefix cache (no GPU work)
+HOST_NAMES = {
+    "h1": "prefix-cache churn: 32 prompts x 8 requests each, shared 1024-token prompt prefix + own tail "
+          "U[0,512], arriving one by one (add with lookup, append with hashing), then freed",
+}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c2",
-                    choices=sorted(WORKLOAD_NAMES) + sorted(PREFILL_NAMES) + sorted(SWAP_NAMES))
+                    choices=sorted(WORKLOAD_NAMES) + sorted(PREFILL_NAMES) + sorted(SWAP_NAMES) + sorted(HOST_NAMES))
     ap.add_argument("--partition-size", type=int, default=None,
                     help="positions per partition; 0 = automatic even split (default: the workload's, "
                          "512 for c5, automatic otherwise)")
@@ -534,6 +541,64 @@ def main_swap(args):
     print(json.dumps(res), flush=True)
 
 
+def host_churn_requests(seed=31, prompts=32, per=8, prefix=1024, bs=16):
+    rng = np.random.default_rng(seed)
+    reqs = []
+    for p in range(prompts):
+        stem = rng.integers(0, 32000, size=prefix).tolist()
+        for _ in range(per):
+            reqs.append(stem + rng.integers(0, 32000, size=int(rng.integers(0, 513))).tolist())
+    return reqs
+
+
+def run_churn(bm, reqs):
+    hits = 0
+    for i, r in enumerate(reqs):
+        n = bm.add_seq_cached(i, r)
+        bm.append_tokens(i, r[n:])
+        hits += n
+    for i in range(len(reqs)):
+        bm.free_seq(i)
+    return hits
+
+
+def main_host(args):
+    import paged_kv_cache_117_amd as pa
+
+    reqs = host_churn_requests()
+    toks = sum(len(r) for r in reqs)
+    nb = sum(-(-len(r) // 16) for r in reqs) + 16
+    times = []
+    for _ in range(max(1, args.steps)):
+        bm = pa.BlockManager(nb, 16, prefix_cache=True)
+        t = time.perf_counter()
+        hits = run_churn(bm, reqs)
+        times.append(time.perf_counter() - t)
+    dt = float(np.median(times))
+    full_blocks = sum(len(r) // 16 for r in reqs)
+    res = {
+        "metric": "host prefix-cache requests/s (lookup + append with chained SHA-256 block hashes)",
+        "value": round(len(reqs) / dt, 1), "unit": "requests/s", "n_gpus": 0, "steps": len(times), "warmup": 0,
+        "ms_per_step": round(dt * 1e3, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int32 tokens", "data": "synthetic",
+        "config": {"workload": HOST_NAMES[args.config], "key": args.config, "requests": len(reqs), "tokens": toks},
+        "cached_token_fraction": round(hits / toks, 4), "blocks_hashed_per_s": round(full_blocks / dt, 1),
+        "roofline": None, "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle.prefix_cache import CachingBlockManager  # test infrastructure: this leg only
+
+        sub = reqs[:64]
+        t = time.perf_counter()
+        run_churn(CachingBlockManager(nb, 16), sub)
+        odt = time.perf_counter() - t
+        res["cpu_baseline"] = {"value": round(len(sub) / odt, 1), "unit": "requests/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"oracle prefix cache (Python, hashlib) on the first {len(sub)} requests, "
+                                         f"{odt:.3f} s; host CPU: {cpu_info()}"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -545,6 +610,9 @@ def main():
               "attention, so run one process per GPU.", file=sys.stderr)
         sys.exit(2)
 
+    if args.config in HOST_NAMES:
+        main_host(args)
+        return
     if args.config in SWAP_NAMES:
         import torch
 
