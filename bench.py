@@ -91,6 +91,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--placement", choices=["shuffled", "sequential"], default="shuffled")
+    ap.add_argument("--block-size", type=int, default=16,
+                    help="slots per KV block for the decode workloads (16, 32, 64, 128)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -329,7 +331,7 @@ def main_prefill(args):
     from paged_kv_cache_117_amd import metrics
     from workloads import make_prefill_workload
 
-    w = make_prefill_workload(args.config)
+    w = make_prefill_workload(args.config, block_size=args.block_size)
     eb = metrics.ELEM_BYTES[w.dtype]
     tdt = {"fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
     order = w.perm if args.placement == "shuffled" else np.arange(w.num_blocks, dtype=np.int32)
@@ -636,7 +638,7 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
-    w = make_workload(args.config)
+    w = make_workload(args.config, block_size=args.block_size)
     if args.partition_size is None:
         args.partition_size = WORKLOAD_PARTITION.get(args.config, 0)
     eb = metrics.ELEM_BYTES[w.dtype]

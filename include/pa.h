@@ -3,9 +3,10 @@
  *
  * The KV cache is a pool of fixed-size blocks; each sequence reaches its
  * blocks through a block table that maps logical block j (positions
- * 16j..16j+15) to a physical block id (PagedAttention and vLLM: Paging the
- * KV Cache Like an OS, "Step 3: blocks and block tables"; PagedAttention
- * (tensortonic), "4. Finding Tokens with a Block Table").
+ * bs*j..bs*j+bs-1, bs = block_size, 16 by default) to a physical block id
+ * (PagedAttention and vLLM: Paging the KV Cache Like an OS, "Step 3: blocks
+ * and block tables"; PagedAttention (tensortonic), "4. Finding Tokens with a
+ * Block Table").
  *
  * Layouts (all row-major, C order):
  *   K pool, V pool : [num_blocks][num_kv_heads][block_size][head_dim]  (two tensors)
@@ -51,7 +52,7 @@ typedef enum {
   PA_OK = 0,
   PA_ERR_NULL = 1,        /* a required pointer is NULL */
   PA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range, misaligned pointer */
-  PA_ERR_UNSUPPORTED = 3, /* block_size != 16, head_dim not 64/128, bad dtype */
+  PA_ERR_UNSUPPORTED = 3, /* block_size, head_dim (64/128) or dtype the call does not take */
   PA_ERR_WORKSPACE = 4,   /* workspace missing or too small */
   PA_ERR_LAUNCH = 5,      /* the HIP runtime refused the launch */
   PA_ERR_NO_BLOCKS = 6,   /* block manager: the free list cannot cover the request */
@@ -66,8 +67,8 @@ typedef enum {
  * (KV head j = h / g, g = num_q_heads / num_kv_heads):
  *   x_t   = scale * q[s][h] . K_j(t)           for positions t = 0..L-1,
  *   out   = sum_t softmax(x)_t * V_j(t),
- * where position t lives in physical block block_tables[s][t / 16] at slot
- * t % 16.  This is ordinary attention over the sequence's valid positions,
+ * where position t lives in physical block block_tables[s][t / bs] at slot
+ * t % bs (bs = block_size).  This is ordinary attention over the sequence's valid positions,
  * the final block truncated at L; only addresses differ (PagedAttention and
  * vLLM: Paging the KV Cache Like an OS, "Step 5: attention over scattered
  * blocks"; PagedAttention (tensortonic), "5. Reading the Cache During
@@ -99,13 +100,15 @@ typedef enum {
  *                    must be <= max_blocks_per_seq * block_size
  *   scale            softmax scale (typically 1/sqrt(head_dim)), finite
  *   partition_size   positions per partition, a positive multiple of
- *                    block_size; 0 = automatic (see above)
+ *                    16; 0 = automatic (see above)
  *   workspace        device scratch of at least pa_decode_workspace_bytes(...)
  *                    bytes (may be NULL when that is 0); 256-byte aligned;
  *                    contents need no initialisation and are clobbered
  *   stream           hipStream_t or NULL
- * Supported: block_size 16, head_dim 64 or 128, any num_q_heads that is a
- * multiple of num_kv_heads.  `out` must not alias any input or the workspace.
+ * Supported: block_size 16, 32, 64 or 128 (the kernels walk 16-slot tiles,
+ * 2^k of them per block; 8 returns PA_ERR_UNSUPPORTED), head_dim 64 or 128,
+ * any num_q_heads that is a multiple of num_kv_heads.  `out` must not alias
+ * any input or the workspace.
  */
 pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
                       const int32_t* block_tables, const int32_t* context_lens,
@@ -138,7 +141,7 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads
  * head h (KV head j = h / g):
  *   x_t = scale * q[row][h] . K_j(t)            for t = 0..p   (causal),
  *   out[row][h] = sum_t softmax(x)_t * V_j(t),
- * with position t read from block block_tables[s][t / 16], slot t % 16.
+ * with position t read from block block_tables[s][t / bs], slot t % bs.
  * Where a position lives changes neither its place in the sequence nor the
  * causal mask (PagedAttention (tensortonic), "5. Reading the Cache During
  * Attention").  With T = 1 this is pa_decode's attention.
@@ -156,10 +159,11 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads
  *   max_query_len    host, >= every T (sizes the launch), <= num_tokens
  *   scale            softmax scale (typically 1/sqrt(head_dim)), finite
  *   stream           hipStream_t or NULL
- * Supported: fp16 and bf16 (fp32 returns PA_ERR_UNSUPPORTED), block_size 16,
- * head_dim 64 or 128, any num_q_heads that is a multiple of num_kv_heads.
+ * Supported: fp16 and bf16 (fp32 returns PA_ERR_UNSUPPORTED), block_size 8,
+ * 16, 32, 64 or 128, head_dim 64 or 128, any num_q_heads that is a multiple
+ * of num_kv_heads.
  * Device-side contract violations are never dereferenced: a sequence with
- * T > L, L > max_blocks_per_seq * 16, T > max_query_len or a row range
+ * T > L, L > max_blocks_per_seq * block_size, T > max_query_len or a row range
  * outside [0, num_tokens) gets NaN rows (those inside [0, num_tokens)); a
  * block id outside [0, num_blocks) makes the rows that would read it NaN.
  * `out` must not alias any input.  Needs no workspace.
@@ -174,11 +178,11 @@ pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, const void*
 /*
  * pa_write_kv -- store new tokens' K and V rows in their slots
  * (reshape-and-cache).  For each token i with slot = slot_mapping[i] >= 0:
- *   k_pool[slot / 16][h][slot % 16][:] = k_new[i][h][:]   for every KV head h,
+ *   k_pool[slot / bs][h][slot % bs][:] = k_new[i][h][:]   for every KV head h,
  * and the same for V.  One launch covers every token of the step
  * (PagedAttention (tensortonic), "5. Reading the Cache During Attention";
  * PagedAttention and vLLM: Paging the KV Cache Like an OS, "Step 5", the
- * fused write kernel).  Negative slots are skipped; slots >= num_blocks * 16
+ * fused write kernel).  Negative slots are skipped; slots >= num_blocks * block_size
  * are skipped too (caller error, never written).  Non-negative slots must be
  * distinct.  Bytes outside the addressed rows are never touched.
  *
@@ -186,6 +190,8 @@ pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, const void*
  *   k_new, v_new     device, [num_tokens][num_kv_heads][head_dim], dtype
  *   slot_mapping     device, int64 [num_tokens]
  */
+/* (pa_write_kv, pa_copy_blocks and pa_swap_blocks take any block_size that is a
+ * power of two up to 128.) */
 pa_status_t pa_write_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                         const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
                         int head_dim, int block_size, int num_blocks, pa_dtype_t dtype,

@@ -103,6 +103,8 @@ const char* device_view(const void* p, const char* what, pa_status_t* st) {
   return nullptr;
 }
 
+bool pow2_block(int bs) { return bs >= 1 && bs <= 128 && (bs & (bs - 1)) == 0; }
+
 int elem_bytes(pa_dtype_t dt) { return dt == PA_FP32 ? 4 : (dt == PA_FP16 || dt == PA_BF16) ? 2 : 0; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -117,7 +119,7 @@ extern "C" pa_status_t pa_write_kv(void* k_pool, void* v_pool, const void* k_new
   clear_error();
   const int eb = elem_bytes(dtype);
   if (eb == 0) return fail(PA_ERR_UNSUPPORTED, "pa_write_kv: unknown dtype %d", (int)dtype);
-  if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "pa_write_kv: block_size %d (only 16)", block_size);
+  if (!pow2_block(block_size)) return fail(PA_ERR_UNSUPPORTED, "pa_write_kv: block_size %d (a power of two up to 128)", block_size);
   if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_write_kv: head_dim %d", head_dim);
   if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0)
     return fail(PA_ERR_SHAPE, "pa_write_kv: num_tokens=%d num_kv_heads=%d num_blocks=%d", num_tokens, num_kv_heads,
@@ -142,7 +144,7 @@ extern "C" pa_status_t pa_copy_blocks(void* k_pool, void* v_pool, const int32_t*
   clear_error();
   const int eb = elem_bytes(dtype);
   if (eb == 0) return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: unknown dtype %d", (int)dtype);
-  if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: block_size %d (only 16)", block_size);
+  if (!pow2_block(block_size)) return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: block_size %d (a power of two up to 128)", block_size);
   if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: head_dim %d", head_dim);
   if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks < 0)
     return fail(PA_ERR_SHAPE, "pa_copy_blocks: num_pairs=%d num_kv_heads=%d num_blocks=%d", num_pairs, num_kv_heads,
@@ -169,7 +171,7 @@ extern "C" pa_status_t pa_swap_blocks(void* dst_k, void* dst_v, const void* src_
   clear_error();
   const int eb = elem_bytes(dtype);
   if (eb == 0) return fail(PA_ERR_UNSUPPORTED, "pa_swap_blocks: unknown dtype %d", (int)dtype);
-  if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "pa_swap_blocks: block_size %d (only 16)", block_size);
+  if (!pow2_block(block_size)) return fail(PA_ERR_UNSUPPORTED, "pa_swap_blocks: block_size %d (a power of two up to 128)", block_size);
   if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_swap_blocks: head_dim %d", head_dim);
   if (num_pairs < 0 || num_kv_heads <= 0 || num_src_blocks < 0 || num_dst_blocks < 0)
     return fail(PA_ERR_SHAPE, "pa_swap_blocks: num_pairs=%d num_kv_heads=%d num_src_blocks=%d num_dst_blocks=%d",

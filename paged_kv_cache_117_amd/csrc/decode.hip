@@ -2,7 +2,8 @@
 //
 // What is computed: for each sequence s (length L) and query head h, ordinary
 // softmax attention of q[s][h] over the L valid K/V rows of KV head h/g,
-// where position t is found through the block table at block t/16, slot t%16
+// where position t is found through the block table at block t/bs, slot t%bs
+// (bs = 16 << lm; the kernels walk 16-slot tiles, 2^lm of them per block)
 // (PagedAttention and vLLM: Paging the KV Cache Like an OS, "Step 5";
 // PagedAttention (tensortonic), "5. Reading the Cache During Attention").
 //
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(64) void decode_part_valu(void* __restrict__ out, c
                                                       float* __restrict__ ws_o, float* __restrict__ ws_m,
                                                       float* __restrict__ ws_l, int B, int Hq, int Hkv, int g,
                                                       int nsub, int num_blocks, int maxb, int max_ctx, float qscale,
-                                                      int psize, int P) {
+                                                      int psize, int P, int lm) {
   constexpr int ES = Elem<DT>::kBytes;
   constexpr int ROWB = D * ES;
   constexpr int LPR = ROWB / 16;
@@ -110,18 +111,20 @@ __global__ __launch_bounds__(64) void decode_part_valu(void* __restrict__ out, c
   const int b0 = p * (psize / 16);
   const int b1 = min(b0 + psize / 16, nblk);
   const int32_t* btrow = bt + (size_t)s * maxb;
-  const size_t blk_stride = (size_t)Hkv * 16 * ROWB;
-  const size_t lane_off = (size_t)kvh * 16 * ROWB + r * ROWB + c * 16;
+  const size_t lane_off = (size_t)r * ROWB + c * 16;
   bool bad = false;
 
+  // `blk` counts 16-slot tiles; a block of 16 << lm slots holds 1 << lm of
+  // them, so tile blk is slots [16 (blk mod 2^lm), +16) of table entry blk >> lm.
   for (int blk = b0; blk < b1; ++blk) {
-    const int phys = btrow[blk];
+    const int phys = btrow[blk >> lm];
     if (phys < 0 || phys >= num_blocks) {
       bad = true;
       break;
     }
-    const char* kb = kp + (size_t)phys * blk_stride + lane_off;
-    const char* vb = vp + (size_t)phys * blk_stride + lane_off;
+    const size_t row = ((((size_t)phys * Hkv + kvh) << lm) | (size_t)(blk & ((1 << lm) - 1)));
+    const char* kb = kp + row * (16 * ROWB) + lane_off;
+    const char* vb = vp + row * (16 * ROWB) + lane_off;
     uint4 kr[NI], vr[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) kr[i] = *reinterpret_cast<const uint4*>(kb + i * RPI * ROWB);
@@ -269,7 +272,7 @@ void launch_valu(const DecodeArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)a.P * a.Hkv * a.nsub * a.B;
   hipLaunchKernelGGL((decode_part_valu<DT, D, GMAX>), dim3(grid), dim3(64), 0, st, a.out, a.q, a.kp, a.vp, a.bt,
                      a.cl, a.ws_o, a.ws_m, a.ws_l, a.B, a.Hq, a.Hkv, a.g, a.nsub, a.num_blocks, a.maxb, a.max_ctx,
-                     a.qscale, a.psize, a.P);
+                     a.qscale, a.psize, a.P, a.lm);
 }
 
 template <int DT, int D>

@@ -75,7 +75,11 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
   clear_error();
   if (dtype != PA_FP32 && dtype != PA_FP16 && dtype != PA_BF16)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: unknown dtype %d", (int)dtype);
-  if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d (only 16)", block_size);
+  // The kernels walk 16-slot tiles (one MFMA operand); a block holds 2^lm of them.
+  int lm = -1;
+  for (int k = 0; k <= 3; ++k)
+    if (block_size == 16 << k) lm = k;
+  if (lm < 0) return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d (16, 32, 64 or 128)", block_size);
   if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d (64 or 128)", head_dim);
   if (num_seqs < 0 || num_seqs > 65535)
     return fail(PA_ERR_SHAPE, "pa_decode: num_seqs %d outside [0, 65535]", num_seqs);
@@ -85,12 +89,14 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
   if (num_blocks <= 0 || max_blocks_per_seq <= 0)
     return fail(PA_ERR_SHAPE, "pa_decode: num_blocks %d, max_blocks_per_seq %d", num_blocks, max_blocks_per_seq);
   if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
-    return fail(PA_ERR_SHAPE, "pa_decode: max_context_len %d outside [0, max_blocks_per_seq*16 = %lld]",
+    return fail(PA_ERR_SHAPE, "pa_decode: max_context_len %d outside [0, max_blocks_per_seq*block_size = %lld]",
                 max_context_len, (long long)max_blocks_per_seq * block_size);
   const int psize = partition_size == 0 ? kDefaultPartition : partition_size;
-  if (psize <= 0 || psize % block_size != 0)
+  if (psize <= 0 || psize % 16 != 0)
     return fail(PA_ERR_SHAPE, "pa_decode: partition_size %d must be a positive multiple of 16", partition_size);
   if (!isfinite(scale)) return fail(PA_ERR_SHAPE, "pa_decode: scale is not finite");
+  if (((int64_t)num_blocks * num_kv_heads << lm) > 0x7fffffffLL)
+    return fail(PA_ERR_SHAPE, "pa_decode: %d blocks of %d KV heads is too large", num_blocks, num_kv_heads);
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
     return fail(PA_ERR_NULL, "pa_decode: NULL pointer");
@@ -102,11 +108,11 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
   // Balanced split: 16-bit KV, batches whose lengths fit its LDS table.
   // Units are single blocks unless a partition size is given.
   const bool half = dtype != PA_FP32 && !force_valu();
-  const int unit = partition_size == 0 ? 1 : psize / block_size;
-  // (its tile descriptors hold block * num_kv_heads + head in 28 bits)
+  const int unit = partition_size == 0 ? 1 : psize / 16;
+  // (its tile descriptors hold the tile row ((block * num_kv_heads + head) << lm) + tile in 28 bits)
   const bool use_stream = half && num_seqs <= kStreamMaxSeqs && !force_partition() &&
                           stream_units_bound(num_seqs, num_q_heads, num_kv_heads, max_context_len, unit) < (1 << 30) &&
-                          (int64_t)num_blocks * num_kv_heads < (1 << 28);
+                          ((int64_t)num_blocks * num_kv_heads << lm) < (1 << 28);
   // MFMA partition kernels: 16-bit KV, partitions of at most 4096 positions
   // (a wave holds at most 64 block ids).  Everything else: the VALU kernel.
   const bool mfma = half && (use_stream || psize <= 4096);
@@ -155,6 +161,7 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
   a.P = P;
   a.qscale = scale * 1.4426950408889634f;
   a.dtype = dtype;
+  a.lm = lm;
   a.stream = use_stream;
   if (use_stream) {
     // One workgroup of 4 independent wavefronts per CU (4 wavefronts with
@@ -170,7 +177,7 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
   } else {
     // Partitions of up to 64 blocks: one wavefront each, and the
     // workgroup's four partitions merged into one workspace entry.
-    a.wave_part = mfma && psize / block_size <= 64;
+    a.wave_part = mfma && psize / 16 <= 64;
     a.per_entry = a.wave_part ? 4 : 1;
     a.entries = (P + a.per_entry - 1) / a.per_entry;
     if ((int64_t)a.entries * num_kv_heads * a.nsub * num_seqs > 0x7fffffffLL)

@@ -30,6 +30,7 @@ struct DecodeArgs {
   int num_blocks, maxb, max_ctx, psize, P;
   float qscale;  // scale * log2(e)
   pa_dtype_t dtype;
+  int lm;        // log2(block_size / 16): the kernels walk 16-slot tiles, 2^lm per block
 };
 
 // Workspace: the partition partials, when some sequence spans more than one

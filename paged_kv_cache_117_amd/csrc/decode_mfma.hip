@@ -395,8 +395,6 @@ struct Body {
     const int col = lane & 15;
     const int x16 = (lane ^ 16) << 2;  // ds_bpermute addresses of the partner lanes
     const int x32 = (lane ^ 32) << 2;
-    const size_t blk_stride = (size_t)Hkv * 16 * ROWB;
-    const size_t head_off = (size_t)kvh * 16 * ROWB;
     const uint16_t* qsrc = &sh.q[col][grp * 8];
     float m_run = kNegInf;  // running max of head `col`, base 2
     float l_run = 0.f;      // running sum over this lane's tokens
@@ -409,7 +407,7 @@ struct Body {
       pipeline(
           cnt, kA, vA, kB, vB,
           [&](int k, uint4(&kr)[KS], VVec(&vr)[4]) {
-            const size_t off = (size_t)__builtin_amdgcn_readlane(myid, k) * blk_stride + head_off;
+            const size_t off = (size_t)(unsigned)__builtin_amdgcn_readlane(myid, k) * (16 * ROWB);
             T::load(kp + off, vp + off, grp, col, min(15, L - 1 - (first + k * step) * 16), kr, vr);
           },
           [&](int k, const uint4(&kr)[KS], const VVec(&vr)[4], bool valid) {
@@ -428,17 +426,22 @@ struct Body {
   }
 };
 
-// Lane k's physical id of logical block bidx(k) for k < cnt (0 elsewhere);
-// ids outside [0, num_blocks) become 0, never dereferenced, and set `bad`
-// (in every lane).
+// Lane k's tile row for logical 16-slot tile bidx(k), k < cnt (0 elsewhere):
+// the tile is slots [16 (t mod 2^lm), +16) of table entry t >> lm, i.e. row
+// ((id * Hkv + kvh) << lm) + t mod 2^lm of 16 * ROWB bytes.  Ids outside
+// [0, num_blocks) become 0, never dereferenced, and set `bad` (in every lane).
 template <typename F>
-__device__ __forceinline__ int load_ids(const int32_t* btrow, int cnt, int num_blocks, F bidx, bool& bad) {
+__device__ __forceinline__ int load_ids(const int32_t* btrow, int cnt, int num_blocks, F bidx, bool& bad, int Hkv,
+                                        int kvh, int lm) {
   const int lane = threadIdx.x & 63;
-  int id = 0;
-  if (lane < cnt) id = btrow[bidx(lane)];
+  int id = 0, t = 0;
+  if (lane < cnt) {
+    t = bidx(lane);
+    id = btrow[t >> lm];
+  }
   const bool ok = id >= 0 && id < num_blocks;
   bad = !__all(lane >= cnt || ok);
-  return ok ? id : 0;
+  return ok ? ((id * Hkv + kvh) << lm) | (t & ((1 << lm) - 1)) : 0;
 }
 
 // Where a workgroup of either kernel sits in the 1-D grid: KV head (and
@@ -483,7 +486,7 @@ __global__ __launch_bounds__(256) void decode_part_wave(void* __restrict__ out, 
                                                        float* __restrict__ ws_o, float* __restrict__ ws_m,
                                                        float* __restrict__ ws_l, int B, int Hq, int Hkv, int g,
                                                        int nsub, int num_blocks, int maxb, int max_ctx, float qscale,
-                                                       int psize, int E) {
+                                                       int psize, int E, int lm) {
   using Bd = Body<DT, D, GMAX>;
   static_assert(GMAX <= 16, "one MFMA column per query head");
   __shared__ typename Bd::Shared sh;
@@ -511,7 +514,8 @@ __global__ __launch_bounds__(256) void decode_part_wave(void* __restrict__ out, 
   const int b0 = max(p, 0) * pblk;
   const int cnt = p < 0 ? 0 : min(pblk, (L + 15) / 16 - b0);
   bool bad;
-  const int myid = load_ids(bt + (size_t)pl.s * maxb, cnt, num_blocks, [&](int k) { return b0 + k; }, bad);
+  const int myid =
+      load_ids(bt + (size_t)pl.s * maxb, cnt, num_blocks, [&](int k) { return b0 + k; }, bad, Hkv, pl.kvh, lm);
   Bd::run(sh, kp, vp, myid, bad, cnt, b0, 1, L, pl.kvh, Hkv, pl.nh, qscale, nent, pl.rank, pl.row0, E, out, ws_o,
           ws_m, ws_l);
 }
@@ -530,7 +534,7 @@ __global__ __launch_bounds__(256) void decode_part_mfma(void* __restrict__ out, 
                                                        float* __restrict__ ws_o, float* __restrict__ ws_m,
                                                        float* __restrict__ ws_l, int B, int Hq, int Hkv, int g,
                                                        int nsub, int num_blocks, int maxb, int max_ctx, float qscale,
-                                                       int psize, int E) {
+                                                       int psize, int E, int lm) {
   using Bd = Body<DT, D, GMAX>;
   static_assert(GMAX <= 16, "one MFMA column per query head");
   __shared__ typename Bd::Shared sh;
@@ -556,7 +560,8 @@ __global__ __launch_bounds__(256) void decode_part_mfma(void* __restrict__ out, 
   const int cnt = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 0;  // this wave's (<= 64)
   bool bad;
   const int myid =
-      load_ids(bt + (size_t)pl.s * maxb, cnt, num_blocks, [&](int k) { return b0 + wave + k * kWaves; }, bad);
+      load_ids(bt + (size_t)pl.s * maxb, cnt, num_blocks, [&](int k) { return b0 + wave + k * kWaves; }, bad, Hkv,
+               pl.kvh, lm);
   Bd::run(sh, kp, vp, myid, bad, cnt, b0 + wave, kWaves, L, pl.kvh, Hkv, pl.nh, qscale, nparts, p, pl.row0, E, out,
           ws_o, ws_m, ws_l);
 }
@@ -621,7 +626,8 @@ struct Piece {
   int np;     // pieces of the segment (valid with kFirstUnit)
   int flags;  // kWhole | kEnds | kFirstUnit | kLastSlot | kStarts
   int bad;    // an invalid block id in this portion
-  int bto;    // block-table index of chunk tile kk: bto + kk
+  int bto;    // chunk tile kk is the sequence's 16-slot tile bto + kk
+  int srow;   // first block-table entry of the sequence (s * maxb)
   int kvh;    // KV head
   int rb;     // last filled slot of chunk tile kk: min(15, rb - 16 kk)
   int kb;     // first chunk tile
@@ -634,7 +640,8 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
                                                     const int32_t* __restrict__ cl, float* __restrict__ pc_o,
                                                     float* __restrict__ pc_m, float* __restrict__ pc_l,
                                                     int2* __restrict__ info, int B, int Hq, int Hkv, int g, int nsub,
-                                                    int num_blocks, int maxb, int max_ctx, float qscale, int unit) {
+                                                    int num_blocks, int maxb, int max_ctx, float qscale, int unit,
+                                                    int lm) {
   using T = Tile<DT, D>;
   constexpr int KS = T::KS, DPL = T::DPL, ROWB = T::ROWB, QROW = T::QROW, QCH = T::QCH;
   using VVec = typename T::VVec;
@@ -790,7 +797,8 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
         pc.np = np;
         pc.flags = flags;
         pc.bad = 0;
-        pc.bto = sj * maxb + tbj - KBj;
+        pc.bto = tbj - KBj;  // chunk tile kk is the sequence's 16-slot tile bto + kk
+        pc.srow = sj * maxb;
         pc.kvh = kvhj;
         pc.rb = Lj - 1 - (tbj - KBj) * 16;
         pc.kb = KBj;
@@ -862,7 +870,7 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
         dpc[i] = p;
         // (kk is inside piece p by construction; the check keeps a planning
         // error from reading outside the sequence's table row)
-        if (kk - pcs[p].kb < pcs[p].nt) ids[i] = bt[pcs[p].bto + kk];
+        if (kk - pcs[p].kb < pcs[p].nt) ids[i] = bt[pcs[p].srow + ((pcs[p].bto + kk) >> lm)];
         else ids[i] = -1;
       }
     }
@@ -890,7 +898,8 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
           id = 0;
           atomicOr(&s_pc[wave][dpc[i]].bad, 1);
         }
-        desc[kk] = ((unsigned)(id * Hkv + pc.kvh) << 4) | (unsigned)min(15, pc.rb - 16 * kk);
+        const unsigned row = ((unsigned)(id * Hkv + pc.kvh) << lm) | (unsigned)((pc.bto + kk) & ((1 << lm) - 1));
+        desc[kk] = (row << 4) | (unsigned)min(15, pc.rb - 16 * kk);
       }
     }
 #pragma unroll
@@ -1031,7 +1040,7 @@ void launch(const DecodeArgs& a, hipStream_t st) {
   if (a.stream) {
     hipLaunchKernelGGL((decode_stream<DT, D, GMAX>), dim3(a.grid), dim3(256), 0, st, a.out, a.q, a.kp, a.vp, a.bt, a.cl,
                        a.ws_o, a.ws_m, a.ws_l, a.info, a.B, a.Hq, a.Hkv, a.g, a.nsub, a.num_blocks, a.maxb, a.max_ctx,
-                       a.qscale, a.unit);
+                       a.qscale, a.unit, a.lm);
     hipLaunchKernelGGL((decode_stream_reduce<DT, D, GMAX>), dim3(a.Hkv * a.nsub, a.B), dim3(256), 0, st, a.out,
                        a.ws_o, a.ws_m, a.ws_l, a.info, a.Hq, a.g, a.nsub);
     return;
@@ -1040,11 +1049,11 @@ void launch(const DecodeArgs& a, hipStream_t st) {
   if (a.wave_part)
     hipLaunchKernelGGL((decode_part_wave<DT, D, GMAX>), dim3(grid), dim3(256), 0, st, a.out, a.q, a.kp, a.vp, a.bt,
                        a.cl, a.ws_o, a.ws_m, a.ws_l, a.B, a.Hq, a.Hkv, a.g, a.nsub, a.num_blocks, a.maxb, a.max_ctx,
-                       a.qscale, a.psize, a.entries);
+                       a.qscale, a.psize, a.entries, a.lm);
   else
     hipLaunchKernelGGL((decode_part_mfma<DT, D, GMAX>), dim3(grid), dim3(256), 0, st, a.out, a.q, a.kp, a.vp, a.bt,
                        a.cl, a.ws_o, a.ws_m, a.ws_l, a.B, a.Hq, a.Hkv, a.g, a.nsub, a.num_blocks, a.maxb, a.max_ctx,
-                       a.qscale, a.psize, a.entries);
+                       a.qscale, a.psize, a.entries, a.lm);
 }
 
 template <int DT, int D>

@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   const int q0 = a.qs[s], q1 = a.qs[s + 1], L = a.cl[s];
   const int T = q1 - q0;
   const int g = a.g;
-  if (q0 < 0 || q1 < q0 || q1 > a.N || T > L || L > a.maxb * 16 || T > a.max_q) {
+  if (q0 < 0 || q1 < q0 || q1 > a.N || T > L || (int64_t)L > ((int64_t)a.maxb << a.lbs) || T > a.max_q) {
     // Unservable sequence: NaN over whatever part of its row range exists.
     if (tile == a.tiles - 1) {
       const int r0 = min(max(q0, 0), a.N), r1 = min(max(q1, r0), a.N);
@@ -190,8 +190,9 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
 
   // Cooperative load of one step's K and V chunks into registers.
   const int32_t* btrow = a.bt + (size_t)s * a.maxb;
-  const size_t head_off = (size_t)kvh * 16 * D;
-  const size_t blk_stride = (size_t)a.Hkv * 16 * D;
+  const int bmask = (1 << a.lbs) - 1;  // slots per block - 1
+  const size_t head_off = ((size_t)kvh * D) << a.lbs;
+  const size_t blk_stride = ((size_t)a.Hkv * D) << a.lbs;
   const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.kp);
   const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.vp);
   bool bad = false;
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
 #pragma unroll
     for (int m = 0; m < LOADS; ++m) {
       const int tt = (tid + 256 * m) / CH;
-      ids[m] = btrow[min(step * kStep + tt, L - 1) >> 4];
+      ids[m] = btrow[min(step * kStep + tt, L - 1) >> a.lbs];
     }
   };
   auto issue = [&](int step, const int (&ids)[LOADS]) __attribute__((always_inline)) {
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
         bad = true;
         id = 0;
       }
-      const size_t off = (size_t)id * blk_stride + head_off + (size_t)(pos & 15) * D + ch * 8;
+      const size_t off = (size_t)id * blk_stride + head_off + (size_t)(pos & bmask) * D + ch * 8;
       kreg[m] = *reinterpret_cast<const u32x4*>(kp + off);
       vreg[m] = *reinterpret_cast<const u32x4*>(vp + off);
     }

@@ -24,7 +24,10 @@ extern "C" pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, 
   if (dtype != PA_FP32 && dtype != PA_FP16 && dtype != PA_BF16)
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill: unknown dtype %d", (int)dtype);
   if (dtype == PA_FP32) return fail(PA_ERR_UNSUPPORTED, "pa_prefill: fp32 KV is not supported (fp16 or bf16)");
-  if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "pa_prefill: block_size %d (only 16)", block_size);
+  int lbs = -1;
+  for (int k = 3; k <= 7; ++k)
+    if (block_size == 1 << k) lbs = k;
+  if (lbs < 0) return fail(PA_ERR_UNSUPPORTED, "pa_prefill: block_size %d (8, 16, 32, 64 or 128)", block_size);
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill: head_dim %d (64 or 128)", head_dim);
   if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0)
@@ -65,6 +68,7 @@ extern "C" pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, 
   a.num_blocks = num_blocks;
   a.maxb = max_blocks_per_seq;
   a.max_q = max_query_len;
+  a.lbs = lbs;
   a.neg_scale = scale < 0.f;
   a.qscale = fabsf(scale) * 1.4426950408889634f;
   a.dtype = dtype;

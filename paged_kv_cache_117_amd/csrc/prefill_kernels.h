@@ -27,6 +27,7 @@ struct PrefillArgs {
   int tiles;      // row tiles per (sequence, KV head) in the launch
   int grid;       // workgroups launched: 8 * ceil(B * Hkv / 8) * tiles
   int neg_scale;  // scale < 0: the kernel flips the query's sign
+  int lbs;        // log2(block_size)
   float qscale;   // |scale| * log2(e)
   pa_dtype_t dtype;
 };

@@ -77,7 +77,7 @@ def call_decode(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(bs=8), 3), (dict(D=96), 3), (dict(dt=7), 3),
+    (dict(bs=8), 3), (dict(bs=48), 3), (dict(bs=256), 3), (dict(D=96), 3), (dict(dt=7), 3),
     (dict(Hq=3, Hkv=2), 2), (dict(maxctx=33), 2), (dict(ps=24), 2), (dict(B=-1), 2),
     (dict(scale=float("inf")), 2), (dict(q=NULL), 1), (dict(out=8), 2),
     (dict(maxctx=600, maxb=64), 4), (dict(dt=2), 4), (dict(dt=1, wsb=64, ws=256), 4),
@@ -93,7 +93,7 @@ def test_decode_zero_sequences_is_a_no_op():
 
 
 def test_write_and_copy_host_validation():
-    assert L.pa_write_kv(16, 16, 16, 16, 16, 1, 2, 64, 8, 4, 0, NULL) == 3
+    assert L.pa_write_kv(16, 16, 16, 16, 16, 1, 2, 64, 24, 4, 0, NULL) == 3  # block size not a power of two
     assert L.pa_write_kv(16, 16, 16, 16, NULL, 1, 2, 64, 16, 4, 0, NULL) == 1
     assert L.pa_write_kv(16, 16, 8, 16, 16, 1, 2, 64, 16, 4, 0, NULL) == 2
     assert L.pa_write_kv(NULL, NULL, NULL, NULL, NULL, 0, 2, 64, 16, 4, 0, NULL) == 0
@@ -126,7 +126,7 @@ def call_prefill(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(bs=8), 3), (dict(D=96), 3), (dict(dt=7), 3), (dict(dt=0), 3),
+    (dict(bs=4), 3), (dict(bs=256), 3), (dict(D=96), 3), (dict(dt=7), 3), (dict(dt=0), 3),
     (dict(Hq=3, Hkv=2), 2), (dict(maxq=5), 2), (dict(N=-1), 2), (dict(B=-1), 2), (dict(nb=0), 2),
     (dict(scale=float("nan")), 2), (dict(qs=NULL), 1), (dict(q=NULL), 1), (dict(out=8), 2),
 ])
@@ -145,7 +145,7 @@ def test_swap_host_validation():
     """Checks that come before any pointer query or launch."""
     sw = L.pa_swap_blocks
     assert sw(16, 16, 16, 16, 16, 1, 2, 64, 16, 4, 4, 7, NULL) == 3   # dtype
-    assert sw(16, 16, 16, 16, 16, 1, 2, 64, 8, 4, 4, 2, NULL) == 3    # block size
+    assert sw(16, 16, 16, 16, 16, 1, 2, 64, 256, 4, 4, 2, NULL) == 3  # block size
     assert sw(16, 16, 16, 16, 16, 1, 2, 96, 16, 4, 4, 2, NULL) == 3   # head dim
     assert sw(16, 16, 16, 16, 16, -1, 2, 64, 16, 4, 4, 2, NULL) == 2  # negative count
     assert sw(16, 16, NULL, 16, 16, 1, 2, 64, 16, 4, 4, 2, NULL) == 1

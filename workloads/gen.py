@@ -134,8 +134,8 @@ CONFIGS = {
 }
 
 
-def _pool_blocks(lens, factor=1.25):
-    need = int(sum(-(-int(l) // BLOCK_SIZE) for l in lens))
+def _pool_blocks(lens, factor=1.25, block_size=BLOCK_SIZE):
+    need = int(sum(-(-int(l) // block_size) for l in lens))
     return need, int(math.ceil(factor * need))
 
 
@@ -150,6 +150,7 @@ def make_custom(
     num_blocks: int | None = None,
     pool_factor: float = 1.25,
     partition_size: int = 512,
+    block_size: int = BLOCK_SIZE,
 ) -> Workload:
     """Independent sequences: each prefilled with L-1 tokens, then one step.
 
@@ -160,7 +161,7 @@ def make_custom(
         lens = np.asarray(context_lens(_rng(seed, _S_LENS)), dtype=np.int32)
     else:
         lens = np.asarray(context_lens, dtype=np.int32)
-    need, sized = _pool_blocks(lens, pool_factor)
+    need, sized = _pool_blocks(lens, pool_factor, block_size)
     nb = sized if num_blocks is None else int(num_blocks)
     if nb < need:
         raise ValueError(f"pool of {nb} blocks < {need} needed")
@@ -168,8 +169,8 @@ def make_custom(
     perm = _rng(seed, _S_PERM).permutation(nb).astype(np.int32)
     D, Hq, Hkv = head_dim, num_q_heads, num_kv_heads
     q = _normal_storage(seed, _S_Q, (B, Hq, D), dtype)
-    k_pool = _normal_storage(seed, _S_K, (nb, Hkv, BLOCK_SIZE, D), dtype)
-    v_pool = _normal_storage(seed, _S_V, (nb, Hkv, BLOCK_SIZE, D), dtype)
+    k_pool = _normal_storage(seed, _S_K, (nb, Hkv, block_size, D), dtype)
+    v_pool = _normal_storage(seed, _S_V, (nb, Hkv, block_size, D), dtype)
     k_new = _normal_storage(seed, _S_KNEW, (B, Hkv, D), dtype)
     v_new = _normal_storage(seed, _S_VNEW, (B, Hkv, D), dtype)
     ops = []
@@ -181,7 +182,7 @@ def make_custom(
         name=name, dtype=dtype, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
         num_blocks=nb, scale=float(np.float32(1.0) / np.sqrt(np.float32(D))),
         context_lens=lens, perm=perm, q=q, k_pool=k_pool, v_pool=v_pool,
-        k_new=k_new, v_new=v_new, ops=ops, seq_ids=list(range(B)),
+        k_new=k_new, v_new=v_new, ops=ops, seq_ids=list(range(B)), block_size=block_size,
         partition_size=partition_size, meta={"seed": seed, "pool_need": need},
     )
 
@@ -224,9 +225,16 @@ def _make_prefix_share(name, seed, prefix, tails_fn, prompts=32, n=8):
     )
 
 
-def make_workload(key: str) -> Workload:
-    """The named decode-step workloads (see CONFIGS)."""
+def make_workload(key: str, block_size: int = BLOCK_SIZE) -> Workload:
+    """The named decode-step workloads (see CONFIGS); ``block_size`` resizes
+    the pool's blocks (independent-sequence workloads only)."""
     key = key.lower()
+    if block_size != BLOCK_SIZE:
+        if key in ("c4", "c4b"):
+            raise ValueError("the prefix-share workloads use 16-slot blocks")
+        w = make_workload(key)
+        return make_custom(w.name, w.dtype, w.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                           seed=w.meta["seed"], partition_size=w.partition_size, block_size=block_size)
     if key == "c1":
         return make_custom("c1", "fp32", [1, 5, 16, 37], 2, 2, 64, seed=1, num_blocks=16)
     if key == "c2":
@@ -322,7 +330,7 @@ PREFILL_CONFIGS = {
 
 
 def make_prefill_custom(name, dtype, prior_lens, chunk_lens, num_q_heads, num_kv_heads, head_dim, seed,
-                        pool_factor: float = 1.25) -> PrefillWorkload:
+                        pool_factor: float = 1.25, block_size: int = BLOCK_SIZE) -> PrefillWorkload:
     """Independent sequences: each holds its prior tokens, then one chunk is appended.
 
     ``prior_lens`` / ``chunk_lens`` may be lists or one callable
@@ -335,14 +343,14 @@ def make_prefill_custom(name, dtype, prior_lens, chunk_lens, num_q_heads, num_kv
     prior = np.asarray(prior, dtype=np.int32)
     chunk = np.asarray(chunk, dtype=np.int32)
     assert prior.shape == chunk.shape and (prior >= 0).all() and (chunk >= 0).all()
-    need, nb = _pool_blocks(prior + chunk, pool_factor)
+    need, nb = _pool_blocks(prior + chunk, pool_factor, block_size)
     nb = max(nb, need, 1)
     B, N = len(prior), int(chunk.sum())
     D, Hq, Hkv = head_dim, num_q_heads, num_kv_heads
     perm = _rng(seed, _S_PERM).permutation(nb).astype(np.int32)
     q = _normal_storage(seed, _S_Q, (N, Hq, D), dtype)
-    k_pool = _normal_storage(seed, _S_K, (nb, Hkv, BLOCK_SIZE, D), dtype)
-    v_pool = _normal_storage(seed, _S_V, (nb, Hkv, BLOCK_SIZE, D), dtype)
+    k_pool = _normal_storage(seed, _S_K, (nb, Hkv, block_size, D), dtype)
+    v_pool = _normal_storage(seed, _S_V, (nb, Hkv, block_size, D), dtype)
     k_new = _normal_storage(seed, _S_KNEW, (N, Hkv, D), dtype)
     v_new = _normal_storage(seed, _S_VNEW, (N, Hkv, D), dtype)
     ops = []
@@ -354,12 +362,16 @@ def make_prefill_custom(name, dtype, prior_lens, chunk_lens, num_q_heads, num_kv
         name=name, dtype=dtype, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, num_blocks=nb,
         scale=float(np.float32(1.0) / np.sqrt(np.float32(D))), prior_lens=prior, chunk_lens=chunk,
         perm=perm, q=q, k_pool=k_pool, v_pool=v_pool, k_new=k_new, v_new=v_new, ops=ops,
-        seq_ids=list(range(B)), meta={"seed": seed, "pool_need": need})
+        seq_ids=list(range(B)), block_size=block_size, meta={"seed": seed, "pool_need": need})
 
 
-def make_prefill_workload(key: str) -> PrefillWorkload:
+def make_prefill_workload(key: str, block_size: int = BLOCK_SIZE) -> PrefillWorkload:
     """The named chunked-prefill workloads (see PREFILL_CONFIGS)."""
     key = key.lower()
+    if block_size != BLOCK_SIZE:
+        w = make_prefill_workload(key)
+        return make_prefill_custom(w.name, w.dtype, w.prior_lens, w.chunk_lens, w.num_q_heads, w.num_kv_heads,
+                                   w.head_dim, seed=w.meta["seed"], block_size=block_size)
     if key == "p0":
         return make_prefill_custom("p0", "bf16", [0, 20, 5, 64, 100, 9], [1, 7, 16, 33, 130, 0], 8, 2, 64, seed=10)
     if key == "p1":
