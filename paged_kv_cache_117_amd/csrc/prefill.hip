@@ -28,9 +28,10 @@
 //  * PV transposed, O^T = V^T P^T, again with v_mfma_f32_16x16x32: lane
 //    group G's eight k-slots are tokens 4G..4G+3 of the first half and of
 //    the second half, which are exactly the eight weights the lane holds
-//    from the score layout; the V operand (rows = head dims DPL*c + u) is
-//    built from eight 16-byte LDS reads by v_perm_b32 pair interleaves and
-//    shared by all of the wave's column groups.  The output keeps the query
+//    from the score layout.  V is staged in LDS already transposed into that
+//    k-slot order (each thread loads two consecutive tokens and packs their
+//    values pairwise), so the V operand of each output tile is one 16-byte
+//    LDS read, shared by all of the wave's column groups.  The output keeps the query
 //    row in the lane's column, so the rescale by 2^(m_old - m_new) is
 //    lane-local.
 //
@@ -86,10 +87,6 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   }
 }
 
-// 32-bit word w (a compile-time constant after unrolling) of a vector.
-__device__ __forceinline__ uint32_t word(const uint4& v, int w) { return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w; }
-__device__ __forceinline__ uint32_t word(const uint2& v, int w) { return w == 0 ? v.x : v.y; }
-
 // Max of x over lanes l, l ^ 16, l ^ 32 and l ^ 48: the four token groups
 // of the MFMA output layout.
 __device__ __forceinline__ float max_groups(float x, int x16, int x32) {
@@ -116,12 +113,18 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   constexpr int DPL = D / 16;                // output dims per lane per row = PV MFMAs per column group
   constexpr int CH = D / 8;                  // 16-byte chunks per token row
   constexpr int LOADS = kStep * CH / 256;    // chunks of K (and of V) per thread per step
+  constexpr int PAIRS = LOADS / 2;           // (token pair, chunk) items per thread per step
+  constexpr int VROW = kPair + 8;            // LDS row of V^T: one pass's 32 slots + 16 bytes of padding
   constexpr int R = kWaves * 16 * NC;        // rows per workgroup
-  static_assert(LOADS >= 1 && kStep * CH % 256 == 0, "step must split evenly over the threads");
-  using VVec = typename std::conditional<DPL == 8, uint4, uint2>::type;
+  static_assert(PAIRS >= 1 && kStep * CH % 512 == 0, "token pairs must split evenly over the threads");
 
   __shared__ __align__(16) uint16_t sK[2][kStep][ROW];
-  __shared__ __align__(16) uint16_t sV[2][kStep][ROW];
+  // V transposed for the PV A operand: row (pass, u * 16 + c) holds head dim
+  // DPL * c + u of the pass's 32 positions in k-slot order (slot 8G + e is
+  // token 16 (e / 4) + 4G + e % 4), so lane (G, c) reads its operand for
+  // output tile u as one 16-byte row segment.  Rows are 80 bytes: 16
+  // consecutive rows hit 16 distinct 16-byte bank groups.
+  __shared__ __align__(16) uint16_t sV[2][kPairs * D][VROW];
   __shared__ int s_bad;
 
   // XCD-aware numbering.  The hardware deals workgroups round-robin over the
@@ -199,42 +202,60 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   // (plain vector types: HIP's uint4 is copied by memcpy, which keeps these
   // arrays in scratch memory)
   u32x4 kreg[LOADS], vreg[LOADS];
-  // Block id behind each of this thread's loads of a step, fetched one step
-  // ahead of the K/V loads that use it.  These are per-lane vector loads on
-  // purpose: a scalar load would share its wait counter with the LDS operand
-  // reads, and since scalar loads complete out of order the first operand
-  // wait of every step would then also wait for the table lookup.
-  // Positions past L-1 read position L-1.
-  auto load_ids = [&](int step, int (&ids)[LOADS]) __attribute__((always_inline)) {
+  // Thread item m (of PAIRS per step): token pair tp = it / CH (positions
+  // 2 tp and 2 tp + 1 of the step) at 16-byte chunk ch = it % CH, it = tid +
+  // 256 m; both tokens sit in one block (blocks hold >= 8 slots).  The block
+  // id behind each item is fetched one step ahead of the K/V loads that use
+  // it, as a per-lane vector load on purpose: a scalar load would share its
+  // wait counter with the LDS operand reads, and since scalar loads complete
+  // out of order the first operand wait of every step would then also wait
+  // for the table lookup.  Positions past L-1 read position L-1.
+  auto load_ids = [&](int step, int (&ids)[PAIRS]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int m = 0; m < LOADS; ++m) {
-      const int tt = (tid + 256 * m) / CH;
-      ids[m] = btrow[min(step * kStep + tt, L - 1) >> a.lbs];
+    for (int m = 0; m < PAIRS; ++m) {
+      const int tp = (tid + 256 * m) / CH;
+      ids[m] = btrow[min(step * kStep + 2 * tp, L - 1) >> a.lbs];
     }
   };
-  auto issue = [&](int step, const int (&ids)[LOADS]) __attribute__((always_inline)) {
+  auto issue = [&](int step, const int (&ids)[PAIRS]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int m = 0; m < LOADS; ++m) {
-      const int u = tid + 256 * m;
-      const int tt = u / CH, ch = u - tt * CH;
-      const int pos = min(step * kStep + tt, L - 1);
+    for (int m = 0; m < PAIRS; ++m) {
+      const int it = tid + 256 * m;
+      const int tp = it / CH, ch = it - tp * CH;
       int id = ids[m];
       if ((unsigned)id >= (unsigned)a.num_blocks) {
         bad = true;
         id = 0;
       }
-      const size_t off = (size_t)id * blk_stride + head_off + (size_t)(pos & bmask) * D + ch * 8;
-      kreg[m] = *reinterpret_cast<const u32x4*>(kp + off);
-      vreg[m] = *reinterpret_cast<const u32x4*>(vp + off);
+      const size_t blk = (size_t)id * blk_stride + head_off + ch * 8;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int pos = min(step * kStep + 2 * tp + j, L - 1);
+        const size_t off = blk + (size_t)(pos & bmask) * D;
+        kreg[2 * m + j] = *reinterpret_cast<const u32x4*>(kp + off);
+        vreg[2 * m + j] = *reinterpret_cast<const u32x4*>(vp + off);
+      }
     }
   };
   auto stash = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int m = 0; m < LOADS; ++m) {
-      const int u = tid + 256 * m;
-      const int tt = u / CH, ch = u - tt * CH;
-      *reinterpret_cast<u32x4*>(&sK[buf][tt][ch * 8]) = kreg[m];
-      *reinterpret_cast<u32x4*>(&sV[buf][tt][ch * 8]) = vreg[m];
+    for (int m = 0; m < PAIRS; ++m) {
+      const int it = tid + 256 * m;
+      const int tp = it / CH, ch = it - tp * CH;
+      *reinterpret_cast<u32x4*>(&sK[buf][2 * tp][ch * 8]) = kreg[2 * m];
+      *reinterpret_cast<u32x4*>(&sK[buf][2 * tp + 1][ch * 8]) = kreg[2 * m + 1];
+      // V^T: the pair's values of each of the chunk's 8 dims, packed into
+      // one word (token 2 tp in the low half) at k-slot sg, sg + 1.
+      const int pp = (2 * tp) / kPair, t = (2 * tp) % kPair;
+      const int sg = 8 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int dd = 8 * ch + i;
+        const int rr = pp * D + (dd % DPL) * 16 + dd / DPL;
+        const uint32_t lo = vreg[2 * m][i >> 1], hi = vreg[2 * m + 1][i >> 1];
+        *reinterpret_cast<uint32_t*>(&sV[buf][rr][sg]) =
+            __builtin_amdgcn_perm(hi, lo, (i & 1) ? 0x07060302u : 0x05040100u);
+      }
     }
   };
 
@@ -320,26 +341,17 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
       // row sums of the rounded weights: an all-ones A operand
       l_acc[n] = mfma32<DT>(ones, pb[n], l_acc[n]);
     }
-    // V rows of the lane's eight k-slot tokens at dims [DPL*c, DPL*c + DPL).
-    VVec vr[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      vr[e] = *reinterpret_cast<const VVec*>(&sV[buf][r0 + 16 * (e >> 2) + 4 * G + (e & 3)][DPL * c]);
+    // PV: the V^T operand of output tile u is one 16-byte LDS read.
 #pragma unroll
     for (int u = 0; u < DPL; ++u) {
-      const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;
-      const int w = u >> 1;
-      const uint4 va = make_uint4(__builtin_amdgcn_perm(word(vr[1], w), word(vr[0], w), sel),
-                                  __builtin_amdgcn_perm(word(vr[3], w), word(vr[2], w), sel),
-                                  __builtin_amdgcn_perm(word(vr[5], w), word(vr[4], w), sel),
-                                  __builtin_amdgcn_perm(word(vr[7], w), word(vr[6], w), sel));
+      const uint4 va = *reinterpret_cast<const uint4*>(&sV[buf][(r0 / kPair) * D + u * 16 + c][8 * G]);
 #pragma unroll
       for (int n = 0; n < NC; ++n) acc[n][u] = mfma32<DT>(va, pb[n], acc[n][u]);
     }
   };
 
   if (tid == 0) s_bad = 0;
-  int ids[LOADS];
+  int ids[PAIRS];
   load_ids(0, ids);
   issue(0, ids);
   stash(0);
