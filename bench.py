@@ -58,6 +58,7 @@ PREFILL_NAMES = {
     "p2": "Qwen2.5-72B prefill chunk layer fp16 (4 seqs x 1024-token chunks, prior context U[0,7168], "
           "Hq=64, Hkv=8, D=128, block 16)",
     "p3": "mixed chunked-prefill step bf16, Llama shapes (4 chunks of 512 + 60 single tokens)",
+    "p4": "prefix-cache continuation bf16, Llama shapes (4 seqs x 64 new tokens after U[24576,32704] cached)",
 }
 
 
@@ -366,10 +367,14 @@ def main_prefill(args):
     k_new, v_new = dev(w.k_new, True), dev(w.v_new, True)
     lens = dev(w.context_lens.astype(np.int32))
     qstart = dev(w.query_start.astype(np.int32))
+    pf_psize = args.partition_size or 0
+    ws_bytes = pa.prefill_workspace_bytes(w.num_seqs, w.num_tokens, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                          w.max_query_len, w.max_context_len, pf_psize)
     sets = []
     for r in range(R):
         t = np.where(tables >= 0, tables + r * nb, -1).astype(np.int32)
-        sets.append(dict(tables=dev(t), slots=dev(slots + r * nb * w.block_size), out=torch.empty_like(q)))
+        sets.append(dict(tables=dev(t), slots=dev(slots + r * nb * w.block_size), out=torch.empty_like(q),
+                         ws=torch.empty(max(1, ws_bytes), dtype=torch.uint8, device="cuda")))
     stream = torch.cuda.current_stream()
 
     def step(r, ev=None):
@@ -377,7 +382,8 @@ def main_prefill(args):
         pa.write_kv(k_pool, v_pool, k_new, v_new, s["slots"], stream=stream)
         if ev is not None:
             ev[0].record(stream)
-        pa.prefill(q, k_pool, v_pool, s["tables"], lens, qstart, w.scale, w.max_query_len, out=s["out"],
+        pa.prefill(q, k_pool, v_pool, s["tables"], lens, qstart, w.scale, w.max_query_len, w.max_context_len,
+                   out=s["out"], partition_size=pf_psize, workspace=s["ws"],
                    stream=stream)
         if ev is not None:
             ev[1].record(stream)
@@ -427,6 +433,8 @@ def main_prefill(args):
             "block_size": w.block_size,
             "placement": args.placement,
             "rotating_sets": R,
+            "partition_size": pf_psize or "auto",
+            "split": bool(ws_bytes),
         },
         "mfma_peak_frac": round(value / peak, 4),
         "tokens_per_s": round(w.num_tokens / (ms_step * 1e-3), 1),

@@ -157,39 +157,47 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads
  *                    non-decreasing, query_start[num_seqs] = num_tokens;
  *                    T = 0 is allowed (no rows)
  *   max_query_len    host, >= every T (sizes the launch), <= num_tokens
+ *   max_context_len  host, >= every L when the launch is split (below);
+ *                    <= max_blocks_per_seq * block_size
+ *   partition_size   0: automatic -- a launch of fewer than 512 workgroups
+ *                    (row tiles of 128 query rows x KV heads x sequences)
+ *                    over contexts longer than 512 positions is cut into
+ *                    position partitions (at least 512 positions each) until
+ *                    it has about 1024; > 0: always cut at that many
+ *                    positions (rounded up to a multiple of 64).  Each
+ *                    partition's rows carry an online-softmax partial and a
+ *                    second kernel merges them with log-sum-exp weights, the
+ *                    same rule as pa_decode's reduce.
  *   scale            softmax scale (typically 1/sqrt(head_dim)), finite
+ *   workspace        device scratch of at least pa_prefill_workspace_bytes(...)
+ *                    bytes (NULL allowed when that is 0); 256-byte aligned;
+ *                    contents need no initialisation and are clobbered
  *   stream           hipStream_t or NULL
  * Supported: fp16 and bf16 (fp32 returns PA_ERR_UNSUPPORTED), block_size 8,
  * 16, 32, 64 or 128, head_dim 64 or 128, any num_q_heads that is a multiple
  * of num_kv_heads.
  * Device-side contract violations are never dereferenced: a sequence with
- * T > L, L > max_blocks_per_seq * block_size, T > max_query_len or a row range
- * outside [0, num_tokens) gets NaN rows (those inside [0, num_tokens)); a
- * block id outside [0, num_blocks) makes the rows that would read it NaN.
- * `out` must not alias any input.  Needs no workspace.
+ * T > L, L > max_blocks_per_seq * block_size, T > max_query_len, L >
+ * max_context_len in a split launch, or a row range outside [0, num_tokens)
+ * gets NaN rows (those inside [0, num_tokens)); a block id outside
+ * [0, num_blocks) makes the rows that would read it NaN.  `out` must not
+ * alias any input or the workspace.
  */
 pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, const void* v_pool,
                        const int32_t* block_tables, const int32_t* context_lens,
                        const int32_t* query_start, int num_seqs, int num_tokens,
                        int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                       int num_blocks, int max_blocks_per_seq, int max_query_len, float scale,
-                       pa_dtype_t dtype, void* stream);
+                       int num_blocks, int max_blocks_per_seq, int max_query_len,
+                       int max_context_len, int partition_size, float scale, pa_dtype_t dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
-/*
- * pa_write_kv -- store new tokens' K and V rows in their slots
- * (reshape-and-cache).  For each token i with slot = slot_mapping[i] >= 0:
- *   k_pool[slot / bs][h][slot % bs][:] = k_new[i][h][:]   for every KV head h,
- * and the same for V.  One launch covers every token of the step
- * (PagedAttention (tensortonic), "5. Reading the Cache During Attention";
- * PagedAttention and vLLM: Paging the KV Cache Like an OS, "Step 5", the
- * fused write kernel).  Negative slots are skipped; slots >= num_blocks * block_size
- * are skipped too (caller error, never written).  Non-negative slots must be
- * distinct.  Bytes outside the addressed rows are never touched.
- *
- *   k_pool, v_pool   device, [num_blocks][num_kv_heads][block_size][head_dim], dtype
- *   k_new, v_new     device, [num_tokens][num_kv_heads][head_dim], dtype
- *   slot_mapping     device, int64 [num_tokens]
- */
+/* Bytes of workspace pa_prefill needs for these sizes (0 when the launch is
+ * not split); depends on sizes only, not on the device or the dtype.
+ * Returns 0 for invalid sizes as well; pa_prefill reports those. */
+size_t pa_prefill_workspace_bytes(int num_seqs, int num_tokens, int num_q_heads, int num_kv_heads,
+                                  int head_dim, int max_query_len, int max_context_len,
+                                  int partition_size);
+
 /* (pa_write_kv, pa_copy_blocks and pa_swap_blocks take any block_size that is a
  * power of two up to 128.) */
 pa_status_t pa_write_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new,

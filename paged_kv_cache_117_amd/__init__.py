@@ -5,7 +5,7 @@ The device work runs in hand-written HIP kernels inside ``libpa.so`` (C ABI in
 the library and fails with ImportError when it has not been built.
 
     decode(q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len)
-    prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale, max_query_len)
+    prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale, max_query_len, max_context_len)
     write_kv(k_pool, v_pool, k_new, v_new, slot_mapping)
     copy_blocks(k_pool, v_pool, block_pairs)
     swap_blocks(dst_k, dst_v, src_k, src_v, block_pairs)   # device <-> pinned host pool
@@ -22,6 +22,7 @@ from .ops import (  # noqa: F401
     decode,
     decode_workspace_bytes,
     prefill,
+    prefill_workspace_bytes,
     swap_blocks,
     write_kv,
 )

@@ -57,9 +57,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
-constexpr int kPair = 32;                 // positions per compute pass: two blocks
+constexpr int kPair = 32;                 // positions per compute pass: two 16-slot halves
 constexpr int kPairs = 2;                 // passes per step (one barrier, one load batch)
 constexpr int kStep = kPair * kPairs;     // positions per step
+static_assert(kStep == kPrefillStep, "partitions are whole steps");
 
 template <int DT>
 __device__ __forceinline__ f32x4 mfma32(const uint4& a, const uint4& b, const f32x4& c) {
@@ -133,11 +134,15 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   // XCD's L2 while the items -- and with 8 KV heads, one head of every
   // sequence -- are spread evenly over the XCDs.  Within an XCD the tiles
   // are ordered latest rows (longest walks) first, across all its items.
+  // With P > 1 each row tile is further cut into P partitions of positions
+  // (latest tile first, its partitions in order).
   const int items = a.B * a.Hkv;
   const int per_xcd = (items + 7) >> 3;  // items per XCD (upper bound)
   const int xcd = (int)(blockIdx.x & 7), local = (int)(blockIdx.x >> 3);
   const int item = (local % per_xcd) * 8 + xcd;
-  const int tile = a.tiles - 1 - local / per_xcd;
+  const int tp = local / per_xcd;
+  const int tile = a.tiles - 1 - tp / a.P;
+  const int part = tp % a.P;
   if (item >= items) return;
   const int kvh = item % a.Hkv;
   const int s = item / a.Hkv;
@@ -146,9 +151,10 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   const int q0 = a.qs[s], q1 = a.qs[s + 1], L = a.cl[s];
   const int T = q1 - q0;
   const int g = a.g;
-  if (q0 < 0 || q1 < q0 || q1 > a.N || T > L || (int64_t)L > ((int64_t)a.maxb << a.lbs) || T > a.max_q) {
+  if (q0 < 0 || q1 < q0 || q1 > a.N || T > L || (int64_t)L > ((int64_t)a.maxb << a.lbs) || T > a.max_q ||
+      (a.P > 1 && L > a.max_ctx)) {
     // Unservable sequence: NaN over whatever part of its row range exists.
-    if (tile == a.tiles - 1) {
+    if (tile == a.tiles - 1 && part == 0) {
       const int r0 = min(max(q0, 0), a.N), r1 = min(max(q1, r0), a.N);
       nan_rows<DT>(a.out, r0, r1, a.Hq, kvh * g, g, D);
     }
@@ -165,7 +171,10 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
 
   // WG and wave row ranges; positions the workgroup must walk.
   const int rho_wg_last = min(tile * R + R, rows) - 1;
-  const int nsteps = (base + rho_wg_last / g) / kStep + 1;
+  const int nsteps_all = (base + rho_wg_last / g) / kStep + 1;
+  const int step0 = part * a.psteps;  // this partition's steps [step0, nsteps)
+  const int nsteps = a.P > 1 ? min(nsteps_all, step0 + a.psteps) : nsteps_all;
+  if (step0 >= nsteps) return;  // no row of the tile reaches this partition
   const int rho_w0 = tile * R + wave * 16 * NC;
   const bool wave_on = rho_w0 < rows;
   const int lim_w_lo = base + min(rho_w0, rows - 1) / g;
@@ -352,14 +361,14 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
 
   if (tid == 0) s_bad = 0;
   int ids[PAIRS];
-  load_ids(0, ids);
-  issue(0, ids);
+  load_ids(step0, ids);
+  issue(step0, ids);
   stash(0);
-  load_ids(1, ids);  // ids of the next step are always one step ahead of its loads
+  load_ids(step0 + 1, ids);  // ids of the next step are always one step ahead of its loads
   __syncthreads();
 
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
+  for (int step = step0; step < nsteps; ++step) {
+    const int buf = (step - step0) & 1;
     const bool more = step + 1 < nsteps;
     if (more) issue(step + 1, ids);
     if (step + 2 < nsteps) load_ids(step + 2, ids);
@@ -382,6 +391,9 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
 
   // Epilogue: lane (G, c) holds dims [4*DPL*G, 4*DPL*G + 4*DPL) of row c of
   // each column group (acc[n][u][j] is dim DPL*(4G + j) + u).
+  // With P > 1: the normalised partial row, its reference max (base 2) and
+  // its sum go to the workspace for prefill_reduce -- only for rows that
+  // reach this partition (the merge reads partitions 0..lim / psize).
   if (!wave_on) return;
 #pragma unroll
   for (int n = 0; n < NC; ++n) {
@@ -389,21 +401,83 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
     const int rho = rho_w0 + 16 * n + c;
     if (rho >= rows) continue;
     const int i = rho / g, h = rho - i * g;
+    if (a.P > 1 && base + i < step0 * kStep) continue;
     const float inv = wg_bad ? __builtin_nanf("") : 1.f / lt;
     float f[4 * DPL];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int u = 0; u < DPL; ++u) f[j * DPL + u] = acc[n][u][j] * inv;
-    char* dst = reinterpret_cast<char*>(a.out) + (((size_t)(q0 + i) * a.Hq + kvh * g + h) * D + 4 * DPL * G) * 2;
+    const size_t row = (size_t)(q0 + i) * a.Hq + kvh * g + h;
+    if (a.P > 1) {
+      const size_t e = row * a.P + part;
+      float* dst = a.ws_o + e * D + 4 * DPL * G;
 #pragma unroll
-    for (int v = 0; v < DPL / 2; ++v) *reinterpret_cast<uint4*>(dst + 16 * v) = pack16<DT>(f + 8 * v);
+      for (int v = 0; v < DPL; ++v) *reinterpret_cast<float4*>(dst + 4 * v) = make_float4(f[4 * v], f[4 * v + 1], f[4 * v + 2], f[4 * v + 3]);
+      if (G == 0) {
+        a.ws_m[e] = wg_bad ? __builtin_nanf("") : m_run[n] * qs;
+        a.ws_l[e] = lt;
+      }
+    } else {
+      char* dst = reinterpret_cast<char*>(a.out) + (row * D + 4 * DPL * G) * 2;
+#pragma unroll
+      for (int v = 0; v < DPL / 2; ++v) *reinterpret_cast<uint4*>(dst + 16 * v) = pack16<DT>(f + 8 * v);
+    }
+  }
+}
+
+// Merge of the partitions of a split launch: one workgroup per query token,
+// threads over (head, 4 dims).  Row (token n, head h) of sequence s at
+// position p took partitions 0..p / psize; each gives (o, m, l) and the row is
+// sum_p w_p o_p / sum_p w_p with w_p = l_p 2^(m_p - M), M = max_p m_p
+// (PagedAttention (tensortonic), "5. Reading the Cache During Attention":
+// softmax normalises over all positions at once).  Sequences the main
+// kernel wrote as NaN are left alone.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void prefill_reduce(PrefillArgs a) {
+  const int n = blockIdx.x;
+  // the token's sequence: the last s with query_start[s] <= n
+  int lo = 0, hi = a.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.qs[mid] <= n)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const int s = lo;
+  const int q0 = a.qs[s], q1 = a.qs[s + 1], L = a.cl[s];
+  const int T = q1 - q0;
+  if (n < q0 || n >= q1 || q0 < 0 || q1 > a.N || T > L || (int64_t)L > ((int64_t)a.maxb << a.lbs) ||
+      T > a.max_q || L > a.max_ctx)
+    return;
+  const int pos = L - T + (n - q0);
+  const int np = pos / (a.psteps * kStep) + 1;
+  for (int c = threadIdx.x; c < a.Hq * (D / 4); c += blockDim.x) {
+    const int h = c / (D / 4), d = (c - h * (D / 4)) * 4;
+    const size_t row = (size_t)n * a.Hq + h;
+    float M = -__builtin_huge_valf();
+    for (int p = 0; p < np; ++p) M = fmaxf(M, a.ws_m[row * a.P + p]);
+    float den = 0.f;
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p = 0; p < np; ++p) {
+      const size_t e = row * a.P + p;
+      const float w = a.ws_l[e] * fast_exp2(a.ws_m[e] - M);
+      const float4 o = *reinterpret_cast<const float4*>(a.ws_o + e * D + d);
+      den += w;
+      num = make_float4(fmaf(w, o.x, num.x), fmaf(w, o.y, num.y), fmaf(w, o.z, num.z), fmaf(w, o.w, num.w));
+    }
+    const float inv = 1.f / den;
+    float f[8] = {num.x * inv, num.y * inv, num.z * inv, num.w * inv, 0.f, 0.f, 0.f, 0.f};
+    const uint4 v = pack16<DT>(f);
+    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(a.out) + (row * D + d) * 2) = make_uint2(v.x, v.y);
   }
 }
 
 template <int DT, int D>
 void launch_nc(const PrefillArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC>), dim3(a.grid), dim3(256), 0, st, a);
+  if (a.P > 1) hipLaunchKernelGGL((prefill_reduce<DT, D>), dim3(a.N), dim3(256), 0, st, a);
 }
 
 template <int DT>

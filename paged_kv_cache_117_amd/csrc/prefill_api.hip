@@ -1,5 +1,5 @@
-// pa_prefill: argument checks and launch of the prefill kernel
-// (prefill.hip).
+// pa_prefill / pa_prefill_workspace_bytes: argument checks, the split
+// decision, workspace carving and the launches (kernels in prefill.hip).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -9,16 +9,66 @@
 
 namespace {
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Automatic split: a launch of fewer than kFewGroups workgroups (row tiles
+// x KV heads x sequences) over contexts longer than kSplitMin positions is
+// cut into position partitions until it has about kTargetGroups workgroups,
+// each walking at least kSplitMin positions.  Only sizes enter the choice
+// (no device query), so the workspace size is known ahead of the call.
+constexpr int64_t kFewGroups = 512, kTargetGroups = 1024, kSplitMin = 512;
+
+struct Split {
+  int P = 1, psteps = 0;
+};
+
+Split choose_split(int num_seqs, int num_q_heads, int num_kv_heads, int max_query_len, int max_context_len,
+                   int partition_size) {
+  Split sp;
+  if (num_seqs <= 0 || num_kv_heads <= 0 || num_q_heads <= 0 || max_query_len <= 0 || max_context_len <= 0)
+    return sp;
+  const int64_t g = num_q_heads / num_kv_heads;
+  const int64_t tiles = ((int64_t)max_query_len * g + pa::kPrefillRows - 1) / pa::kPrefillRows;
+  const int64_t groups = tiles * num_kv_heads * num_seqs;
+  const int64_t S = pa::kPrefillStep;
+  int64_t psize;
+  if (partition_size > 0) {
+    psize = (partition_size + S - 1) / S * S;
+  } else {
+    if (groups >= kFewGroups || max_context_len <= kSplitMin) return sp;
+    int64_t P = (kTargetGroups + groups - 1) / groups;
+    const int64_t pmax = (max_context_len + kSplitMin - 1) / kSplitMin;
+    if (P > pmax) P = pmax;
+    psize = ((max_context_len + P - 1) / P + S - 1) / S * S;
+  }
+  const int64_t P = (max_context_len + psize - 1) / psize;
+  if (P <= 1) return sp;
+  sp.P = (int)P;
+  sp.psteps = (int)(psize / S);
+  return sp;
+}
 
 }  // namespace
+
+extern "C" size_t pa_prefill_workspace_bytes(int num_seqs, int num_tokens, int num_q_heads, int num_kv_heads,
+                                             int head_dim, int max_query_len, int max_context_len,
+                                             int partition_size) {
+  if (num_seqs <= 0 || num_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || head_dim <= 0 || max_query_len <= 0 || max_context_len < 0 ||
+      partition_size < 0)
+    return 0;
+  const Split sp =
+      choose_split(num_seqs, num_q_heads, num_kv_heads, max_query_len, max_context_len, partition_size);
+  return pa::prefill_workspace(num_tokens, num_q_heads, head_dim, sp.P).total;
+}
 
 extern "C" pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, const void* v_pool,
                                   const int32_t* block_tables, const int32_t* context_lens,
                                   const int32_t* query_start, int num_seqs, int num_tokens, int num_q_heads,
                                   int num_kv_heads, int head_dim, int block_size, int num_blocks,
-                                  int max_blocks_per_seq, int max_query_len, float scale, pa_dtype_t dtype,
-                                  void* stream) {
+                                  int max_blocks_per_seq, int max_query_len, int max_context_len,
+                                  int partition_size, float scale, pa_dtype_t dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
   using namespace pa;
   clear_error();
   if (dtype != PA_FP32 && dtype != PA_FP16 && dtype != PA_BF16)
@@ -42,14 +92,28 @@ extern "C" pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, 
     return fail(PA_ERR_SHAPE, "pa_prefill: max_query_len %d exceeds num_tokens %d", max_query_len, num_tokens);
   if ((int64_t)max_blocks_per_seq * block_size > 0x7fffffffLL)
     return fail(PA_ERR_SHAPE, "pa_prefill: max_blocks_per_seq %d too large", max_blocks_per_seq);
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PA_ERR_SHAPE, "pa_prefill: max_context_len %d outside [0, max_blocks_per_seq*block_size = %lld]",
+                max_context_len, (long long)max_blocks_per_seq * block_size);
+  if (partition_size < 0) return fail(PA_ERR_SHAPE, "pa_prefill: partition_size %d < 0", partition_size);
   if ((int64_t)num_tokens * num_q_heads * head_dim > 0x7fffffffffffLL)
     return fail(PA_ERR_SHAPE, "pa_prefill: %d tokens of %d heads is too large", num_tokens, num_q_heads);
   if (!isfinite(scale)) return fail(PA_ERR_SHAPE, "pa_prefill: scale is not finite");
   if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
     return fail(PA_ERR_NULL, "pa_prefill: NULL pointer");
-  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
     return fail(PA_ERR_SHAPE, "pa_prefill: out, q and the pools must be 16-byte aligned");
+
+  const Split sp =
+      choose_split(num_seqs, num_q_heads, num_kv_heads, max_query_len, max_context_len, partition_size);
+  const PrefillWorkspace wl = prefill_workspace(num_tokens, num_q_heads, head_dim, sp.P);
+  if (wl.total > 0) {
+    if (!workspace) return fail(PA_ERR_WORKSPACE, "pa_prefill: needs %zu bytes of workspace, got NULL", wl.total);
+    if (workspace_bytes < wl.total)
+      return fail(PA_ERR_WORKSPACE, "pa_prefill: needs %zu bytes of workspace, got %zu", wl.total, workspace_bytes);
+    if (!aligned(workspace, 256)) return fail(PA_ERR_WORKSPACE, "pa_prefill: workspace must be 256-byte aligned");
+  }
 
   PrefillArgs a{};
   a.out = out;
@@ -68,15 +132,24 @@ extern "C" pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, 
   a.num_blocks = num_blocks;
   a.maxb = max_blocks_per_seq;
   a.max_q = max_query_len;
+  a.max_ctx = max_context_len;
   a.lbs = lbs;
   a.neg_scale = scale < 0.f;
   a.qscale = fabsf(scale) * 1.4426950408889634f;
   a.dtype = dtype;
-  // Grid: 8 XCDs x ceil(items / 8) work items x row tiles (the kernel maps
-  // each workgroup to an item and tile; see prefill.hip).
+  a.P = sp.P;
+  a.psteps = sp.psteps;
+  if (wl.total) {
+    char* ws = static_cast<char*>(workspace);
+    a.ws_o = reinterpret_cast<float*>(ws + wl.o_off);
+    a.ws_m = reinterpret_cast<float*>(ws + wl.m_off);
+    a.ws_l = reinterpret_cast<float*>(ws + wl.l_off);
+  }
+  // Grid: 8 XCDs x ceil(items / 8) work items x row tiles x partitions (the
+  // kernel maps each workgroup to an item, tile and partition; see prefill.hip).
   const int64_t tiles = ((int64_t)max_query_len * a.g + kPrefillRows - 1) / kPrefillRows;
   const int64_t items = (int64_t)num_kv_heads * num_seqs;
-  const int64_t grid = 8 * ((items + 7) / 8) * tiles;
+  const int64_t grid = 8 * ((items + 7) / 8) * tiles * sp.P;
   if (grid > 0x7fffffffLL)
     return fail(PA_ERR_SHAPE, "pa_prefill: launch of %lld workgroups is too large", (long long)grid);
   a.tiles = (int)tiles;

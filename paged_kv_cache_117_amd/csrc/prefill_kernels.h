@@ -23,15 +23,40 @@ struct PrefillArgs {
   const int32_t* cl;
   const int32_t* qs;  // query_start [B + 1]
   int B, N, Hq, Hkv, g, D;
-  int num_blocks, maxb, max_ctx, max_q;
+  int num_blocks, maxb, max_q;
   int tiles;      // row tiles per (sequence, KV head) in the launch
-  int grid;       // workgroups launched: 8 * ceil(B * Hkv / 8) * tiles
+  int P;          // position partitions per row tile (1: no split, rows written directly)
+  int psteps;     // steps (64 positions each) per partition when P > 1
+  int max_ctx;    // every context length must be <= this when P > 1
+  float* ws_o;    // P > 1: [N * Hq][P][D] normalised partial rows
+  float* ws_m;    // P > 1: [N * Hq][P] reference max, base-2 domain
+  float* ws_l;    // P > 1: [N * Hq][P] sum of weights
+  int grid;       // workgroups launched: 8 * ceil(B * Hkv / 8) * tiles * P
   int neg_scale;  // scale < 0: the kernel flips the query's sign
   int lbs;        // log2(block_size)
   float qscale;   // |scale| * log2(e)
   pa_dtype_t dtype;
 };
 
-void launch_prefill_mfma(const PrefillArgs& a, hipStream_t st);  // fp16 / bf16
+// Positions per step of the prefill kernel (partitions are whole steps).
+constexpr int kPrefillStep = 64;
+
+// Workspace of a split launch: partial rows, then maxima, then sums.
+struct PrefillWorkspace {
+  size_t o_off, m_off, l_off, total;
+};
+
+inline PrefillWorkspace prefill_workspace(size_t N, size_t Hq, size_t D, size_t P) {
+  PrefillWorkspace w{};
+  if (P <= 1) return w;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t rows = N * Hq * P;
+  w.m_off = al(rows * D * sizeof(float));
+  w.l_off = w.m_off + al(rows * sizeof(float));
+  w.total = w.l_off + al(rows * sizeof(float));
+  return w;
+}
+
+void launch_prefill_mfma(const PrefillArgs& a, hipStream_t st);  // fp16 / bf16; + the merge when P > 1
 
 }  // namespace pa

@@ -108,8 +108,14 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_cont
     return out
 
 
+def prefill_workspace_bytes(num_seqs: int, num_tokens: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                            max_query_len: int, max_context_len: int, partition_size: int = 0) -> int:
+    return int(LIB.pa_prefill_workspace_bytes(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                                              max_query_len, max_context_len, partition_size))
+
+
 def prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale: float, max_query_len: int,
-            out=None, stream=None):
+            max_context_len: int, out=None, partition_size: int = 0, workspace=None, stream=None):
     """Paged attention for a chunk of new tokens per sequence (pa_prefill).
 
     ``q`` is [N][Hq][D] with sequence s owning rows query_start[s] ..
@@ -135,10 +141,17 @@ def prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale: f
     _device_tensor(out, "out", q.dtype, 3)
     if out.shape != q.shape:
         raise ValueError("out must have q's shape")
+    need = prefill_workspace_bytes(B, N, Hq, Hkv, D, max_query_len, max_context_len, partition_size)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    if workspace is not None:
+        _device_tensor(workspace, "workspace")
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = LIB.pa_prefill(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                         block_tables.data_ptr(), context_lens.data_ptr(), query_start.data_ptr(), B, N, Hq,
-                        Hkv, D, bs, nb, block_tables.shape[1], int(max_query_len), float(scale),
-                        _dtype_code(q), _stream_handle(stream))
+                        Hkv, D, bs, nb, block_tables.shape[1], int(max_query_len), int(max_context_len),
+                        int(partition_size), float(scale), _dtype_code(q), ws_ptr, ws_bytes, _stream_handle(stream))
     check_status(st, "pa_prefill")
     return out
 

@@ -225,14 +225,14 @@ class GpuPrefillStep:
         if len(self.st.slots):
             pa.write_kv(self.k, self.v, self.k_new, self.v_new, self.slots)
 
-    def attend(self, out=None):
+    def attend(self, out=None, partition_size=0):
         import paged_kv_cache_117_amd as pa
 
         w = self.w
         self.out = pa.prefill(self.q, self.k, self.v, self.tables, self.lens, self.qstart, w.scale,
-                              w.max_query_len, out=out)
+                              w.max_query_len, w.max_context_len, out=out, partition_size=partition_size)
         return self.out
 
-    def run(self, out=None):
+    def run(self, out=None, partition_size=0):
         self.write()
-        return self.attend(out)
+        return self.attend(out, partition_size)

@@ -119,19 +119,23 @@ def test_one_hip_runtime_in_the_process():
 
 def call_prefill(**kw):
     a = dict(out=16, q=16, k=16, v=16, bt=16, cl=16, qs=16, B=1, N=4, Hq=2, Hkv=2, D=64, bs=16, nb=4, maxb=2,
-             maxq=4, scale=0.125, dt=2, stream=NULL)
+             maxq=4, maxctx=20, ps=0, scale=0.125, dt=2, ws=NULL, wsb=0, stream=NULL)
     a.update(kw)
     return L.pa_prefill(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["qs"], a["B"], a["N"], a["Hq"],
-                        a["Hkv"], a["D"], a["bs"], a["nb"], a["maxb"], a["maxq"], a["scale"], a["dt"], a["stream"])
+                        a["Hkv"], a["D"], a["bs"], a["nb"], a["maxb"], a["maxq"], a["maxctx"], a["ps"], a["scale"],
+                        a["dt"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(bs=4), 3), (dict(bs=256), 3), (dict(D=96), 3), (dict(dt=7), 3), (dict(dt=0), 3),
     (dict(Hq=3, Hkv=2), 2), (dict(maxq=5), 2), (dict(N=-1), 2), (dict(B=-1), 2), (dict(nb=0), 2),
     (dict(scale=float("nan")), 2), (dict(qs=NULL), 1), (dict(q=NULL), 1), (dict(out=8), 2),
+    (dict(maxctx=33), 2), (dict(ps=-1), 2), (dict(maxctx=200, maxb=16, ps=64), 4),
+    (dict(maxctx=200, maxb=16, ps=64, wsb=64, ws=256), 4), (dict(maxctx=200, maxb=16, ps=64, wsb=1 << 20, ws=8), 4),
 ])
 def test_prefill_host_validation(kw, status):
-    """Rejected before any device work (these calls never reach the GPU)."""
+    """Rejected before any device work (these calls never reach the GPU: every
+    case must fail a host check, the pointers are not real)."""
     assert call_prefill(**kw) == status
     assert L.pa_last_error().decode()
 
@@ -159,3 +163,16 @@ def test_swap_binding_refuses_pageable_host_pools():
     pool = torch.zeros(4, 2, 16, 64)
     with pytest.raises(ValueError):
         pa.swap_blocks(pool, pool.clone(), pool.clone(), pool.clone(), torch.zeros(1, 2, dtype=torch.int32))
+
+
+def test_prefill_workspace_bytes():
+    # unsplit launches need none: many workgroups, or short contexts
+    assert pa.prefill_workspace_bytes(8, 4096, 32, 8, 128, 512, 3704, 0) == 0
+    assert pa.prefill_workspace_bytes(4, 256, 32, 8, 128, 64, 500, 0) == 0
+    # a short chunk over a long context: 4 seqs x 8 heads x 2 tiles = 64 groups -> 16 partitions
+    rows = 256 * 32 * 16
+    assert pa.prefill_workspace_bytes(4, 256, 32, 8, 128, 64, 32768, 0) == _al(rows * 128 * 4) + 2 * _al(rows * 4)
+    # a given partition size always splits: ceil(32768 / 1024) = 32 partitions
+    rows = 256 * 32 * 32
+    assert pa.prefill_workspace_bytes(4, 256, 32, 8, 128, 64, 32768, 1000) == _al(rows * 128 * 4) + 2 * _al(rows * 4)
+    assert pa.prefill_workspace_bytes(0, 256, 32, 8, 128, 64, 32768, 0) == 0

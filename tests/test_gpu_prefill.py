@@ -125,7 +125,7 @@ def test_deterministic_and_placement_invariant():
     t2 = torch.where(t >= 0, p[t.clamp(min=0)], t).int().contiguous()
     import paged_kv_cache_117_amd as pa
 
-    c = pa.prefill(g.q, k2, v2, t2, g.lens, g.qstart, w.scale, w.max_query_len)
+    c = pa.prefill(g.q, k2, v2, t2, g.lens, g.qstart, w.scale, w.max_query_len, w.max_context_len)
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
@@ -161,19 +161,21 @@ def test_bad_block_id_and_bad_lengths_give_nan_rows():
     # sequence 1: a block id past the pool
     t = g.tables.clone()
     t[1, 0] = w.num_blocks + 5
-    out = to_f64(pa.prefill(g.q, g.k, g.v, t, g.lens, g.qstart, w.scale, w.max_query_len), w.dtype)
+    out = to_f64(pa.prefill(g.q, g.k, g.v, t, g.lens, g.qstart, w.scale, w.max_query_len, w.max_context_len),
+                 w.dtype)
     assert np.isnan(out[qs[1]:qs[2]]).all()
     assert np.array_equal(out[qs[0]:qs[1]], good[qs[0]:qs[1]])
     assert np.array_equal(out[qs[2]:], good[qs[2]:])
     # sequence 2: T > L
     lens = g.lens.clone()
     lens[2] = 5
-    out = to_f64(pa.prefill(g.q, g.k, g.v, g.tables, lens, g.qstart, w.scale, w.max_query_len), w.dtype)
+    out = to_f64(pa.prefill(g.q, g.k, g.v, g.tables, lens, g.qstart, w.scale, w.max_query_len,
+                            w.max_context_len), w.dtype)
     assert np.isnan(out[qs[2]:qs[3]]).all()
     assert np.array_equal(out[:qs[2]], good[:qs[2]])
     # sequence 0: T larger than the max_query_len hint
     qst = torch.tensor([0, 14, 20, 30], dtype=torch.int32, device="cuda")
-    out = to_f64(pa.prefill(g.q, g.k, g.v, g.tables, g.lens, qst, w.scale, 10), w.dtype)
+    out = to_f64(pa.prefill(g.q, g.k, g.v, g.tables, g.lens, qst, w.scale, 10, w.max_context_len), w.dtype)
     assert np.isnan(out[0:14]).all()
 
 
@@ -186,7 +188,57 @@ def test_empty_chunks_between_others():
     g = GpuPrefillStep(w)
     g.write()
     out = torch.full_like(g.q, 7.0)
-    pa.prefill(g.q, g.k, g.v, g.tables, g.lens, g.qstart, w.scale, w.max_query_len, out=out)
+    pa.prefill(g.q, g.k, g.v, g.tables, g.lens, g.qstart, w.scale, w.max_query_len, w.max_context_len, out=out)
     st, k, v = oracle_prefill_pools(w)
     want = oracle.prefill(w.q, k, v, st.tables, w.context_lens, w.query_start, w.scale, w.dtype)
     _check(to_f64(out, w.dtype), want, w.dtype, "emp")
+
+
+@pytest.mark.parametrize("psize", [64, 128, 512, 2048])
+def test_split_partitions_every_row(psize):
+    """Position partitions merged with log-sum-exp weights equal the unsplit
+    attention (a partition of one step upward; rows whose causal limit stops
+    before a partition take no part in it)."""
+    w = make_prefill_custom(f"sp{psize}", "bf16", [0, 300, 1000, 77], [130, 40, 200, 1], 8, 2, 128,
+                            seed=700 + psize)
+    print(f"case split psize={psize}", flush=True)
+    g = GpuPrefillStep(w)
+    out = to_f64(g.run(partition_size=psize), "bf16")
+    st, k, v = oracle_prefill_pools(w)
+    want = oracle.prefill(w.q, k, v, st.tables, w.context_lens, w.query_start, w.scale, w.dtype)
+    _check(out, want, "bf16", f"split {psize}")
+
+
+def test_auto_split_short_chunk_long_context():
+    """A prefix-cache continuation: 64 new tokens after 20k-30k cached ones.
+    The automatic split cuts the walk into partitions (sampled rows)."""
+    import paged_kv_cache_117_amd as pa
+
+    w = make_prefill_custom("cont", "bf16", [20000, 31000], [64, 50], 32, 8, 128, seed=710)
+    assert pa.prefill_workspace_bytes(w.num_seqs, w.num_tokens, 32, 8, 128, w.max_query_len,
+                                      w.max_context_len, 0) > 0
+    g = GpuPrefillStep(w)
+    out = to_f64(g.run(), "bf16")
+    assert np.isfinite(out).all()
+    st, k, v = oracle_prefill_pools(w)
+    rows = _sampled(w, nrand=6, seed=3)
+    _check(out[rows], oracle_prefill_rows(w, st, k, v, rows), "bf16", "cont")
+    # the unsplit launch agrees within rounding
+    one = to_f64(g.attend(partition_size=1 << 20), "bf16")
+    assert np.abs(one - out).max() <= TOL["bf16"]
+
+
+def test_split_with_context_past_the_hint_gives_nan_rows():
+    import paged_kv_cache_117_amd as pa
+
+    w = make_prefill_custom("hint", "bf16", [500, 100], [20, 30], 8, 2, 64, seed=720)
+    g = GpuPrefillStep(w)
+    g.write()
+    good = to_f64(g.attend(partition_size=128), "bf16")
+    lens = g.lens.clone()
+    lens[0] = w.max_context_len + 1  # longer than the max_context_len hint
+    out = to_f64(pa.prefill(g.q, g.k, g.v, g.tables, lens, g.qstart, w.scale, w.max_query_len,
+                            w.max_context_len, partition_size=128), "bf16")
+    qs = w.query_start
+    assert np.isnan(out[qs[0]:qs[1]]).all()
+    assert np.array_equal(out[qs[1]:], good[qs[1]:])

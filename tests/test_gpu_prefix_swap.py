@@ -56,7 +56,7 @@ def test_prefix_hit_then_prefill_of_the_rest():
         table = torch.tensor([bm.table(seq)], dtype=torch.int32, device="cuda")
         lens = torch.tensor([len(toks)], dtype=torch.int32, device="cuda")
         qs = torch.tensor([0, len(toks) - n], dtype=torch.int32, device="cuda")
-        out = pa.prefill(to_device(q_bits[n:], "bf16"), k, v, table, lens, qs, scale, len(toks) - n)
+        out = pa.prefill(to_device(q_bits[n:], "bf16"), k, v, table, lens, qs, scale, len(toks) - n, len(toks))
         torch.cuda.synchronize()
         return n, out
 

@@ -326,6 +326,7 @@ PREFILL_CONFIGS = {
     "p1": "Llama-3.1-8B layer, bf16: 8 seqs x 512-token chunks, prior context U[0,3584], Hq=32, Hkv=8, D=128",
     "p2": "Qwen2.5-72B layer, fp16: 4 seqs x 1024-token chunks, prior context U[0,7168], Hq=64, Hkv=8, D=128",
     "p3": "mixed step, Llama shapes, bf16: 4 chunks of 512 (prior U[0,3584]) + 60 single tokens (prior U[127,4095])",
+    "p4": "prefix-cache continuation, Llama shapes, bf16: 4 seqs x 64 new tokens after U[24576,32704] cached",
 }
 
 
@@ -388,4 +389,8 @@ def make_prefill_workload(key: str, block_size: int = BLOCK_SIZE) -> PrefillWork
                                   r.integers(127, 4095, size=60, endpoint=True)])
             return pri, np.concatenate([np.full(4, 512), np.ones(60, np.int64)])
         return make_prefill_custom("p3", "bf16", lens, None, 32, 8, 128, seed=13)
+    if key == "p4":
+        return make_prefill_custom(
+            "p4", "bf16", lambda r: (r.integers(24576, 32704, size=4, endpoint=True), np.full(4, 64)),
+            None, 32, 8, 128, seed=14)
     raise KeyError(key)
