@@ -4,7 +4,8 @@
 // partition's blocks in logical order, base-2 exponentials, log-sum-exp
 // partials), organised for bandwidth with both products on the matrix cores.
 //
-// Per tile (16 slots of one block, one KV head), in one wavefront:
+// Per tile (16 consecutive slots of one block -- a block of 16 << lm slots
+// holds 2^lm tiles -- and one KV head), in one wavefront:
 //  * Scores S = K q^T are one chain of v_mfma_f32_16x16x32_{bf16,f16}: the K
 //    tile is the A operand (lane (G, c) loads 16 bytes of token c at dims
 //    32k+8G, exactly the operand layout, so K goes from HBM to the matrix
@@ -369,9 +370,9 @@ __device__ __forceinline__ void pipeline(int cnt, KBuf& kA, VBuf& vA, KBuf& kB, 
 }
 
 // What both kernels share once a workgroup knows its (sequence, head group):
-// the query tile in LDS, one wave's tile stream over `cnt` blocks (the k-th
-// at logical block first + k * step, its physical id in lane k of `myid`),
-// staging and the merged write of entry `e` of `nentries`.
+// the query tile in LDS, one wave's tile stream over `cnt` 16-slot tiles (the
+// k-th at logical tile first + k * step, its tile row -- see load_ids -- in
+// lane k of `myid`), staging and the merged write of entry `e` of `nentries`.
 template <int DT, int D, int GMAX>
 struct Body {
   using T = Tile<DT, D>;
@@ -386,7 +387,7 @@ struct Body {
   };
 
   __device__ static __forceinline__ void run(Shared& sh, const char* kp, const char* vp, int myid, bool bad, int cnt,
-                                             int first, int step, int L, int kvh, int Hkv, int nh, float qscale,
+                                             int first, int step, int L, int nh, float qscale,
                                              int nentries, int e, size_t row0, int E, void* out, float* ws_o,
                                              float* ws_m, float* ws_l) {
     const int lane = threadIdx.x & 63;
@@ -516,8 +517,7 @@ __global__ __launch_bounds__(256) void decode_part_wave(void* __restrict__ out, 
   bool bad;
   const int myid =
       load_ids(bt + (size_t)pl.s * maxb, cnt, num_blocks, [&](int k) { return b0 + k; }, bad, Hkv, pl.kvh, lm);
-  Bd::run(sh, kp, vp, myid, bad, cnt, b0, 1, L, pl.kvh, Hkv, pl.nh, qscale, nent, pl.rank, pl.row0, E, out, ws_o,
-          ws_m, ws_l);
+  Bd::run(sh, kp, vp, myid, bad, cnt, b0, 1, L, pl.nh, qscale, nent, pl.rank, pl.row0, E, out, ws_o, ws_m, ws_l);
 }
 
 // ---------------------------------------------------------------------------
@@ -562,8 +562,8 @@ __global__ __launch_bounds__(256) void decode_part_mfma(void* __restrict__ out, 
   const int myid =
       load_ids(bt + (size_t)pl.s * maxb, cnt, num_blocks, [&](int k) { return b0 + wave + k * kWaves; }, bad, Hkv,
                pl.kvh, lm);
-  Bd::run(sh, kp, vp, myid, bad, cnt, b0 + wave, kWaves, L, pl.kvh, Hkv, pl.nh, qscale, nparts, p, pl.row0, E, out,
-          ws_o, ws_m, ws_l);
+  Bd::run(sh, kp, vp, myid, bad, cnt, b0 + wave, kWaves, L, pl.nh, qscale, nparts, p, pl.row0, E, out, ws_o, ws_m,
+          ws_l);
 }
 
 // ---------------------------------------------------------------------------
