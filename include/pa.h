@@ -173,9 +173,10 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads
  *                    bytes (NULL allowed when that is 0); 256-byte aligned;
  *                    contents need no initialisation and are clobbered
  *   stream           hipStream_t or NULL
- * Supported: fp16 and bf16 (fp32 returns PA_ERR_UNSUPPORTED), block_size 8,
- * 16, 32, 64 or 128, head_dim 64 or 128, any num_q_heads that is a multiple
- * of num_kv_heads.
+ * Supported: fp16 and bf16 with block_size 8, 16, 32, 64 or 128 (matrix
+ * cores); fp32 with block_size 16, 32, 64 or 128 (VALU, one query token per
+ * work item, never split); head_dim 64 or 128; any num_q_heads that is a
+ * multiple of num_kv_heads.
  * Device-side contract violations are never dereferenced: a sequence with
  * T > L, L > max_blocks_per_seq * block_size, T > max_query_len, L >
  * max_context_len in a split launch, or a row range outside [0, num_tokens)

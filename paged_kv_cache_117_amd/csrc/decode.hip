@@ -50,7 +50,8 @@ __global__ __launch_bounds__(64) void decode_part_valu(void* __restrict__ out, c
                                                       float* __restrict__ ws_o, float* __restrict__ ws_m,
                                                       float* __restrict__ ws_l, int B, int Hq, int Hkv, int g,
                                                       int nsub, int num_blocks, int maxb, int max_ctx, float qscale,
-                                                      int psize, int P, int lm) {
+                                                      int psize, int P, int lm, const int32_t* __restrict__ qst,
+                                                      int nseq, int max_q) {
   constexpr int ES = Elem<DT>::kBytes;
   constexpr int ROWB = D * ES;
   constexpr int LPR = ROWB / 16;
@@ -62,6 +63,10 @@ __global__ __launch_bounds__(64) void decode_part_valu(void* __restrict__ out, c
   const int c = lane % LPR;
   // 1-D grid: KV head / sub-group fastest, then sequence, then partition, so
   // the round-robin deal of workgroups to the 8 XCDs balances the work.
+  // With `qst` (several query tokens per sequence, pa_prefill): s is a
+  // query token, row s of q and out, of the sequence `seq` whose rows
+  // qst[seq] .. qst[seq+1]-1 hold it; at position L_seq - T + (s - qst[seq])
+  // it sees that many positions plus one, through its sequence's table.
   const int hs = Hkv * nsub;
   const int idx = blockIdx.x;
   const int hsub = idx % hs;
@@ -69,9 +74,27 @@ __global__ __launch_bounds__(64) void decode_part_valu(void* __restrict__ out, c
   const int p = idx / (hs * B);
   const int kvh = hsub / nsub;
   const int sub = hsub - kvh * nsub;
-  int L = cl[s];
-  const bool bad_len = L < 0 || L > max_ctx;
-  if (bad_len) L = 0;
+  int seq = s, L;
+  bool bad_len;
+  if (qst) {
+    int lo = 0, hi = nseq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (qst[mid] <= s)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    seq = lo;
+    const int q0 = qst[seq], q1 = qst[seq + 1], Ls = cl[seq], T = q1 - q0;
+    bad_len = s < q0 || s >= q1 || q0 < 0 || q1 > B || T > Ls || (int64_t)Ls > ((int64_t)maxb << (lm + 4)) ||
+              T > max_q;
+    L = bad_len ? 0 : Ls - T + (s - q0) + 1;
+  } else {
+    L = cl[s];
+    bad_len = L < 0 || L > max_ctx;
+    if (bad_len) L = 0;
+  }
   const int hbase = kvh * g + sub * GMAX;
   const int nh = min(GMAX, g - sub * GMAX);
   if (L == 0) {
@@ -110,7 +133,7 @@ __global__ __launch_bounds__(64) void decode_part_valu(void* __restrict__ out, c
   const int nblk = (L + 15) / 16;
   const int b0 = p * (psize / 16);
   const int b1 = min(b0 + psize / 16, nblk);
-  const int32_t* btrow = bt + (size_t)s * maxb;
+  const int32_t* btrow = bt + (size_t)seq * maxb;
   const size_t lane_off = (size_t)r * ROWB + c * 16;
   bool bad = false;
 
@@ -272,7 +295,7 @@ void launch_valu(const DecodeArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)a.P * a.Hkv * a.nsub * a.B;
   hipLaunchKernelGGL((decode_part_valu<DT, D, GMAX>), dim3(grid), dim3(64), 0, st, a.out, a.q, a.kp, a.vp, a.bt,
                      a.cl, a.ws_o, a.ws_m, a.ws_l, a.B, a.Hq, a.Hkv, a.g, a.nsub, a.num_blocks, a.maxb, a.max_ctx,
-                     a.qscale, a.psize, a.P, a.lm);
+                     a.qscale, a.psize, a.P, a.lm, a.qst, a.nseq, a.max_q);
 }
 
 template <int DT, int D>

@@ -31,6 +31,10 @@ struct DecodeArgs {
   float qscale;  // scale * log2(e)
   pa_dtype_t dtype;
   int lm;        // log2(block_size / 16): the kernels walk 16-slot tiles, 2^lm per block
+  // VALU kernel only: several query tokens per sequence (pa_prefill on fp32
+  // KV).  B is then the number of query tokens, qst the [nseq + 1] row starts.
+  const int32_t* qst;
+  int nseq, max_q;
 };
 
 // Workspace: the partition partials, when some sequence spans more than one

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "decode_kernels.h"
 #include "pa_internal.h"
 #include "prefill_kernels.h"
 
@@ -73,11 +74,12 @@ extern "C" pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, 
   clear_error();
   if (dtype != PA_FP32 && dtype != PA_FP16 && dtype != PA_BF16)
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill: unknown dtype %d", (int)dtype);
-  if (dtype == PA_FP32) return fail(PA_ERR_UNSUPPORTED, "pa_prefill: fp32 KV is not supported (fp16 or bf16)");
   int lbs = -1;
   for (int k = 3; k <= 7; ++k)
     if (block_size == 1 << k) lbs = k;
   if (lbs < 0) return fail(PA_ERR_UNSUPPORTED, "pa_prefill: block_size %d (8, 16, 32, 64 or 128)", block_size);
+  if (dtype == PA_FP32 && lbs < 4)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: fp32 KV takes block_size 16, 32, 64 or 128 (got %d)", block_size);
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill: head_dim %d (64 or 128)", head_dim);
   if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0)
@@ -113,6 +115,44 @@ extern "C" pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, 
     if (workspace_bytes < wl.total)
       return fail(PA_ERR_WORKSPACE, "pa_prefill: needs %zu bytes of workspace, got %zu", wl.total, workspace_bytes);
     if (!aligned(workspace, 256)) return fail(PA_ERR_WORKSPACE, "pa_prefill: workspace must be 256-byte aligned");
+  }
+
+  if (dtype == PA_FP32) {
+    // fp32 KV: the VALU attention kernel with one query token per work item
+    // (a token at position p is a single-query attention over p + 1
+    // positions of its sequence), no split.
+    DecodeArgs d{};
+    d.out = out;
+    d.q = q;
+    d.kp = static_cast<const char*>(k_pool);
+    d.vp = static_cast<const char*>(v_pool);
+    d.bt = block_tables;
+    d.cl = context_lens;
+    d.B = num_tokens;
+    d.Hq = num_q_heads;
+    d.Hkv = num_kv_heads;
+    d.g = num_q_heads / num_kv_heads;
+    d.gmax = d.g >= 8 ? 8 : d.g > 2 ? 4 : d.g;
+    d.nsub = (d.g + d.gmax - 1) / d.gmax;
+    d.D = head_dim;
+    d.num_blocks = num_blocks;
+    d.maxb = max_blocks_per_seq;
+    d.max_ctx = 0x7fffffff;
+    d.psize = 1 << 28;  // one partition: the whole walk
+    d.P = 1;
+    d.qscale = scale * 1.4426950408889634f;
+    d.dtype = dtype;
+    d.lm = lbs - 4;
+    d.qst = query_start;
+    d.nseq = num_seqs;
+    d.max_q = max_query_len;
+    if ((int64_t)num_tokens * num_kv_heads * d.nsub > 0x7fffffffLL)
+      return fail(PA_ERR_SHAPE, "pa_prefill: launch of %lld workgroups is too large",
+                  (long long)num_tokens * num_kv_heads * d.nsub);
+    launch_decode_valu(d, static_cast<hipStream_t>(stream));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "pa_prefill: launch failed: %s", hipGetErrorString(e));
+    return PA_OK;
   }
 
   PrefillArgs a{};

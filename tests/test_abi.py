@@ -127,7 +127,7 @@ def call_prefill(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(bs=4), 3), (dict(bs=256), 3), (dict(D=96), 3), (dict(dt=7), 3), (dict(dt=0), 3),
+    (dict(bs=4), 3), (dict(bs=256), 3), (dict(D=96), 3), (dict(dt=7), 3), (dict(dt=0, bs=8), 3),
     (dict(Hq=3, Hkv=2), 2), (dict(maxq=5), 2), (dict(N=-1), 2), (dict(B=-1), 2), (dict(nb=0), 2),
     (dict(scale=float("nan")), 2), (dict(qs=NULL), 1), (dict(q=NULL), 1), (dict(out=8), 2),
     (dict(maxctx=33), 2), (dict(ps=-1), 2), (dict(maxctx=200, maxb=16, ps=64), 4),

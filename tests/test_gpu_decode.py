@@ -46,6 +46,21 @@ def test_c1_tiny_fp32():
         assert np.array_equal(got[0, h], v0[h // (w.num_q_heads // w.num_kv_heads)])
 
 
+def test_c1_appending_after_the_lengths():
+    """C1's sequences one token later (lengths 2, 6, 17, 38): the sequence at
+    16 tokens has a full last block, so its step pops a fresh block from the
+    free list and writes slot 0 of it (Paging the KV Cache Like an OS, "Step
+    3", request A: a new block only when the last one is full)."""
+    w = make_custom("c1+1", "fp32", [2, 6, 17, 38], 2, 2, 64, seed=1, num_blocks=16)
+    g = GpuStep(w)
+    pre = [list(r[r >= 0]) for r in g.st.pre_tables]
+    post = [list(r[r >= 0]) for r in g.st.tables]
+    assert len(post[2]) == len(pre[2]) + 1 and post[2][:-1] == pre[2]
+    assert g.st.slots[2] == post[2][-1] * 16  # slot 0 of the new block
+    assert all(len(post[s]) == len(pre[s]) for s in (0, 1, 3))
+    check(w)
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("g", [1, 2, 3, 4, 8, 16])

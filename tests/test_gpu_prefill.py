@@ -242,3 +242,28 @@ def test_split_with_context_past_the_hint_gives_nan_rows():
     qs = w.query_start
     assert np.isnan(out[qs[0]:qs[1]]).all()
     assert np.array_equal(out[qs[1]:], good[qs[1]:])
+
+
+@pytest.mark.parametrize("g,D,bs", [(1, 64, 16), (3, 128, 32), (4, 64, 128), (8, 128, 16)])
+def test_fp32_every_row(g, D, bs):
+    """fp32 KV goes through the VALU kernel, one query token per work item
+    (tolerance 1e-5)."""
+    w = make_prefill_custom(f"f32_{g}_{D}_{bs}", "fp32", [0, 45, 130, 9], [40, 1, 77, 0], 2 * g, 2, D,
+                            seed=800 + g + D + bs, block_size=bs)
+    print(f"case fp32 g={g} D={D} bs={bs}", flush=True)
+    _full_parity(w)
+
+
+def test_fp32_bad_lengths_give_nan_rows():
+    import paged_kv_cache_117_amd as pa
+
+    w = make_prefill_custom("f32bad", "fp32", [20, 20], [10, 10], 4, 2, 64, seed=810)
+    g = GpuPrefillStep(w)
+    good = to_f64(g.run(), "fp32")
+    lens = g.lens.clone()
+    lens[1] = 5  # T > L
+    out = to_f64(pa.prefill(g.q, g.k, g.v, g.tables, lens, g.qstart, w.scale, w.max_query_len,
+                            w.max_context_len), "fp32")
+    qs = w.query_start
+    assert np.isnan(out[qs[1]:qs[2]]).all()
+    assert np.array_equal(out[:qs[1]], good[:qs[1]])
