@@ -426,15 +426,20 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   }
 }
 
-// Merge of the partitions of a split launch: one workgroup per query token,
-// threads over (head, 4 dims).  Row (token n, head h) of sequence s at
-// position p took partitions 0..p / psize; each gives (o, m, l) and the row is
-// sum_p w_p o_p / sum_p w_p with w_p = l_p 2^(m_p - M), M = max_p m_p
-// (PagedAttention (tensortonic), "5. Reading the Cache During Attention":
-// softmax normalises over all positions at once).  Sequences the main
-// kernel wrote as NaN are left alone.
+// Merge of the partitions of a split launch: workgroup (token n, head
+// group y), one thread per (head, 4 dims).  Row (token n, head h) of
+// sequence s at position p took partitions 0..p / psize; each gives (o, m, l)
+// and the row is sum_p w_p o_p / sum_p w_p with w_p = l_p 2^(m_p - M),
+// M = max_p m_p (PagedAttention (tensortonic), "5. Reading the Cache During
+// Attention": softmax normalises over all positions at once).  Partitions
+// are read 8 at a time with all their loads in flight, the running maximum
+// rescaling what came before.  Sequences the main kernel wrote as NaN are
+// left alone.
+constexpr int kMergeBatch = 8;
+
 template <int DT, int D>
 __global__ __launch_bounds__(256) void prefill_reduce(PrefillArgs a) {
+  constexpr int HPB = 256 / (D / 4);  // heads per workgroup
   const int n = blockIdx.x;
   // the token's sequence: the last s with query_start[s] <= n
   int lo = 0, hi = a.B - 1;
@@ -451,33 +456,58 @@ __global__ __launch_bounds__(256) void prefill_reduce(PrefillArgs a) {
   if (n < q0 || n >= q1 || q0 < 0 || q1 > a.N || T > L || (int64_t)L > ((int64_t)a.maxb << a.lbs) ||
       T > a.max_q || L > a.max_ctx)
     return;
+  const int h = blockIdx.y * HPB + (int)threadIdx.x / (D / 4);
+  if (h >= a.Hq) return;
+  const int d = ((int)threadIdx.x % (D / 4)) * 4;
   const int pos = L - T + (n - q0);
   const int np = pos / (a.psteps * kStep) + 1;
-  for (int c = threadIdx.x; c < a.Hq * (D / 4); c += blockDim.x) {
-    const int h = c / (D / 4), d = (c - h * (D / 4)) * 4;
-    const size_t row = (size_t)n * a.Hq + h;
-    float M = -__builtin_huge_valf();
-    for (int p = 0; p < np; ++p) M = fmaxf(M, a.ws_m[row * a.P + p]);
-    float den = 0.f;
-    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int p = 0; p < np; ++p) {
-      const size_t e = row * a.P + p;
-      const float w = a.ws_l[e] * fast_exp2(a.ws_m[e] - M);
-      const float4 o = *reinterpret_cast<const float4*>(a.ws_o + e * D + d);
-      den += w;
-      num = make_float4(fmaf(w, o.x, num.x), fmaf(w, o.y, num.y), fmaf(w, o.z, num.z), fmaf(w, o.w, num.w));
+  const size_t row = (size_t)n * a.Hq + h;
+  const float* pm = a.ws_m + row * a.P;
+  const float* pl = a.ws_l + row * a.P;
+  const float* po = a.ws_o + row * a.P * D + d;
+  float M = -__builtin_huge_valf(), den = 0.f;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p0 = 0; p0 < np; p0 += kMergeBatch) {
+    float mv[kMergeBatch], lv[kMergeBatch];
+    float4 ov[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      mv[j] = -__builtin_huge_valf();
+      lv[j] = 0.f;
+      ov[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (p0 + j < np) {
+        mv[j] = pm[p0 + j];
+        lv[j] = pl[p0 + j];
+        ov[j] = *reinterpret_cast<const float4*>(po + (size_t)(p0 + j) * D);
+      }
     }
-    const float inv = 1.f / den;
-    float f[8] = {num.x * inv, num.y * inv, num.z * inv, num.w * inv, 0.f, 0.f, 0.f, 0.f};
-    const uint4 v = pack16<DT>(f);
-    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(a.out) + (row * D + d) * 2) = make_uint2(v.x, v.y);
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) Mn = fmaxf(Mn, mv[j]);
+    const float r = fast_exp2(M - Mn);  // 0 on the first batch (M = -inf)
+    den *= r;
+    num = make_float4(num.x * r, num.y * r, num.z * r, num.w * r);
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const float w = lv[j] * fast_exp2(mv[j] - Mn);  // 0 past the last partition
+      den += w;
+      num = make_float4(fmaf(w, ov[j].x, num.x), fmaf(w, ov[j].y, num.y), fmaf(w, ov[j].z, num.z),
+                        fmaf(w, ov[j].w, num.w));
+    }
+    M = Mn;
   }
+  const float inv = 1.f / den;
+  float f[8] = {num.x * inv, num.y * inv, num.z * inv, num.w * inv, 0.f, 0.f, 0.f, 0.f};
+  const uint4 v = pack16<DT>(f);
+  *reinterpret_cast<uint2*>(reinterpret_cast<char*>(a.out) + (row * D + d) * 2) = make_uint2(v.x, v.y);
 }
 
 template <int DT, int D>
 void launch_nc(const PrefillArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC>), dim3(a.grid), dim3(256), 0, st, a);
-  if (a.P > 1) hipLaunchKernelGGL((prefill_reduce<DT, D>), dim3(a.N), dim3(256), 0, st, a);
+  constexpr int HPB = 256 / (D / 4);
+  if (a.P > 1)
+    hipLaunchKernelGGL((prefill_reduce<DT, D>), dim3(a.N, (a.Hq + HPB - 1) / HPB), dim3(256), 0, st, a);
 }
 
 template <int DT>

@@ -225,12 +225,13 @@ class GpuPrefillStep:
         if len(self.st.slots):
             pa.write_kv(self.k, self.v, self.k_new, self.v_new, self.slots)
 
-    def attend(self, out=None, partition_size=0):
+    def attend(self, out=None, partition_size=0, workspace=None):
         import paged_kv_cache_117_amd as pa
 
         w = self.w
         self.out = pa.prefill(self.q, self.k, self.v, self.tables, self.lens, self.qstart, w.scale,
-                              w.max_query_len, w.max_context_len, out=out, partition_size=partition_size)
+                              w.max_query_len, w.max_context_len, out=out, partition_size=partition_size,
+                              workspace=workspace)
         return self.out
 
     def run(self, out=None, partition_size=0):

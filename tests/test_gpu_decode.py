@@ -185,20 +185,35 @@ def _decode_with(g, ws, max_ctx=None, tables=None, partition_size=0):
 
 def test_workspace_reuse_across_calls_and_shapes():
     """One workspace, filled with NaN bit patterns first, serves back-to-back
-    calls of different shapes: no call depends on what an earlier one left."""
+    calls of different shapes and paths (even split, partitions, a split
+    prefill): no call depends on what an earlier one left."""
+    from harness import GpuPrefillStep
+    from workloads import make_prefill_custom
+
     wa = make_custom("wsA", "bf16", [700, 33, 1500, 16, 5000, 2], 32, 8, 128, seed=31)
     wb = make_custom("wsB", "fp16", [90, 4096, 512, 1], 16, 2, 64, seed=32)
-    ga, gb = GpuStep(wa), GpuStep(wb)
+    wp = make_prefill_custom("wsP", "bf16", [3000, 100], [40, 7], 16, 4, 128, seed=35)
+    ga, gb, gp = GpuStep(wa), GpuStep(wb), GpuPrefillStep(wp)
     ra, rb = ga.run().clone(), gb.run().clone()
-    need = max(pa.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_context_len)
-               for w in (wa, wb))
+    rpart = ga.run(partition_size=256).clone()
+    rp = gp.run(partition_size=512).clone()
+    need = max([pa.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_context_len)
+                for w in (wa, wb)] +
+               [pa.decode_workspace_bytes(wa.num_seqs, 32, 8, 128, wa.max_context_len, 256),
+                pa.prefill_workspace_bytes(wp.num_seqs, wp.num_tokens, 16, 4, 128, wp.max_query_len,
+                                           wp.max_context_len, 512)])
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
     for it in range(3):
         print(f"[decode] shared workspace round {it}", flush=True)
         oa = _decode_with(ga, ws)
+        op = gp.attend(partition_size=512, workspace=ws)
         ob = _decode_with(gb, ws)
+        opart = _decode_with(ga, ws, partition_size=256)
+        torch.cuda.synchronize()
         assert torch.equal(ra.view(torch.int16), oa.view(torch.int16))
         assert torch.equal(rb.view(torch.int16), ob.view(torch.int16))
+        assert torch.equal(rpart.view(torch.int16), opart.view(torch.int16))
+        assert torch.equal(rp.view(torch.int16), op.view(torch.int16))
     _, _, _, want = oracle_step(wa)
     assert max_err(to_f64(ra, "bf16"), want) <= TOL["bf16"]
     _, _, _, want = oracle_step(wb)
