@@ -118,6 +118,7 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   constexpr int VROW = kPair + 8;            // LDS row of V^T: one pass's 32 slots + 16 bytes of padding
   constexpr int R = kWaves * 16 * NC;        // rows per workgroup
   static_assert(PAIRS >= 1 && kStep * CH % 512 == 0, "token pairs must split evenly over the threads");
+  static_assert(8 % DPL == 0, "a 16-byte chunk's dims map to whole V^T rows");
 
   __shared__ __align__(16) uint16_t sK[2][kStep][ROW];
   // V transposed for the PV A operand: row (pass, u * 16 + c) holds head dim
@@ -203,10 +204,13 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   // Cooperative load of one step's K and V chunks into registers.
   const int32_t* btrow = a.bt + (size_t)s * a.maxb;
   const int bmask = (1 << a.lbs) - 1;  // slots per block - 1
-  const size_t head_off = ((size_t)kvh * D) << a.lbs;
-  const size_t blk_stride = ((size_t)a.Hkv * D) << a.lbs;
-  const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.kp);
-  const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.vp);
+  // Byte offsets: a block is Hkv * bs * D * 2 bytes (< 2^32, checked on the
+  // host), so a slot's address is one 32 x 32 -> 64-bit multiply-add of the
+  // block id plus a 32-bit offset inside the block.
+  const uint32_t head_off = ((uint32_t)kvh * D * 2) << a.lbs;
+  const uint32_t blk_bytes = ((uint32_t)a.Hkv * D * 2) << a.lbs;
+  const char* kp = a.kp;
+  const char* vp = a.vp;
   bool bad = false;
   // (plain vector types: HIP's uint4 is copied by memcpy, which keeps these
   // arrays in scratch memory)
@@ -231,16 +235,16 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
     for (int m = 0; m < PAIRS; ++m) {
       const int it = tid + 256 * m;
       const int tp = it / CH, ch = it - tp * CH;
-      int id = ids[m];
-      if ((unsigned)id >= (unsigned)a.num_blocks) {
+      uint32_t id = (uint32_t)ids[m];
+      if (id >= (uint32_t)a.num_blocks) {
         bad = true;
         id = 0;
       }
-      const size_t blk = (size_t)id * blk_stride + head_off + ch * 8;
+      const uint32_t in_blk = head_off + ch * 16;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int pos = min(step * kStep + 2 * tp + j, L - 1);
-        const size_t off = blk + (size_t)(pos & bmask) * D;
+        const uint64_t off = (uint64_t)id * blk_bytes + (in_blk + (uint32_t)(pos & bmask) * (D * 2));
         kreg[2 * m + j] = *reinterpret_cast<const u32x4*>(kp + off);
         vreg[2 * m + j] = *reinterpret_cast<const u32x4*>(vp + off);
       }
@@ -254,26 +258,30 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
       *reinterpret_cast<u32x4*>(&sK[buf][2 * tp][ch * 8]) = kreg[2 * m];
       *reinterpret_cast<u32x4*>(&sK[buf][2 * tp + 1][ch * 8]) = kreg[2 * m + 1];
       // V^T: the pair's values of each of the chunk's 8 dims, packed into
-      // one word (token 2 tp in the low half) at k-slot sg, sg + 1.
+      // one word (token 2 tp in the low half) at k-slot sg, sg + 1.  Dim
+      // dd = 8 ch + i goes to row pp D + (dd % DPL) 16 + dd / DPL, which
+      // (DPL dividing 8) is the lane's row pp D + (8 / DPL) ch plus a
+      // constant per i: one address per item, the rest immediate offsets.
       const int pp = (2 * tp) / kPair, t = (2 * tp) % kPair;
       const int sg = 8 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3);
+      uint16_t* vrow = &sV[buf][pp * D + (8 / DPL) * ch][sg];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int dd = 8 * ch + i;
-        const int rr = pp * D + (dd % DPL) * 16 + dd / DPL;
         const uint32_t lo = vreg[2 * m][i >> 1], hi = vreg[2 * m + 1][i >> 1];
-        *reinterpret_cast<uint32_t*>(&sV[buf][rr][sg]) =
+        *reinterpret_cast<uint32_t*>(vrow + ((i % DPL) * 16 + i / DPL) * VROW) =
             __builtin_amdgcn_perm(hi, lo, (i & 1) ? 0x07060302u : 0x05040100u);
       }
     }
   };
 
   float m_run[NC];
+  float moff[NC];   // -m_run * qs: the weights' exponent offset
   f32x4 l_acc[NC];  // row sums of the rounded weights, from the matrix core (all four entries equal)
   f32x4 acc[NC][DPL];
 #pragma unroll
   for (int n = 0; n < NC; ++n) {
     m_run[n] = -__FLT_MAX__;  // finite, so a zero scale gives 2^0, not NaN
+    moff[n] = -m_run[n] * qs;  // (+inf for scales above 1: the first weights overflow and set the reference)
     l_acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < DPL; ++u) acc[n][u] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -281,11 +289,12 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
 
   // One pass over 32 positions starting at t0 (LDS rows r0..r0+31).
   // Lazy rescaling: the weights use a reference max m_run that is raised
-  // only when some row of the wave sees a score more than 2^kSlack above it
-  // (then every row moves to its true running max); otherwise the weights
-  // may exceed 1, by at most 2^kSlack, and the accumulators keep their
-  // scale.  l and acc always share the reference, so o = acc / l is exact.
-  constexpr float kSlack = 8.f;
+  // only when some weight of the wave comes out above 2^kSlack (then every
+  // row moves to its true running max and its weights are recomputed);
+  // otherwise the weights may exceed 1, by at most 2^kSlack, and the
+  // accumulators keep their scale.  l and acc always share the reference,
+  // so o = acc / l is exact.
+  constexpr uint32_t kSlackBits = 0x43800000u;  // 2^kSlack = 256.0f, kSlack = 8
   constexpr uint32_t kOne2 = DT == PA_BF16 ? 0x3F803F80u : 0x3C003C00u;  // two 1.0s of the KV type
   const uint4 ones = make_uint4(kOne2, kOne2, kOne2, kOne2);
   auto pass = [&](auto masked, int buf, int r0, int t0) __attribute__((always_inline)) {
@@ -303,13 +312,14 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
       }
     }
     // Scores of the lane's eight k-slots (k-slot e of lane group G is token
-    // 16*(e/4) + 4G + e%4 of the pass), masked past each row's limit.  Each
-    // lane checks its own scores against the reference; only when some lane
-    // of the wave sees growth past the slack are the rows' maxima gathered
-    // across the four lane groups and the accumulators rescaled.
-    float x[NC][8];
-    float lm[NC];
-    bool grow = false;
+    // 16*(e/4) + 4G + e%4 of the pass), masked past each row's limit, and
+    // their weights 2^(x qs - m qs) against the rows' reference m.  Weights
+    // are >= 0, so their bit patterns order like unsigned integers: one
+    // integer max tells whether some weight of the lane passed 2^kSlack.
+    // Only then (rarely) are the rows' maxima gathered across the four lane
+    // groups, the accumulators rescaled and the weights recomputed.
+    float x[NC][8], p[NC][8];
+    uint32_t pbits = 0;
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
 #pragma unroll
@@ -317,36 +327,37 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
         x[n][e] = sc[n][e >> 2][e & 3];
         if constexpr (kMasked)
           if (t0 + 16 * (e >> 2) + 4 * G + (e & 3) > lim[n]) x[n][e] = -__builtin_huge_valf();
+        // a masked score is -inf: 2^-inf = 0 (with a zero scale 0 * -inf
+        // would be NaN, hence the select)
+        p[n][e] = fast_exp2(fmaf(x[n][e], qs, moff[n]));
+        if constexpr (kMasked) p[n][e] = x[n][e] == -__builtin_huge_valf() ? 0.f : p[n][e];
+        pbits = max(pbits, __float_as_uint(p[n][e]));
       }
-      lm[n] = fmaxf(fmaxf(fmaxf(x[n][0], x[n][1]), fmaxf(x[n][2], x[n][3])),
-                    fmaxf(fmaxf(x[n][4], x[n][5]), fmaxf(x[n][6], x[n][7])));
-      grow |= (lm[n] - m_run[n]) * qs > kSlack;
     }
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    if (__builtin_amdgcn_ballot_w64(pbits > kSlackBits) != 0) {
 #pragma unroll
       for (int n = 0; n < NC; ++n) {
-        const float mn = fmaxf(m_run[n], max_groups(lm[n], x16, x32));
+        const float lm = fmaxf(fmaxf(fmaxf(x[n][0], x[n][1]), fmaxf(x[n][2], x[n][3])),
+                               fmaxf(fmaxf(x[n][4], x[n][5]), fmaxf(x[n][6], x[n][7])));
+        const float mn = fmaxf(m_run[n], max_groups(lm, x16, x32));
         const float alpha = fast_exp2((m_run[n] - mn) * qs);
         m_run[n] = mn;
+        moff[n] = -mn * qs;
         l_acc[n] *= alpha;
 #pragma unroll
         for (int u = 0; u < DPL; ++u) acc[n][u] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[n][e] = fast_exp2(fmaf(x[n][e], qs, moff[n]));
+          if constexpr (kMasked) p[n][e] = x[n][e] == -__builtin_huge_valf() ? 0.f : p[n][e];
+        }
       }
     }
     uint4 pb[NC];
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
-      const float moff = -m_run[n] * qs;
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // a masked score is -inf: 2^-inf = 0 (with a zero scale 0 * -inf
-        // would be NaN, hence the select)
-        p[e] = fast_exp2(fmaf(x[n][e], qs, moff));
-        if constexpr (kMasked) p[e] = x[n][e] == -__builtin_huge_valf() ? 0.f : p[e];
-      }
-      pb[n] = make_uint4(pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3]), pack2<DT>(p[4], p[5]),
-                         pack2<DT>(p[6], p[7]));
+      pb[n] = make_uint4(pack2<DT>(p[n][0], p[n][1]), pack2<DT>(p[n][2], p[n][3]), pack2<DT>(p[n][4], p[n][5]),
+                         pack2<DT>(p[n][6], p[n][7]));
       // row sums of the rounded weights: an all-ones A operand
       l_acc[n] = mfma32<DT>(ones, pb[n], l_acc[n]);
     }

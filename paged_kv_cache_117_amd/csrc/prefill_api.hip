@@ -98,6 +98,10 @@ extern "C" pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, 
     return fail(PA_ERR_SHAPE, "pa_prefill: max_context_len %d outside [0, max_blocks_per_seq*block_size = %lld]",
                 max_context_len, (long long)max_blocks_per_seq * block_size);
   if (partition_size < 0) return fail(PA_ERR_SHAPE, "pa_prefill: partition_size %d < 0", partition_size);
+  // (the kernels address a slot as block id * block bytes + a 32-bit offset)
+  if ((int64_t)num_kv_heads * head_dim * block_size * 4 > 0xffffffffLL)
+    return fail(PA_ERR_SHAPE, "pa_prefill: a block of %d KV heads x %d slots x %d dims is too large", num_kv_heads,
+                block_size, head_dim);
   if ((int64_t)num_tokens * num_q_heads * head_dim > 0x7fffffffffffLL)
     return fail(PA_ERR_SHAPE, "pa_prefill: %d tokens of %d heads is too large", num_tokens, num_q_heads);
   if (!isfinite(scale)) return fail(PA_ERR_SHAPE, "pa_prefill: scale is not finite");
