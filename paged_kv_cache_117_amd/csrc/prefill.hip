@@ -109,7 +109,7 @@ __device__ void nan_rows(void* out, int r0, int r1, int Hq, int h0, int nh, int 
 
 template <int DT, int D, int NC>
 __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
-  constexpr int ROW = D + 8;                 // LDS row stride, elements (16 bytes of padding)
+  constexpr int ROW = D;                     // LDS row of K, elements (16-byte chunks XOR-swizzled)
   constexpr int KS = D / 32;                 // QK k-steps over the head dim
   constexpr int DPL = D / 16;                // output dims per lane per row = PV MFMAs per column group
   constexpr int CH = D / 8;                  // 16-byte chunks per token row
@@ -119,13 +119,25 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   constexpr int R = kWaves * 16 * NC;        // rows per workgroup
   static_assert(PAIRS >= 1 && kStep * CH % 512 == 0, "token pairs must split evenly over the threads");
   static_assert(8 % DPL == 0, "a 16-byte chunk's dims map to whole V^T rows");
+  static_assert(D == 64 || D == 128, "the swizzle keys were measured for these row lengths");
+  auto kkey = [](int r) { return r & (D / 8 - 1); };
 
+  // LDS layout of K: the score reads have lane (G, c) read 16-byte chunk
+  // G + 4k of row c (mod 16).  A 16-byte read takes 4 LDS cycles per
+  // wavefront when its lanes do not conflict.  Chosen by measuring the
+  // bank-conflict counter for these exact lane patterns on gfx950: rows
+  // padded to 272 bytes measured 8 cycles (two-way conflicts); unpadded
+  // rows with chunk j of row r stored at chunk j ^ kkey(r),
+  // kkey(r) = r mod (D / 8), measured 4, and so do the stash writes (lane =
+  // chunk of one token row).
   __shared__ __align__(16) uint16_t sK[2][kStep][ROW];
   // V transposed for the PV A operand: row (pass, u * 16 + c) holds head dim
   // DPL * c + u of the pass's 32 positions in k-slot order (slot 8G + e is
   // token 16 (e / 4) + 4G + e % 4), so lane (G, c) reads its operand for
-  // output tile u as one 16-byte row segment.  Rows are 80 bytes: 16
-  // consecutive rows hit 16 distinct 16-byte bank groups.
+  // output tile u as one 16-byte chunk.  Rows are 80 bytes: the stash's
+  // 4-byte writes (16 lanes, 16 consecutive rows, one column) then hit 16
+  // distinct banks; the 16-byte reads measure two-way conflicts, which
+  // costs less here than a 64-byte swizzled row whose writes conflict.
   __shared__ __align__(16) uint16_t sV[2][kPairs * D][VROW];
   __shared__ int s_bad;
 
@@ -255,8 +267,8 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
     for (int m = 0; m < PAIRS; ++m) {
       const int it = tid + 256 * m;
       const int tp = it / CH, ch = it - tp * CH;
-      *reinterpret_cast<u32x4*>(&sK[buf][2 * tp][ch * 8]) = kreg[2 * m];
-      *reinterpret_cast<u32x4*>(&sK[buf][2 * tp + 1][ch * 8]) = kreg[2 * m + 1];
+      *reinterpret_cast<u32x4*>(&sK[buf][2 * tp][(ch ^ kkey(2 * tp)) * 8]) = kreg[2 * m];
+      *reinterpret_cast<u32x4*>(&sK[buf][2 * tp + 1][(ch ^ kkey(2 * tp + 1)) * 8]) = kreg[2 * m + 1];
       // V^T: the pair's values of each of the chunk's 8 dims, packed into
       // one word (token 2 tp in the low half) at k-slot sg, sg + 1.  Dim
       // dd = 8 ch + i goes to row pp D + (dd % DPL) 16 + dd / DPL, which
@@ -306,7 +318,7 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(&sK[buf][r0 + 16 * half + c][32 * k + 8 * G]);
+        const uint4 ka = *reinterpret_cast<const uint4*>(&sK[buf][r0 + 16 * half + c][((4 * k + G) ^ kkey(c)) * 8]);
 #pragma unroll
         for (int n = 0; n < NC; ++n) sc[n][half] = mfma32<DT>(ka, qr[n][k], sc[n][half]);
       }
