@@ -200,6 +200,22 @@ def pmc_summary(args):
     print(json.dumps(rec))
 
 
+def kv_utilization(bm, seq_ids, tables, block_size, num_blocks):
+    """KV-cache utilisation after the host step: filled slots / slots of the
+    blocks in use (a block shared by several sequences counts once, filled
+    as far as its fullest holder), and blocks in use / pool blocks."""
+    fill = {}
+    for s, sid in enumerate(seq_ids):
+        L = bm.num_tokens(int(sid))
+        row = tables[s]
+        for j in range(-(-L // block_size)):
+            b = int(row[j])
+            fill[b] = max(fill.get(b, 0), min(block_size, L - j * block_size))
+    in_use = num_blocks - bm.num_free()
+    return {"kv_slot_utilization": round(sum(fill.values()) / max(1, in_use * block_size), 4),
+            "kv_blocks_in_use_frac": round(in_use / num_blocks, 4)}
+
+
 def cpu_info():
     model = "unknown"
     try:
@@ -346,6 +362,7 @@ def main_prefill(args):
     slots = np.asarray(slots, dtype=np.int64)
     tables = bm.tables(w.seq_ids, w.max_blocks_per_seq)
     host_bm_ms = (time.perf_counter() - t0) * 1e3
+    kv_util = kv_utilization(bm, w.seq_ids, tables, w.block_size, w.num_blocks)
 
     def dev(a, kv=False):
         a = np.ascontiguousarray(a)
@@ -442,6 +459,7 @@ def main_prefill(args):
         "prefill_ms_median": round(float(np.median(pf_ms)), 5),
         "prefill_io_gbps": round(io / (pf_avg * 1e-3) / 1e9, 2),
         "host_block_manager_ms": round(host_bm_ms, 3),
+        **kv_util,
         "wall_s": round(wall, 3),
         "roofline": {
             "kernel": "pa_prefill",
@@ -661,6 +679,7 @@ def main():
     pairs = bm.take_copies_array()
     tables = bm.tables(w.seq_ids, w.max_blocks_per_seq)
     host_bm_ms = (time.perf_counter() - t0) * 1e3
+    kv_util = kv_utilization(bm, w.seq_ids, tables, w.block_size, w.num_blocks)
 
     # ---- device buffers: R rotating sets, each a private region of one pool --------
     nb = w.num_blocks
@@ -773,6 +792,7 @@ def main():
         "device_copy_gbps": None,
         "decode_frac_of_copy": None,
         "host_block_manager_ms": round(host_bm_ms, 3),
+        **kv_util,
         "wall_s": round(wall, 3),
         "roofline": {
             "kernel": "pa_decode",

@@ -27,3 +27,26 @@ def test_poison_keeps_exactly_the_cached_positions():
     # the slot the step writes is poisoned
     for slot in st.slots:
         assert not kept[slot // 16, slot % 16]
+
+
+def test_bench_kv_utilization_counts_shared_blocks_once():
+    """The bench's utilisation figure: filled slots over slots of blocks in
+    use, a shared block counted once.  Sequence 0 has 20 tokens (blocks
+    A: 16, B: 4); its fork shares A and B, then appends 1 token, which copies
+    B (count 2) into C and writes there (5 filled).  In use: A, B, C of 8."""
+    import os
+    import sys
+
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+
+    bm = pa.BlockManager(8, 16)
+    bm.add_seq(0)
+    bm.append(0, 20)
+    bm.fork(0, 1)
+    bm.append(1, 1)
+    bm.take_copies()
+    tables = bm.tables([0, 1], 4)
+    u = bench.kv_utilization(bm, [0, 1], tables, 16, 8)
+    assert u["kv_blocks_in_use_frac"] == 3 / 8
+    assert u["kv_slot_utilization"] == round((16 + 4 + 5) / 48, 4)
