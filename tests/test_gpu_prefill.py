@@ -55,7 +55,7 @@ def test_tiny_fp16_every_row():
 
 # (g, D, dtype): group sizes that fill 16-row columns in different ways
 SHAPES = [(1, 128, "fp16"), (2, 64, "bf16"), (4, 128, "bf16"), (5, 64, "fp16"), (8, 128, "fp16"),
-          (16, 64, "bf16"), (3, 128, "bf16")]
+          (16, 64, "bf16"), (3, 128, "bf16"), (32, 128, "bf16")]
 
 
 @pytest.mark.parametrize("g,D,dtype", SHAPES)
@@ -90,7 +90,7 @@ def _sampled(w, nrand=8, seed=0):
     return np.unique(np.asarray(rows))
 
 
-@pytest.mark.parametrize("key", ["p1", "p2", "p3"])
+@pytest.mark.parametrize("key", ["p1", "p2", "p3", "p4"])
 def test_full_size_sampled_rows(key):
     w = make_prefill_workload(key)
     print(f"case {key}", flush=True)
