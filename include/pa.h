@@ -192,6 +192,21 @@ pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, const void*
                        int max_context_len, int partition_size, float scale, pa_dtype_t dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_time_next_main_kernel -- timing hook (instrumentation, not part of the
+ * pages' method).  The next pa_decode or pa_prefill call that launches
+ * kernels records `start_event` on its stream right before its main kernel
+ * and `stop_event` right after it, ahead of any merge kernel, and then drops
+ * the request; hipEventElapsedTime of the pair is that kernel's duration.
+ *   start_event, stop_event  hipEvent_t handles created by the caller (not
+ *                            owned by the library); both NULL cancels a
+ *                            pending request; exactly one NULL returns
+ *                            PA_ERR_NULL
+ * One pending request per process (the last call wins); a call that fails
+ * its argument checks leaves the request pending.
+ */
+pa_status_t pa_time_next_main_kernel(void* start_event, void* stop_event);
+
 /* Bytes of workspace pa_prefill needs for these sizes (0 when the launch is
  * not split); depends on sizes only, not on the device or the dtype.
  * Returns 0 for invalid sizes as well; pa_prefill reports those. */

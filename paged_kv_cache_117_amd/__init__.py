@@ -24,5 +24,6 @@ from .ops import (  # noqa: F401
     prefill,
     prefill_workspace_bytes,
     swap_blocks,
+    time_next_main_kernel,
     write_kv,
 )

@@ -186,11 +186,20 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
   }
 
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  void *ev0, *ev1;
+  take_main_kernel_events(&ev0, &ev1);
+  if (ev0 && hipEventRecord(static_cast<hipEvent_t>(ev0), st) != hipSuccess)
+    return fail(PA_ERR_LAUNCH, "pa_decode: recording the timing start event failed");
   if (mfma)
     launch_decode_mfma(a, st);
   else
     launch_decode_valu(a, st);
-  if (!a.stream && a.entries > 1) launch_decode_reduce(a, st);
+  if (ev1 && hipEventRecord(static_cast<hipEvent_t>(ev1), st) != hipSuccess)
+    return fail(PA_ERR_LAUNCH, "pa_decode: recording the timing stop event failed");
+  if (a.stream)
+    launch_decode_stream_reduce(a, st);
+  else if (a.entries > 1)
+    launch_decode_reduce(a, st);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "pa_decode: launch failed: %s", hipGetErrorString(e));
   return PA_OK;

@@ -84,7 +84,8 @@ inline StreamLayout stream_layout(size_t B, size_t Hq, size_t Hkv, size_t D) {
 
 // Partition kernels (the reduce is launched separately when P > 1).
 void launch_decode_valu(const DecodeArgs& a, hipStream_t st);   // any dtype
-void launch_decode_mfma(const DecodeArgs& a, hipStream_t st);   // fp16 / bf16; the balanced split launches its own reduce
+void launch_decode_mfma(const DecodeArgs& a, hipStream_t st);   // fp16 / bf16, main kernel only
 void launch_decode_reduce(const DecodeArgs& a, hipStream_t st);
+void launch_decode_stream_reduce(const DecodeArgs& a, hipStream_t st);  // the balanced split's merge
 
 }  // namespace pa

@@ -1041,8 +1041,6 @@ void launch(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((decode_stream<DT, D, GMAX>), dim3(a.grid), dim3(256), 0, st, a.out, a.q, a.kp, a.vp, a.bt, a.cl,
                        a.ws_o, a.ws_m, a.ws_l, a.info, a.B, a.Hq, a.Hkv, a.g, a.nsub, a.num_blocks, a.maxb, a.max_ctx,
                        a.qscale, a.unit, a.lm);
-    hipLaunchKernelGGL((decode_stream_reduce<DT, D, GMAX>), dim3(a.Hkv * a.nsub, a.B), dim3(256), 0, st, a.out,
-                       a.ws_o, a.ws_m, a.ws_l, a.info, a.Hq, a.g, a.nsub);
     return;
   }
   const unsigned grid = (unsigned)a.entries * a.Hkv * a.nsub * a.B;
@@ -1056,30 +1054,43 @@ void launch(const DecodeArgs& a, hipStream_t st) {
                        a.qscale, a.psize, a.entries, a.lm);
 }
 
-template <int DT, int D>
+template <int DT, int D, int GMAX>
+void launch_merge(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((decode_stream_reduce<DT, D, GMAX>), dim3(a.Hkv * a.nsub, a.B), dim3(256), 0, st, a.out, a.ws_o,
+                     a.ws_m, a.ws_l, a.info, a.Hq, a.g, a.nsub);
+}
+
+template <int DT, int D, bool kMerge>
 void launch_g(const DecodeArgs& a, hipStream_t st) {
   switch (a.gmax) {
-    case 4: launch<DT, D, 4>(a, st); break;
-    case 8: launch<DT, D, 8>(a, st); break;
-    default: launch<DT, D, 16>(a, st); break;
+    case 4: kMerge ? launch_merge<DT, D, 4>(a, st) : launch<DT, D, 4>(a, st); break;
+    case 8: kMerge ? launch_merge<DT, D, 8>(a, st) : launch<DT, D, 8>(a, st); break;
+    default: kMerge ? launch_merge<DT, D, 16>(a, st) : launch<DT, D, 16>(a, st); break;
   }
 }
 
-template <int DT>
+template <int DT, bool kMerge>
 void launch_d(const DecodeArgs& a, hipStream_t st) {
   if (a.D == 64)
-    launch_g<DT, 64>(a, st);
+    launch_g<DT, 64, kMerge>(a, st);
   else
-    launch_g<DT, 128>(a, st);
+    launch_g<DT, 128, kMerge>(a, st);
 }
 
 }  // namespace
 
 void launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
   if (a.dtype == PA_FP16)
-    launch_d<PA_FP16>(a, st);
+    launch_d<PA_FP16, false>(a, st);
   else
-    launch_d<PA_BF16>(a, st);
+    launch_d<PA_BF16, false>(a, st);
+}
+
+void launch_decode_stream_reduce(const DecodeArgs& a, hipStream_t st) {
+  if (a.dtype == PA_FP16)
+    launch_d<PA_FP16, true>(a, st);
+  else
+    launch_d<PA_BF16, true>(a, st);
 }
 
 }  // namespace pa

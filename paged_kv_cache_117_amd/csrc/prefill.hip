@@ -525,29 +525,37 @@ __global__ __launch_bounds__(256) void prefill_reduce(PrefillArgs a) {
   *reinterpret_cast<uint2*>(reinterpret_cast<char*>(a.out) + (row * D + d) * 2) = make_uint2(v.x, v.y);
 }
 
-template <int DT, int D>
+template <int DT, int D, bool kMerge>
 void launch_nc(const PrefillArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC>), dim3(a.grid), dim3(256), 0, st, a);
   constexpr int HPB = 256 / (D / 4);
-  if (a.P > 1)
+  if (!kMerge)
+    hipLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC>), dim3(a.grid), dim3(256), 0, st, a);
+  else if (a.P > 1)
     hipLaunchKernelGGL((prefill_reduce<DT, D>), dim3(a.N, (a.Hq + HPB - 1) / HPB), dim3(256), 0, st, a);
 }
 
-template <int DT>
+template <int DT, bool kMerge>
 void launch_d(const PrefillArgs& a, hipStream_t st) {
   if (a.D == 64)
-    launch_nc<DT, 64>(a, st);
+    launch_nc<DT, 64, kMerge>(a, st);
   else
-    launch_nc<DT, 128>(a, st);
+    launch_nc<DT, 128, kMerge>(a, st);
 }
 
 }  // namespace
 
 void launch_prefill_mfma(const PrefillArgs& a, hipStream_t st) {
   if (a.dtype == PA_FP16)
-    launch_d<PA_FP16>(a, st);
+    launch_d<PA_FP16, false>(a, st);
   else
-    launch_d<PA_BF16>(a, st);
+    launch_d<PA_BF16, false>(a, st);
+}
+
+void launch_prefill_reduce(const PrefillArgs& a, hipStream_t st) {
+  if (a.dtype == PA_FP16)
+    launch_d<PA_FP16, true>(a, st);
+  else
+    launch_d<PA_BF16, true>(a, st);
 }
 
 }  // namespace pa

@@ -153,7 +153,14 @@ extern "C" pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, 
     if ((int64_t)num_tokens * num_kv_heads * d.nsub > 0x7fffffffLL)
       return fail(PA_ERR_SHAPE, "pa_prefill: launch of %lld workgroups is too large",
                   (long long)num_tokens * num_kv_heads * d.nsub);
-    launch_decode_valu(d, static_cast<hipStream_t>(stream));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    void *ev0, *ev1;
+    take_main_kernel_events(&ev0, &ev1);
+    if (ev0 && hipEventRecord(static_cast<hipEvent_t>(ev0), st) != hipSuccess)
+      return fail(PA_ERR_LAUNCH, "pa_prefill: recording the timing start event failed");
+    launch_decode_valu(d, st);
+    if (ev1 && hipEventRecord(static_cast<hipEvent_t>(ev1), st) != hipSuccess)
+      return fail(PA_ERR_LAUNCH, "pa_prefill: recording the timing stop event failed");
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "pa_prefill: launch failed: %s", hipGetErrorString(e));
     return PA_OK;
@@ -198,7 +205,15 @@ extern "C" pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, 
     return fail(PA_ERR_SHAPE, "pa_prefill: launch of %lld workgroups is too large", (long long)grid);
   a.tiles = (int)tiles;
   a.grid = (int)grid;
-  launch_prefill_mfma(a, static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  void *ev0, *ev1;
+  take_main_kernel_events(&ev0, &ev1);
+  if (ev0 && hipEventRecord(static_cast<hipEvent_t>(ev0), st) != hipSuccess)
+    return fail(PA_ERR_LAUNCH, "pa_prefill: recording the timing start event failed");
+  launch_prefill_mfma(a, st);
+  if (ev1 && hipEventRecord(static_cast<hipEvent_t>(ev1), st) != hipSuccess)
+    return fail(PA_ERR_LAUNCH, "pa_prefill: recording the timing stop event failed");
+  launch_prefill_reduce(a, st);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "pa_prefill: launch failed: %s", hipGetErrorString(e));
   return PA_OK;

@@ -57,6 +57,7 @@ inline PrefillWorkspace prefill_workspace(size_t N, size_t Hq, size_t D, size_t 
   return w;
 }
 
-void launch_prefill_mfma(const PrefillArgs& a, hipStream_t st);  // fp16 / bf16; + the merge when P > 1
+void launch_prefill_mfma(const PrefillArgs& a, hipStream_t st);    // fp16 / bf16, main kernel only
+void launch_prefill_reduce(const PrefillArgs& a, hipStream_t st);  // the merge (nothing when P == 1)
 
 }  // namespace pa

@@ -233,5 +233,23 @@ def abi_version() -> int:
     return int(LIB.pa_abi_version())
 
 
+def time_next_main_kernel(start, stop) -> None:
+    """pa_time_next_main_kernel: the next decode / prefill call records the
+    two torch.cuda.Event objects (timing enabled) right around its main
+    kernel; ``start.elapsed_time(stop)`` is then that kernel's duration.
+    None, None cancels a pending request."""
+    if start is None and stop is None:
+        check_status(LIB.pa_time_next_main_kernel(None, None), "pa_time_next_main_kernel")
+        return
+    handles = []
+    for ev in (start, stop):
+        if not isinstance(ev, torch.cuda.Event):
+            raise TypeError("start and stop must be torch.cuda.Event objects")
+        if not ev.cuda_event:
+            ev.record()  # torch creates the underlying event on its first record
+        handles.append(ev.cuda_event)
+    check_status(LIB.pa_time_next_main_kernel(handles[0], handles[1]), "pa_time_next_main_kernel")
+
+
 def _as_ptr(arr, ctype):
     return arr.ctypes.data_as(ctypes.POINTER(ctype))

@@ -176,3 +176,13 @@ def test_prefill_workspace_bytes():
     rows = 256 * 32 * 32
     assert pa.prefill_workspace_bytes(4, 256, 32, 8, 128, 64, 32768, 1000) == _al(rows * 128 * 4) + 2 * _al(rows * 4)
     assert pa.prefill_workspace_bytes(0, 256, 32, 8, 128, 64, 32768, 0) == 0
+
+
+def test_time_next_main_kernel_argument_rules():
+    # one event without the other is refused; none cancels (nothing is launched here)
+    assert L.pa_time_next_main_kernel(None, 12345) == 1  # PA_ERR_NULL
+    assert b"both" in L.pa_last_error()
+    assert L.pa_time_next_main_kernel(None, None) == 0
+    pa.time_next_main_kernel(None, None)
+    with pytest.raises(TypeError):
+        pa.time_next_main_kernel(1, 2)

@@ -313,3 +313,29 @@ def test_stream_query_groups_of_32_heads():
     segments per KV head in the split)."""
     w = make_custom("g32", "fp16", [1, 700, 2049, 33], 64, 2, 128, seed=39)
     check(w)
+
+
+def test_main_kernel_timing_hook_is_inside_the_call_and_one_shot():
+    """pa_time_next_main_kernel: the events bracket the main kernel of the
+    next call only (within the whole call's own event pair), and a later
+    call leaves them alone."""
+    w = make_custom("timing", "bf16", [700, 2000, 33, 4096], 32, 8, 128, seed=41)
+    g = GpuStep(w)
+    g.run()
+    torch.cuda.synchronize()
+    call = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    kern = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    call[0].record()
+    pa.time_next_main_kernel(kern[0], kern[1])
+    out = g.run()
+    call[1].record()
+    torch.cuda.synchronize()
+    t_call, t_kern = call[0].elapsed_time(call[1]), kern[0].elapsed_time(kern[1])
+    assert 0.0 < t_kern <= t_call
+    assert call[0].elapsed_time(kern[0]) >= 0.0 and kern[1].elapsed_time(call[1]) >= 0.0
+    # one-shot: another call does not move the events
+    g.run()
+    torch.cuda.synchronize()
+    assert kern[0].elapsed_time(kern[1]) == t_kern
+    _, _, _, want = oracle_step(w)
+    assert max_err(to_f64(out, "bf16"), want) <= TOL["bf16"]
