@@ -37,6 +37,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["paged_kv_cache_117_amd/csrc/decode_mfma.hip", "paged_kv_cache_117_amd/csrc/decode.hip",
                   "paged_kv_cache_117_amd/csrc/decode_api.hip", "paged_kv_cache_117_amd/build_lib.py"]
 METRIC = "paged decode attention KV-read GB/s (% of MI355X HBM peak); seq-steps/s"
+WARMUP_SECONDS = 0.2  # default warmup: GPU work before timing, for settled clocks
 # partition size a workload states (positions per partition); others use the automatic split
 WORKLOAD_PARTITION = {"c5": 512}
 WORKLOAD_NAMES = {
@@ -82,7 +83,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps (default: at least 10, and at least %.1f s of GPU work, "
+                         "so that clocks have settled)" % WARMUP_SECONDS)
     ap.add_argument("--config", default="c2",
                     choices=sorted(WORKLOAD_NAMES) + sorted(PREFILL_NAMES) + sorted(SWAP_NAMES) + sorted(HOST_NAMES))
     ap.add_argument("--partition-size", type=int, default=None,
@@ -226,6 +229,27 @@ def timing_events(torch, n, stream):
         a.record(stream)
         b.record(stream)
     return evs, kevs
+
+
+def warm_up(torch, step, n=None):
+    """Untimed steps before the timed region: exactly `n` when given, else at
+    least 10 and at least WARMUP_SECONDS of GPU work (the GPU raises its
+    clocks over the first tens of milliseconds of sustained load; a short
+    warmup times part of that ramp).  Returns the number of steps run."""
+    i = 0
+    if n is not None:
+        for i in range(n):
+            step(i)
+        torch.cuda.synchronize()
+        return n
+    t0 = time.perf_counter()
+    while True:
+        step(i)
+        i += 1
+        if i >= 10 and i % 10 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= WARMUP_SECONDS:
+                return i
 
 
 def main_kernel_pass(torch, step, steps, R, kevs):
@@ -433,9 +457,7 @@ def main_prefill(args):
         if ev is not None:
             ev[1].record(stream)
 
-    for i in range(args.warmup):
-        step(i % R)
-    torch.cuda.synchronize()
+    args.warmup = warm_up(torch, lambda i: step(i % R), args.warmup)
     evs, kevs = timing_events(torch, args.steps, stream)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -540,9 +562,7 @@ def main_swap(args):
         if ev is not None:
             ev[2].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    args.warmup = warm_up(torch, lambda i: step(), args.warmup)
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -764,9 +784,7 @@ def main():
         if ev is not None:
             ev[1].record(stream)
 
-    for i in range(args.warmup):
-        step(i % R)
-    torch.cuda.synchronize()
+    args.warmup = warm_up(torch, lambda i: step(i % R), args.warmup)
     evs, kevs = timing_events(torch, args.steps, stream)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
