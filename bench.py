@@ -254,11 +254,10 @@ def warm_up(torch, step, n=None):
 
 def main_kernel_pass(torch, step, steps, R, kevs):
     """The main kernel's mean duration (ms) over `steps` more steps of the
-    same work, each with the library recording `kevs[i]` right around that
-    kernel.  A pass of its own: a timing event inside the call costs the GPU a
-    few microseconds, so the timed region above carries none, and this
-    figure includes one event's overhead (it reads slightly above the
-    rocprofv3 kernel average)."""
+    same work, the library handing `kevs[i]` to that kernel's launch so they
+    take its own start and end (agreeing with the rocprofv3 kernel average).
+    A pass of its own: events attached to a launch slow the whole call by a
+    few microseconds, so the timed region above carries none."""
     torch.cuda.synchronize()
     for i in range(steps):
         step(i % R, None, kevs[i])

@@ -195,9 +195,10 @@ pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, const void*
 /*
  * pa_time_next_main_kernel -- timing hook (instrumentation, not part of the
  * pages' method).  The next pa_decode or pa_prefill call that launches
- * kernels records `start_event` on its stream right before its main kernel
- * and `stop_event` right after it, ahead of any merge kernel, and then drops
- * the request; hipEventElapsedTime of the pair is that kernel's duration.
+ * kernels hands the two events to the launch of its main kernel
+ * (hipExtLaunchKernel), so they take that kernel's start and end and not
+ * those of any merge kernel after it, and then drops the request;
+ * hipEventElapsedTime of the pair is the main kernel's duration.
  *   start_event, stop_event  hipEvent_t handles created by the caller (not
  *                            owned by the library); both NULL cancels a
  *                            pending request; exactly one NULL returns

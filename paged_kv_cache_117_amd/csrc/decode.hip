@@ -22,6 +22,7 @@
 // The arithmetic order depends only on logical positions (block j of the
 // sequence, slot within the block), never on physical block ids, so any
 // placement of the same logical cache gives bit-identical results.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -293,7 +294,8 @@ namespace {
 template <int DT, int D, int GMAX>
 void launch_valu(const DecodeArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)a.P * a.Hkv * a.nsub * a.B;
-  hipLaunchKernelGGL((decode_part_valu<DT, D, GMAX>), dim3(grid), dim3(64), 0, st, a.out, a.q, a.kp, a.vp, a.bt,
+  hipExtLaunchKernelGGL((decode_part_valu<DT, D, GMAX>), dim3(grid), dim3(64), 0, st,
+                        static_cast<hipEvent_t>(a.ev_start), static_cast<hipEvent_t>(a.ev_stop), 0, a.out, a.q, a.kp, a.vp, a.bt,
                      a.cl, a.ws_o, a.ws_m, a.ws_l, a.B, a.Hq, a.Hkv, a.g, a.nsub, a.num_blocks, a.maxb, a.max_ctx,
                      a.qscale, a.psize, a.P, a.lm, a.qst, a.nseq, a.max_q);
 }

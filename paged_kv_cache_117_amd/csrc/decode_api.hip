@@ -186,16 +186,11 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
   }
 
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  void *ev0, *ev1;
-  take_main_kernel_events(&ev0, &ev1);
-  if (ev0 && hipEventRecord(static_cast<hipEvent_t>(ev0), st) != hipSuccess)
-    return fail(PA_ERR_LAUNCH, "pa_decode: recording the timing start event failed");
+  take_main_kernel_events(&a.ev_start, &a.ev_stop);
   if (mfma)
     launch_decode_mfma(a, st);
   else
     launch_decode_valu(a, st);
-  if (ev1 && hipEventRecord(static_cast<hipEvent_t>(ev1), st) != hipSuccess)
-    return fail(PA_ERR_LAUNCH, "pa_decode: recording the timing stop event failed");
   if (a.stream)
     launch_decode_stream_reduce(a, st);
   else if (a.entries > 1)

@@ -35,6 +35,10 @@ struct DecodeArgs {
   // KV).  B is then the number of query tokens, qst the [nseq + 1] row starts.
   const int32_t* qst;
   int nseq, max_q;
+  // Caller's timing events for the main kernel (hipEvent_t, or NULL): passed
+  // to its launch, so they take the kernel's own start and end.
+  void* ev_start;
+  void* ev_stop;
 };
 
 // Workspace: the partition partials, when some sequence spans more than one

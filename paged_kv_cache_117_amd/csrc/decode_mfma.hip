@@ -44,6 +44,7 @@
 // The partition kernels stage each wave's (m, l) and normalised rows in LDS
 // and write the workgroup's entry with the same log-sum-exp merge as the
 // reduce kernel.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -1035,21 +1036,24 @@ __global__ __launch_bounds__(256) void decode_stream_reduce(void* __restrict__ o
   }
 }
 
+// The main kernel's launch carries the caller's timing events (if any).
+#define EV(a) static_cast<hipEvent_t>((a).ev_start), static_cast<hipEvent_t>((a).ev_stop)
+
 template <int DT, int D, int GMAX>
 void launch(const DecodeArgs& a, hipStream_t st) {
   if (a.stream) {
-    hipLaunchKernelGGL((decode_stream<DT, D, GMAX>), dim3(a.grid), dim3(256), 0, st, a.out, a.q, a.kp, a.vp, a.bt, a.cl,
+    hipExtLaunchKernelGGL((decode_stream<DT, D, GMAX>), dim3(a.grid), dim3(256), 0, st, EV(a), 0, a.out, a.q, a.kp, a.vp, a.bt, a.cl,
                        a.ws_o, a.ws_m, a.ws_l, a.info, a.B, a.Hq, a.Hkv, a.g, a.nsub, a.num_blocks, a.maxb, a.max_ctx,
                        a.qscale, a.unit, a.lm);
     return;
   }
   const unsigned grid = (unsigned)a.entries * a.Hkv * a.nsub * a.B;
   if (a.wave_part)
-    hipLaunchKernelGGL((decode_part_wave<DT, D, GMAX>), dim3(grid), dim3(256), 0, st, a.out, a.q, a.kp, a.vp, a.bt,
+    hipExtLaunchKernelGGL((decode_part_wave<DT, D, GMAX>), dim3(grid), dim3(256), 0, st, EV(a), 0, a.out, a.q, a.kp, a.vp, a.bt,
                        a.cl, a.ws_o, a.ws_m, a.ws_l, a.B, a.Hq, a.Hkv, a.g, a.nsub, a.num_blocks, a.maxb, a.max_ctx,
                        a.qscale, a.psize, a.entries, a.lm);
   else
-    hipLaunchKernelGGL((decode_part_mfma<DT, D, GMAX>), dim3(grid), dim3(256), 0, st, a.out, a.q, a.kp, a.vp, a.bt,
+    hipExtLaunchKernelGGL((decode_part_mfma<DT, D, GMAX>), dim3(grid), dim3(256), 0, st, EV(a), 0, a.out, a.q, a.kp, a.vp, a.bt,
                        a.cl, a.ws_o, a.ws_m, a.ws_l, a.B, a.Hq, a.Hkv, a.g, a.nsub, a.num_blocks, a.maxb, a.max_ctx,
                        a.qscale, a.psize, a.entries, a.lm);
 }

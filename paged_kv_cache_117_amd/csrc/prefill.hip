@@ -40,6 +40,7 @@
 // workgroup's rows become NaN.  A sequence whose (T, L) cannot be served
 // (T > L, L past the table, T past max_query_len, bad row range) gets NaN
 // rows instead of a computed result.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -529,7 +530,8 @@ template <int DT, int D, bool kMerge>
 void launch_nc(const PrefillArgs& a, hipStream_t st) {
   constexpr int HPB = 256 / (D / 4);
   if (!kMerge)
-    hipLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC>), dim3(a.grid), dim3(256), 0, st, a);
+    hipExtLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC>), dim3(a.grid), dim3(256), 0, st,
+                          static_cast<hipEvent_t>(a.ev_start), static_cast<hipEvent_t>(a.ev_stop), 0, a);
   else if (a.P > 1)
     hipLaunchKernelGGL((prefill_reduce<DT, D>), dim3(a.N, (a.Hq + HPB - 1) / HPB), dim3(256), 0, st, a);
 }

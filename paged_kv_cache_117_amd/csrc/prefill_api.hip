@@ -154,13 +154,8 @@ extern "C" pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, 
       return fail(PA_ERR_SHAPE, "pa_prefill: launch of %lld workgroups is too large",
                   (long long)num_tokens * num_kv_heads * d.nsub);
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    void *ev0, *ev1;
-    take_main_kernel_events(&ev0, &ev1);
-    if (ev0 && hipEventRecord(static_cast<hipEvent_t>(ev0), st) != hipSuccess)
-      return fail(PA_ERR_LAUNCH, "pa_prefill: recording the timing start event failed");
+    take_main_kernel_events(&d.ev_start, &d.ev_stop);
     launch_decode_valu(d, st);
-    if (ev1 && hipEventRecord(static_cast<hipEvent_t>(ev1), st) != hipSuccess)
-      return fail(PA_ERR_LAUNCH, "pa_prefill: recording the timing stop event failed");
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "pa_prefill: launch failed: %s", hipGetErrorString(e));
     return PA_OK;
@@ -206,13 +201,8 @@ extern "C" pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, 
   a.tiles = (int)tiles;
   a.grid = (int)grid;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  void *ev0, *ev1;
-  take_main_kernel_events(&ev0, &ev1);
-  if (ev0 && hipEventRecord(static_cast<hipEvent_t>(ev0), st) != hipSuccess)
-    return fail(PA_ERR_LAUNCH, "pa_prefill: recording the timing start event failed");
+  take_main_kernel_events(&a.ev_start, &a.ev_stop);
   launch_prefill_mfma(a, st);
-  if (ev1 && hipEventRecord(static_cast<hipEvent_t>(ev1), st) != hipSuccess)
-    return fail(PA_ERR_LAUNCH, "pa_prefill: recording the timing stop event failed");
   launch_prefill_reduce(a, st);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "pa_prefill: launch failed: %s", hipGetErrorString(e));

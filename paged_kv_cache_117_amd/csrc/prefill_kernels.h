@@ -36,6 +36,8 @@ struct PrefillArgs {
   int lbs;        // log2(block_size)
   float qscale;   // |scale| * log2(e)
   pa_dtype_t dtype;
+  void* ev_start;  // caller's timing events for prefill_mfma (hipEvent_t, or NULL)
+  void* ev_stop;
 };
 
 // Positions per step of the prefill kernel (partitions are whole steps).
