@@ -38,6 +38,21 @@ KERNEL_SOURCES = ["paged_kv_cache_117_amd/csrc/decode_mfma.hip", "paged_kv_cache
                   "paged_kv_cache_117_amd/csrc/decode_api.hip", "paged_kv_cache_117_amd/build_lib.py"]
 METRIC = "paged decode attention KV-read GB/s (% of MI355X HBM peak); seq-steps/s"
 WARMUP_SECONDS = 0.2  # default warmup: GPU work before timing, for settled clocks
+# Layers of the models the decode workloads are shaped after (one layer is benchmarked); used only
+# to state the model's KV bytes per token next to the pages' sizing example.
+MODEL_LAYERS = {"c2": 32, "c3": 40, "c4": 32, "c4b": 32, "c5": 80}
+# Figures the source pages report, with the hardware they were measured on: context, not targets.
+PAGES_CONTEXT = {
+    "kv_memory_holding_tokens": "20.4-38.2% in the contiguous-slab servers profiled by the SOSP 2023 "
+                                "PagedAttention paper vs 96.3% with paged blocks, on NVIDIA A100 "
+                                "(PagedAttention: Virtual Memory for the KV Cache; PagedAttention and vLLM: "
+                                "Paging the KV Cache Like an OS)",
+    "serving_throughput": "2-4x over FasterTransformer and Orca at equal latency, NVIDIA A100 "
+                          "(Batching and PagedAttention)",
+    "kv_bytes_per_token_opt13b": "800 KB in FP16 (2 x 5120 hidden x 40 layers x 2 bytes); 1.6 GB for a "
+                                 "2048-token request; about 30% of a 40 GB A100 left for the KV cache next to "
+                                 "the 26 GB of weights (PagedAttention: Virtual Memory for the KV Cache)",
+}
 # partition size a workload states (positions per partition); others use the automatic split
 WORKLOAD_PARTITION = {"c5": 512}
 WORKLOAD_NAMES = {
@@ -849,6 +864,9 @@ def main():
         "decode_frac_of_copy": None,
         "host_block_manager_ms": round(host_bm_ms, 3),
         **kv_util,
+        "kv_bytes_per_token_model": (2 * w.num_kv_heads * w.head_dim * eb * MODEL_LAYERS[args.config]
+                                     if args.config in MODEL_LAYERS else None),
+        "pages_context": PAGES_CONTEXT,
         "wall_s": round(wall, 3),
         "roofline": {
             "kernel": "pa_decode main kernel (decode_stream for batches of up to 4096 sequences)",
