@@ -129,15 +129,30 @@ struct pa_bm {
       push_free(b);
   }
 
+  // SHA-256 of parent (32 zero bytes for a sequence's first block) || the
+  // block's tokens as int32 little-endian || extra key, hashed from one buffer.
   Digest chain_hash(const Digest* parent, const int32_t* toks, const std::string& extra) const {
-    pa::Sha256 s;
-    Digest zero{};
-    s.update(parent ? parent->data() : zero.data(), 32);
+    uint8_t small[32 + 4 * 64];
+    std::vector<uint8_t> big;
+    uint8_t* msg = small;
+    if (block_size > 64) {
+      big.resize(32 + 4 * (size_t)block_size);
+      msg = big.data();
+    }
+    if (parent)
+      std::memcpy(msg, parent->data(), 32);
+    else
+      std::memset(msg, 0, 32);
     for (int i = 0; i < block_size; ++i) {
       const uint32_t t = (uint32_t)toks[i];
-      const uint8_t le[4] = {(uint8_t)t, (uint8_t)(t >> 8), (uint8_t)(t >> 16), (uint8_t)(t >> 24)};
-      s.update(le, 4);
+      uint8_t* o = msg + 32 + 4 * i;
+      o[0] = (uint8_t)t;
+      o[1] = (uint8_t)(t >> 8);
+      o[2] = (uint8_t)(t >> 16);
+      o[3] = (uint8_t)(t >> 24);
     }
+    pa::Sha256 s;
+    s.update(msg, 32 + 4 * (size_t)block_size);
     s.update(extra.data(), extra.size());
     return s.finish();
   }

@@ -109,13 +109,12 @@ void Sha256::update(const void* data, size_t n) {
 }
 
 Digest Sha256::finish() {
+  // Padding: 0x80, zeros up to 56 bytes modulo 64, the bit length (big-endian).
   const uint64_t bits = bits_;
-  const uint8_t one = 0x80, zero = 0;
-  update(&one, 1);
-  while (fill_ != 56) update(&zero, 1);
-  uint8_t len[8];
-  for (int i = 0; i < 8; ++i) len[i] = (uint8_t)(bits >> (56 - 8 * i));
-  update(len, 8);
+  uint8_t pad[72] = {0x80};
+  const size_t nz = (fill_ < 56 ? 56 - fill_ : 120 - fill_);  // 0x80 plus zeros
+  for (int i = 0; i < 8; ++i) pad[nz + i] = (uint8_t)(bits >> (56 - 8 * i));
+  update(pad, nz + 8);
   Digest d;
   for (int i = 0; i < 8; ++i)
     for (int j = 0; j < 4; ++j) d[4 * i + j] = (uint8_t)(h_[i] >> (24 - 8 * j));
