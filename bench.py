@@ -267,6 +267,18 @@ def warm_up(torch, step, n=None):
                 return i
 
 
+def call_pass(torch, step, steps, R, evs):
+    """Durations (ms) of the library call alone over `steps` more steps of the
+    same work, with an event pair around each call.  A pass of its own: an
+    event recorded in the stream costs the GPU time, so the timed region
+    above holds nothing but the steps."""
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(i % R, evs[i])
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in evs])
+
+
 def main_kernel_pass(torch, step, steps, R, kevs):
     """The main kernel's mean duration (ms) over `steps` more steps of the
     same work, the library handing `kevs[i]` to that kernel's launch so they
@@ -479,12 +491,12 @@ def main_prefill(args):
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
-        step(i % R, evs[i])
+        step(i % R)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    pf_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    pf_ms = call_pass(torch, step, args.steps, R, evs)
     pf_avg = float(pf_ms.mean())
     kern_avg = main_kernel_pass(torch, step, args.steps, R, kevs)
     flops = metrics.prefill_flops(w.prior_lens, w.chunk_lens, w.num_q_heads, w.head_dim)
@@ -580,12 +592,16 @@ def main_swap(args):
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0.record(stream)
     for i in range(args.steps):
-        step(evs[i])
+        step()
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
+    for i in range(args.steps):  # the two directions apart: a pass of its own (events cost GPU time)
+        step(evs[i])
+    torch.cuda.synchronize()
     out_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in evs]))
     in_ms = float(np.mean([b.elapsed_time(c) for _, b, c in evs]))
     # reference: the DMA engines copying one contiguous buffer of the same size each way
@@ -806,12 +822,12 @@ def main():
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
-        step(i % R, evs[i])
+        step(i % R)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
-    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    dec_ms = call_pass(torch, step, args.steps, R, evs)
     kern_avg = main_kernel_pass(torch, step, args.steps, R, kevs)
     ms_step = total_ms / args.steps
 
