@@ -163,7 +163,7 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads
  *                    (row tiles of 128 query rows x KV heads x sequences)
  *                    over contexts longer than 512 positions is cut into
  *                    position partitions (at least 512 positions each) until
- *                    it has about 1024; > 0: always cut at that many
+ *                    it has about 512; > 0: always cut at that many
  *                    positions (rounded up to a multiple of 64).  Each
  *                    partition's rows carry an online-softmax partial and a
  *                    second kernel merges them with log-sum-exp weights, the

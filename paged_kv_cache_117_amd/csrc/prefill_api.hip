@@ -14,10 +14,13 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 // Automatic split: a launch of fewer than kFewGroups workgroups (row tiles
 // x KV heads x sequences) over contexts longer than kSplitMin positions is
-// cut into position partitions until it has about kTargetGroups workgroups,
-// each walking at least kSplitMin positions.  Only sizes enter the choice
-// (no device query), so the workspace size is known ahead of the call.
-constexpr int64_t kFewGroups = 512, kTargetGroups = 1024, kSplitMin = 512;
+// cut into position partitions until it has about kTargetGroups workgroups
+// -- one round of two resident workgroups on each of the 256 compute units;
+// a second round measured slower (64 new tokens after 24k-32k cached ones:
+// 666 TFLOP/s at 8 partitions, 543 at 16) -- each walking at least kSplitMin
+// positions.  Only sizes enter the choice (no device query), so the
+// workspace size is known ahead of the call.
+constexpr int64_t kFewGroups = 512, kTargetGroups = 512, kSplitMin = 512;
 
 struct Split {
   int P = 1, psteps = 0;

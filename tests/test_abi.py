@@ -169,8 +169,8 @@ def test_prefill_workspace_bytes():
     # unsplit launches need none: many workgroups, or short contexts
     assert pa.prefill_workspace_bytes(8, 4096, 32, 8, 128, 512, 3704, 0) == 0
     assert pa.prefill_workspace_bytes(4, 256, 32, 8, 128, 64, 500, 0) == 0
-    # a short chunk over a long context: 4 seqs x 8 heads x 2 tiles = 64 groups -> 16 partitions
-    rows = 256 * 32 * 16
+    # a short chunk over a long context: 4 seqs x 8 heads x 2 tiles = 64 groups -> 8 partitions
+    rows = 256 * 32 * 8
     assert pa.prefill_workspace_bytes(4, 256, 32, 8, 128, 64, 32768, 0) == _al(rows * 128 * 4) + 2 * _al(rows * 4)
     # a given partition size always splits: ceil(32768 / 1024) = 32 partitions
     rows = 256 * 32 * 32
