@@ -93,7 +93,7 @@ typedef enum {
  *   q                device, [num_seqs][num_q_heads][head_dim], dtype
  *   k_pool, v_pool   device, [num_blocks][num_kv_heads][block_size][head_dim], dtype
  *   block_tables     device, int32 [num_seqs][max_blocks_per_seq]; entries at
- *                    index >= ceil(L/16) are never read
+ *                    index >= ceil(L/block_size) are never read
  *   context_lens     device, int32 [num_seqs]; 0 <= L <= max_context_len
  *                    (L = 0 writes a zero row)
  *   max_context_len  host hint >= every context_lens[s]; sizes the launch;
@@ -109,6 +109,13 @@ typedef enum {
  * 2^k of them per block; 8 returns PA_ERR_UNSUPPORTED), head_dim 64 or 128,
  * any num_q_heads that is a multiple of num_kv_heads.  `out` must not alias
  * any input or the workspace.
+ *
+ * Kernel selection can be overridden for measurements through the
+ * environment variable PA_DECODE_KERNEL, read at each call: "valu" runs
+ * 16-bit KV through the vector-ALU partition kernel (the fp32 kernel, no
+ * matrix cores), "partition" runs the matrix-core partition kernels instead
+ * of the even split.  Unset or any other value: the choice described above.
+ * Every choice computes the same attention within the stated tolerances.
  */
 pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
                       const int32_t* block_tables, const int32_t* context_lens,
@@ -151,7 +158,7 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads
  *   q                device, [num_tokens][num_q_heads][head_dim], dtype
  *   k_pool, v_pool   device, [num_blocks][num_kv_heads][block_size][head_dim], dtype
  *   block_tables     device, int32 [num_seqs][max_blocks_per_seq]; entries at
- *                    index >= ceil(L/16) are never read
+ *                    index >= ceil(L/block_size) are never read
  *   context_lens     device, int32 [num_seqs]
  *   query_start      device, int32 [num_seqs + 1]: query_start[0] = 0,
  *                    non-decreasing, query_start[num_seqs] = num_tokens;
@@ -215,8 +222,36 @@ size_t pa_prefill_workspace_bytes(int num_seqs, int num_tokens, int num_q_heads,
                                   int head_dim, int max_query_len, int max_context_len,
                                   int partition_size);
 
-/* (pa_write_kv, pa_copy_blocks and pa_swap_blocks take any block_size that is a
- * power of two up to 128.) */
+/*
+ * pa_write_kv -- store the new tokens' K and V rows in their slots
+ * (reshape-and-cache).  For each token i whose slot = slot_mapping[i]
+ * satisfies 0 <= slot < num_blocks * block_size:
+ *   k_pool[slot / block_size][h][slot % block_size][:] = k_new[i][h][:]
+ *   v_pool[slot / block_size][h][slot % block_size][:] = v_new[i][h][:]
+ * for every KV head h.  The new key and value go to the block and offset the
+ * block manager assigned before the query attends to them (PagedAttention
+ * (tensortonic), "5. Reading the Cache During Attention"); every token of the
+ * step is written by one launch (PagedAttention and vLLM: Paging the KV Cache
+ * Like an OS, "Step 5", where the write kernels are fused to save launches).
+ *
+ *   k_pool, v_pool   device, [num_blocks][num_kv_heads][block_size][head_dim],
+ *                    dtype; only the addressed rows are written, no other
+ *                    byte is touched
+ *   k_new, v_new     device, [num_tokens][num_kv_heads][head_dim], dtype; read
+ *   slot_mapping     device, int64 [num_tokens]; slot = block * block_size +
+ *                    offset.  A negative slot skips its token (padding); a
+ *                    slot >= num_blocks * block_size is a caller error and is
+ *                    skipped too, never written
+ *   num_tokens       >= 0 (0 launches nothing)
+ *   stream           hipStream_t or NULL
+ * The non-negative slots of one call must be distinct: two tokens naming one
+ * slot race and the row holds either token's bytes.  Supported: fp32, fp16
+ * and bf16, head_dim 64 or 128, any block_size that is a power of two up to
+ * 128 (pa_copy_blocks and pa_swap_blocks take the same block sizes).
+ * Returns PA_ERR_NULL, PA_ERR_SHAPE (negative sizes, tensors not 16-byte
+ * aligned), PA_ERR_UNSUPPORTED or PA_ERR_LAUNCH before or at the launch;
+ * the copy itself cannot fail.
+ */
 pa_status_t pa_write_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                         const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
                         int head_dim, int block_size, int num_blocks, pa_dtype_t dtype,

@@ -6,7 +6,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpa.so")
+# PA_LIB_PATH names another build of the same library (the host-sanitizer run
+# links one under _build/san); the in-tree libpa.so otherwise.
+LIB_PATH = os.environ.get("PA_LIB_PATH") or os.path.join(HERE, "libpa.so")
 
 PA_FP32, PA_FP16, PA_BF16 = 0, 1, 2
 PA_OK = 0

@@ -33,11 +33,18 @@ class BlockManager:
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
 
+    # bound at class creation: at interpreter shutdown module globals (LIB)
+    # may already be cleared when the last managers are collected
+    _destroy = LIB.pa_bm_destroy
+
     def __del__(self):
         h = getattr(self, "_h", None)
         if h is not None and h.value:
-            LIB.pa_bm_destroy(h)
             self._h = None
+            try:
+                type(self)._destroy(h)
+            except Exception:  # the library itself is gone: nothing left to free
+                pass
 
     # operations
     def add_seq(self, seq: int) -> None:

@@ -19,9 +19,9 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 // PA_DECODE_KERNEL=valu selects the VALU partition kernel for 16-bit KV too,
 // PA_DECODE_KERNEL=partition the MFMA partition kernels instead of the
-// balanced split (read once; for comparisons).
+// balanced split (read at each call, so a process can compare them).
 const char* kernel_override() {
-  static const char* v = getenv("PA_DECODE_KERNEL");
+  const char* v = getenv("PA_DECODE_KERNEL");
   return v ? v : "";
 }
 bool force_valu() { return strcmp(kernel_override(), "valu") == 0; }

@@ -59,6 +59,27 @@ def _stream_handle(stream) -> int:
     return int(stream)
 
 
+def _launch_stream(stream):
+    """The torch stream the library launches on (current, given, or a raw
+    hipStream_t handle wrapped without taking ownership).  Temporaries the
+    binding allocates for a call are allocated on it, so torch's caching
+    allocator does not hand their memory to other work while the call's
+    kernels still use it."""
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
+def _alloc_on(ts, fn):
+    """fn() with `ts` current, so its allocations belong to `ts`."""
+    if ts == torch.cuda.current_stream():
+        return fn()
+    with torch.cuda.stream(ts):
+        return fn()
+
+
 def _dtype_code(t):
     try:
         return _DTYPES[t.dtype]
@@ -88,14 +109,15 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_cont
     _device_tensor(context_lens, "context_lens", torch.int32, 1)
     if block_tables.shape[0] != B or context_lens.shape[0] != B:
         raise ValueError("block_tables / context_lens rows must equal num_seqs")
+    ts = _launch_stream(stream)
     if out is None:
-        out = torch.empty_like(q)
+        out = _alloc_on(ts, lambda: torch.empty_like(q))
     _device_tensor(out, "out", q.dtype, 3)
     if out.shape != q.shape:
         raise ValueError("out must have q's shape")
     need = decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, partition_size)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device) if need else None
+    if workspace is None and need:
+        workspace = _alloc_on(ts, lambda: torch.empty(need, dtype=torch.uint8, device=q.device))
     if workspace is not None:
         _device_tensor(workspace, "workspace")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -103,7 +125,7 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_cont
     st = LIB.pa_decode(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                        block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, bs, nb,
                        block_tables.shape[1], int(max_context_len), float(scale), _dtype_code(q),
-                       int(partition_size), ws_ptr, ws_bytes, _stream_handle(stream))
+                       int(partition_size), ws_ptr, ws_bytes, ts.cuda_stream)
     check_status(st, "pa_decode")
     return out
 
@@ -136,14 +158,15 @@ def prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale: f
     B = context_lens.shape[0]
     if block_tables.shape[0] != B or query_start.shape[0] != B + 1:
         raise ValueError("block_tables rows must equal num_seqs and query_start must have num_seqs + 1 entries")
+    ts = _launch_stream(stream)
     if out is None:
-        out = torch.empty_like(q)
+        out = _alloc_on(ts, lambda: torch.empty_like(q))
     _device_tensor(out, "out", q.dtype, 3)
     if out.shape != q.shape:
         raise ValueError("out must have q's shape")
     need = prefill_workspace_bytes(B, N, Hq, Hkv, D, max_query_len, max_context_len, partition_size)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    if workspace is None and need:
+        workspace = _alloc_on(ts, lambda: torch.empty(need, dtype=torch.uint8, device=q.device))
     if workspace is not None:
         _device_tensor(workspace, "workspace")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -151,7 +174,7 @@ def prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale: f
     st = LIB.pa_prefill(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                         block_tables.data_ptr(), context_lens.data_ptr(), query_start.data_ptr(), B, N, Hq,
                         Hkv, D, bs, nb, block_tables.shape[1], int(max_query_len), int(max_context_len),
-                        int(partition_size), float(scale), _dtype_code(q), ws_ptr, ws_bytes, _stream_handle(stream))
+                        int(partition_size), float(scale), _dtype_code(q), ws_ptr, ws_bytes, ts.cuda_stream)
     check_status(st, "pa_prefill")
     return out
 

@@ -30,7 +30,7 @@ def run_write_copy(w):
     return g, to_host_storage(g.k, w.dtype), to_host_storage(g.v, w.dtype)
 
 
-@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4", "c4b"])
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4", "c4b", "c5"])
 def test_step_writes_and_copies_bit_exact(key):
     w = make_workload(key)
     print(f"[write/copy] {key}: {w.num_seqs} seqs, pool {w.num_blocks} blocks", flush=True)
