@@ -112,10 +112,16 @@ def parse():
     ap.add_argument("--placement", choices=["shuffled", "sequential"], default="shuffled")
     ap.add_argument("--block-size", type=int, default=16,
                     help="slots per KV block for the decode workloads (16, 32, 64, 128)")
+    ap.add_argument("--decode-kernel", choices=["auto", "valu", "partition"], default="auto",
+                    help="pa_decode kernel override (PA_DECODE_KERNEL): valu = vector-ALU kernel for 16-bit KV "
+                         "too, partition = matrix-core partition kernels instead of the even split")
+    ap.add_argument("--no-second", action="store_true",
+                    help="c2 only: skip the Qwen2.5-72B (c5) sub-record of the default run")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
-    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
-                    help="turn rocprofv3 counter CSVs into profiles/decode_<config>_traffic.json")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("READ_CSV", "WRITE_CSV", "COPY_READ_CSV", "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 TCC counter CSVs (read and write passes of the decode bench and of "
+                         "--calibrate-copy) into profiles/decode_<config>_traffic.json")
     return ap.parse_args()
 
 
@@ -127,14 +133,19 @@ def kernel_fingerprint():
     return h.hexdigest()[:16]
 
 
-def traffic_record(key):
+def traffic_record(key, partition_size):
+    """The committed counter record of this workload's main kernel, while the
+    kernel sources are the ones it was taken with (else None)."""
     path = os.path.join(PROFILES, f"decode_{key}_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except OSError:
         return None
-    return rec if rec.get("kernel_sha") == kernel_fingerprint() else None
+    ok = (rec.get("kernel_sha") == kernel_fingerprint() and rec.get("config") == key
+          and rec.get("partition_size") == partition_size and "read_scale" in rec
+          and os.environ.get("PA_DECODE_KERNEL", "") in ("", "auto"))
+    return rec if ok else None
 
 
 def calibrate_copy():
@@ -150,9 +161,10 @@ def calibrate_copy():
     print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}))
 
 
-def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
+def copy_bandwidth(torch, nbytes=1 << 30, reps=200):
     """The box's device-to-device copy rate: bytes read + bytes written per
-    second of a plain 1 GiB copy (HIP events, after two warm-up copies)."""
+    second of a plain 1 GiB copy (HIP events around `reps` copies, after two
+    warm-up copies)."""
     src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(2):
@@ -186,30 +198,67 @@ def dominant_kernel_name(path, kernel_pred):
     return "?"
 
 
+# gfx950 L2 (TCC) -> memory fabric request counters, summed over the L2
+# channels.  Read bytes = 32 n32 + 64 n64 + 128 n128 (requests by size); the
+# DRAM-bound reads are also counted in 32-byte units (a 64-byte request as 2,
+# 128-byte as 4).  Write bytes = 64 n64 + 32 (n - n64).
+READ_COUNTERS = ["TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum",
+                 "TCC_EA0_RDREQ_DRAM_32B_sum"]
+WRITE_COUNTERS = ["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"]
+
+
+def _read_bytes(c):
+    return 32 * c["TCC_EA0_RDREQ_32B_sum"] + 64 * c["TCC_EA0_RDREQ_64B_sum"] + 128 * c["TCC_EA0_RDREQ_128B_sum"]
+
+
+def _write_bytes(c):
+    return 64 * c["TCC_EA0_WRREQ_64B_sum"] + 32 * (c["TCC_EA0_WRREQ_sum"] - c["TCC_EA0_WRREQ_64B_sum"])
+
+
 def pmc_summary(args):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dominant decode kernel,
-    scaled by what the same counters read for a 1 GiB device copy."""
+    """HBM bytes per launch of the dominant decode kernel from the TCC request
+    counters, each direction scaled by what the same counters read for a
+    plain 1 GiB device copy (1 GiB read, 1 GiB written)."""
+    from paged_kv_cache_117_amd import metrics
+    from workloads import make_workload
+
     dec = lambda n: ("decode_stream" in n and "reduce" not in n) or "decode_part" in n
     copy = lambda n: "copy" in n.lower() or "elementwise" in n.lower()
-    fetch, nf = _counter_means(args.pmc_summary[0], dec)
-    write, _ = _counter_means(args.pmc_summary[1], dec)
-    cfetch, _ = _counter_means(args.pmc_summary[2], copy)
-    cwrite, _ = _counter_means(args.pmc_summary[3], copy)
+    rd, nf = _counter_means(args.pmc_summary[0], dec)
+    wr, _ = _counter_means(args.pmc_summary[1], dec)
+    crd, _ = _counter_means(args.pmc_summary[2], copy)
+    cwr, _ = _counter_means(args.pmc_summary[3], copy)
     gib = float(1 << 30)
-    f_fetch = gib / (cfetch["FETCH_SIZE"] * 1024)
-    f_write = gib / (cwrite["WRITE_SIZE"] * 1024)
+    r_scale = gib / _read_bytes(crd)
+    w_scale = gib / _write_bytes(cwr)
+    read_b = _read_bytes(rd)
+    write_b = _write_bytes(wr)
+    psize = args.partition_size if args.partition_size is not None else WORKLOAD_PARTITION.get(args.config, 0)
+    w = make_workload(args.config, block_size=args.block_size)
+    eb = metrics.ELEM_BYTES[w.dtype]
+    io = metrics.decode_io_bytes(w.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, eb, w.block_size)
+    kv = metrics.decode_kv_bytes(w.context_lens, w.num_kv_heads, w.head_dim, eb)
+    traffic = read_b * r_scale + write_b * w_scale
     rec = {
         "config": args.config,
+        "partition_size": psize,
         "kernel": dominant_kernel_name(args.pmc_summary[0], dec),
         "kernel_sha": kernel_fingerprint(),
-        "dispatches": nf.get("FETCH_SIZE", 0),
-        "fetch_kib_per_dispatch": round(fetch["FETCH_SIZE"], 1),
-        "write_kib_per_dispatch": round(write["WRITE_SIZE"], 1),
-        "copy_fetch_kib_per_gib": round(cfetch["FETCH_SIZE"], 1),
-        "copy_write_kib_per_gib": round(cwrite["WRITE_SIZE"], 1),
-        "fetch_scale": round(f_fetch, 4),
-        "write_scale": round(f_write, 4),
-        "traffic_bytes_per_launch": int(fetch["FETCH_SIZE"] * 1024 * f_fetch + write["WRITE_SIZE"] * 1024 * f_write),
+        "dispatches": nf.get("TCC_EA0_RDREQ_128B_sum", 0),
+        "read_counters_per_dispatch": {k: round(rd[k], 1) for k in READ_COUNTERS},
+        "write_counters_per_dispatch": {k: round(wr[k], 1) for k in WRITE_COUNTERS},
+        "copy_read_counters": {k: round(crd[k], 1) for k in READ_COUNTERS},
+        "copy_write_counters": {k: round(cwr[k], 1) for k in WRITE_COUNTERS},
+        "read_bytes_by_size": int(read_b),
+        "read_bytes_dram_32b_units": int(32 * rd["TCC_EA0_RDREQ_DRAM_32B_sum"]),
+        "write_bytes_by_size": int(write_b),
+        "write_bytes_dram_32b_units": int(32 * wr["TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"]),
+        "read_scale": round(r_scale, 4),
+        "write_scale": round(w_scale, 4),
+        "traffic_bytes_per_launch": int(traffic),
+        "algorithmic_bytes_per_launch": io,
+        "kv_bytes_per_launch": kv,
+        "traffic_over_algorithmic": round(traffic / io, 4),
     }
     os.makedirs(PROFILES, exist_ok=True)
     out = os.path.join(PROFILES, f"decode_{args.config}_traffic.json")
@@ -305,80 +354,48 @@ def cpu_info():
     return model
 
 
-def blas_threads():
-    try:
-        from threadpoolctl import threadpool_info
-
-        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-        return max(n) if n else 1
-    except Exception:
-        return 1
-
-
-def cpu_one_thread(w, tables, budget_s):
-    """The same oracle pass with BLAS limited to one thread, on as many leading
-    sequences as fit the budget: GB/s."""
-    import oracle
-    from paged_kv_cache_117_amd import metrics
-
-    try:
-        from threadpoolctl import threadpool_limits
-    except Exception:
-        return None
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        oracle.decode(w.q[:1], w.k_pool, w.v_pool, tables[:1], w.context_lens[:1], w.scale, w.dtype)
-        per_tok = (time.perf_counter() - t0) / max(1, int(w.context_lens[0]))
-        rows, acc = 0, 0
-        for L in w.context_lens:
-            if (acc + int(L)) * per_tok > budget_s and rows > 0:
-                break
-            acc += int(L)
-            rows += 1
-        t0 = time.perf_counter()
-        oracle.decode(w.q[:rows], w.k_pool, w.v_pool, tables[:rows], w.context_lens[:rows], w.scale, w.dtype)
-        dt = time.perf_counter() - t0
-    kvb = metrics.decode_kv_bytes(w.context_lens[:rows], w.num_kv_heads, w.head_dim, metrics.ELEM_BYTES[w.dtype])
-    return {"value": round(kvb / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "rows": rows}
-
-
 def cpu_baseline(w, tables, budget_s):
-    """The oracle as it stands, on whole-batch passes of the same step, for ~budget_s."""
+    """The oracle as it stands, on whole-batch passes of the same step (or as
+    many leading sequences as fit the budget), with BLAS held to one thread:
+    its per-(sequence, head) loop runs on one core whatever BLAS is allowed
+    (the same rate was measured with all host threads)."""
     import oracle  # test infrastructure: only this leg of the bench uses it
     from paged_kv_cache_117_amd import metrics
+    from threadpoolctl import threadpool_limits
 
     eb = metrics.ELEM_BYTES[w.dtype]
     k, v = w.k_pool, w.v_pool
-    # as many leading sequences as fit the budget (one timed probe sequence first)
-    t0 = time.perf_counter()
-    oracle.decode(w.q[:1], k, v, tables[:1], w.context_lens[:1], w.scale, w.dtype)
-    per_tok = (time.perf_counter() - t0) / max(1, int(w.context_lens[0]))
-    total_tok = int(w.context_lens.sum())
-    reps = 1
-    rows = w.num_seqs
-    if per_tok * total_tok > budget_s:
-        acc = 0
-        rows = 0
-        for L in w.context_lens:
-            if (acc + int(L)) * per_tok > budget_s and rows > 0:
-                break
-            acc += int(L)
-            rows += 1
-    else:
-        reps = max(1, int(budget_s / max(per_tok * total_tok, 1e-9)))
-        reps = min(reps, 20)
-    sel = slice(0, rows)
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        oracle.decode(w.q[sel], k, v, tables[sel], w.context_lens[sel], w.scale, w.dtype)
-    dt = (time.perf_counter() - t0) / reps
+    with threadpool_limits(limits=1):
+        # as many leading sequences as fit the budget (one timed probe sequence first)
+        t0 = time.perf_counter()
+        oracle.decode(w.q[:1], k, v, tables[:1], w.context_lens[:1], w.scale, w.dtype)
+        per_tok = (time.perf_counter() - t0) / max(1, int(w.context_lens[0]))
+        total_tok = int(w.context_lens.sum())
+        reps = 1
+        rows = w.num_seqs
+        if per_tok * total_tok > budget_s:
+            acc = 0
+            rows = 0
+            for L in w.context_lens:
+                if (acc + int(L)) * per_tok > budget_s and rows > 0:
+                    break
+                acc += int(L)
+                rows += 1
+        else:
+            reps = max(1, min(20, int(budget_s / max(per_tok * total_tok, 1e-9))))
+        sel = slice(0, rows)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.decode(w.q[sel], k, v, tables[sel], w.context_lens[sel], w.scale, w.dtype)
+        dt = (time.perf_counter() - t0) / reps
     kvb = metrics.decode_kv_bytes(w.context_lens[sel], w.num_kv_heads, w.head_dim, eb)
     return {
         "value": round(kvb / dt / 1e9, 4),
         "unit": "GB/s",
-        "cores": blas_threads(),
+        "cores": 1,
+        "host_cores": os.cpu_count(),
         "kind": "oracle",
-        "sample": (f"fp64 numpy oracle decode (gather + two-pass softmax) over the first {rows} of "
+        "sample": (f"fp64 numpy oracle decode (gather + two-pass softmax), one thread, over the first {rows} of "
                    f"{w.num_seqs} sequences x {reps} pass(es), {dt:.3f} s per pass; "
                    f"seq-steps/s {rows / dt:.2f}; host CPU: {cpu_info()}"),
     }
@@ -391,6 +408,8 @@ def prefill_cpu_baseline(w, tables, budget_s):
     import oracle  # test infrastructure: only this leg of the bench uses it
     from paged_kv_cache_117_amd import metrics
 
+    from threadpoolctl import threadpool_limits
+
     P = int(w.prior_lens[0])
 
     def run(n):
@@ -398,18 +417,20 @@ def prefill_cpu_baseline(w, tables, budget_s):
         oracle.prefill(w.q[:n], w.k_pool, w.v_pool, tables[:1], [P + n], [0, n], w.scale, w.dtype)
         return time.perf_counter() - t0
 
-    t1 = run(1)
-    t4 = run(4)
-    per_row = max((t4 - t1) / 3, 1e-6)
-    n = max(1, min(int(w.chunk_lens[0]), int((budget_s - max(t1 - per_row, 0.0)) / per_row)))
-    dt = run(n)
+    with threadpool_limits(limits=1):
+        t1 = run(1)
+        t4 = run(4)
+        per_row = max((t4 - t1) / 3, 1e-6)
+        n = max(1, min(int(w.chunk_lens[0]), int((budget_s - max(t1 - per_row, 0.0)) / per_row)))
+        dt = run(n)
     fl = metrics.prefill_flops([P], [n], w.num_q_heads, w.head_dim)
     return {
         "value": round(fl / dt / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": blas_threads(),
+        "cores": 1,
+        "host_cores": os.cpu_count(),
         "kind": "oracle",
-        "sample": (f"fp64 numpy oracle prefill (gather + two-pass softmax per row) over the first {n} of "
+        "sample": (f"fp64 numpy oracle prefill (gather + two-pass softmax per row), one thread, over the first {n} of "
                    f"{int(w.chunk_lens[0])} chunk tokens of sequence 0 (prior {P}), {dt:.3f} s; "
                    f"tokens/s {n / dt:.2f}; host CPU: {cpu_info()}"),
     }
@@ -709,46 +730,16 @@ def main_host(args):
     print(json.dumps(res), flush=True)
 
 
-def main():
-    args = parse()
-    if args.pmc_summary:
-        pmc_summary(args)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path has no "
-              "multi-GPU mode: sequences or KV heads shard across GPUs with no exchange inside "
-              "attention, so run one process per GPU.", file=sys.stderr)
-        sys.exit(2)
-
-    if args.config in HOST_NAMES:
-        main_host(args)
-        return
-    if args.config in SWAP_NAMES:
-        import torch
-
-        torch.cuda.set_device(0)
-        main_swap(args)
-        return
-    if args.config in PREFILL_NAMES:
-        import torch
-
-        torch.cuda.set_device(0)
-        main_prefill(args)
-        return
-
-    import torch
-
+def decode_bench(torch, key, args, partition_size, steps, warmup, cpu_budget):
+    """One paged decode step per iteration on workload `key`: the step's
+    copy-on-write copies (if any), pa_write_kv, pa_decode.  Returns the
+    fields of the JSON line (timed region, per-call and main-kernel passes,
+    roofline of the main kernel, the oracle baseline when cpu_budget > 0)."""
     import paged_kv_cache_117_amd as pa
     from paged_kv_cache_117_amd import metrics
     from workloads import make_workload
 
-    torch.cuda.set_device(0)
-    if args.calibrate_copy:
-        calibrate_copy()
-        return
-    w = make_workload(args.config, block_size=args.block_size)
-    if args.partition_size is None:
-        args.partition_size = WORKLOAD_PARTITION.get(args.config, 0)
+    w = make_workload(key, block_size=args.block_size)
     eb = metrics.ELEM_BYTES[w.dtype]
     tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
 
@@ -786,6 +777,8 @@ def main():
     k_new = dev(w.k_new, "kv")
     v_new = dev(w.v_new, "kv")
     lens = dev(w.context_lens.astype(np.int32))
+    ws_bytes = pa.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_context_len,
+                                         partition_size)
     sets = []
     for r in range(R):
         t = np.where(tables >= 0, tables + r * nb, -1).astype(np.int32)
@@ -794,9 +787,7 @@ def main():
             slots=dev(slots + r * nb * w.block_size),
             pairs=dev((pairs + r * nb).astype(np.int32)) if len(pairs) else None,
             out=torch.empty_like(q),
-            ws=torch.empty(max(1, pa.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                                                            w.max_context_len, args.partition_size)),
-                           dtype=torch.uint8, device="cuda"),
+            ws=torch.empty(max(1, ws_bytes), dtype=torch.uint8, device="cuda"),
         ))
     stream = torch.cuda.current_stream()
 
@@ -810,56 +801,49 @@ def main():
         if kev is not None:
             pa.time_next_main_kernel(*kev)  # events around the main decode kernel alone
         pa.decode(q, k_pool, v_pool, s["tables"], lens, w.scale, w.max_context_len, out=s["out"],
-                  partition_size=args.partition_size, workspace=s["ws"], stream=stream)
+                  partition_size=partition_size, workspace=s["ws"], stream=stream)
         if ev is not None:
             ev[1].record(stream)
 
-    args.warmup = warm_up(torch, lambda i: step(i % R), args.warmup)
-    evs, kevs = timing_events(torch, args.steps, stream)
+    warmup = warm_up(torch, lambda i: step(i % R), warmup)
+    evs, kevs = timing_events(torch, steps, stream)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(i % R)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
-    dec_ms = call_pass(torch, step, args.steps, R, evs)
-    kern_avg = main_kernel_pass(torch, step, args.steps, R, kevs)
-    ms_step = total_ms / args.steps
+    dec_ms = call_pass(torch, step, steps, R, evs)
+    kern_avg = main_kernel_pass(torch, step, steps, R, kevs)
+    ms_step = total_ms / steps
 
     kv_bytes = metrics.decode_kv_bytes(w.context_lens, w.num_kv_heads, w.head_dim, eb)
     unique_kv_bytes = metrics.decode_unique_kv_bytes(tables, w.context_lens, w.num_kv_heads, w.head_dim, eb,
                                                      w.block_size)
-    io_bytes = metrics.decode_io_bytes(w.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, eb)
+    io_bytes = metrics.decode_io_bytes(w.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, eb,
+                                       w.block_size)
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     dec_avg = float(dec_ms.mean())
     achieved = io_bytes / (kern_avg * 1e-3) / 1e9
-
     res = {
-        "metric": METRIC,
         "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_NAMES[args.config],
-            "key": args.config,
+            "workload": WORKLOAD_NAMES[key],
+            "key": key,
             "num_seqs": w.num_seqs,
             "kv_bytes_per_step": kv_bytes,
             "unique_kv_bytes_per_step": unique_kv_bytes,
             "block_size": w.block_size,
-            "partition_size": args.partition_size or "auto (even split over all wavefronts)",
+            "partition_size": partition_size or "auto (even split over all wavefronts)",
             "placement": args.placement,
             "rotating_sets": R,
             "copy_pairs": int(len(pairs)),
@@ -876,16 +860,13 @@ def main():
         # distinct physical blocks read (shared prefix blocks once): equals the
         # logical rate unless sequences share blocks
         "decode_unique_kv_gbps": round(unique_kv_bytes / (dec_avg * 1e-3) / 1e9, 2),
-        "device_copy_gbps": None,
-        "decode_frac_of_copy": None,
         "host_block_manager_ms": round(host_bm_ms, 3),
         **kv_util,
-        "kv_bytes_per_token_model": (2 * w.num_kv_heads * w.head_dim * eb * MODEL_LAYERS[args.config]
-                                     if args.config in MODEL_LAYERS else None),
-        "pages_context": PAGES_CONTEXT,
+        "kv_bytes_per_token_model": (2 * w.num_kv_heads * w.head_dim * eb * MODEL_LAYERS[key]
+                                     if key in MODEL_LAYERS else None),
         "wall_s": round(wall, 3),
         "roofline": {
-            "kernel": "pa_decode main kernel (decode_stream for batches of up to 4096 sequences)",
+            "kernel": "pa_decode main kernel (%s)" % main_kernel_label(w.dtype, w.num_seqs),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
@@ -894,20 +875,109 @@ def main():
             "traffic": None,
         },
         "traffic_note": None,
-        "cpu_baseline": None,
+        "algorithmic_bytes_per_launch": io_bytes,
     }
+    rec = traffic_record(key, partition_size)
+    if rec is not None:
+        res["roofline"]["traffic"] = rec["traffic_bytes_per_launch"]
+        res["traffic_note"] = ("HBM bytes per main-kernel launch from rocprofv3 TCC counters (read requests by "
+                               "size + write requests by size, summed over channels), scaled by a 1 GiB copy "
+                               "(read scale %.4f, write scale %.4f); %.3f x the algorithmic bytes per launch (%d)"
+                               % (rec["read_scale"], rec["write_scale"], rec["traffic_bytes_per_launch"] / io_bytes,
+                                  io_bytes))
+    del sets, k_pool, v_pool
+    torch.cuda.empty_cache()
+    if cpu_budget > 0:
+        res["cpu_baseline"] = cpu_baseline(w, tables, cpu_budget)
+    return res
+
+
+def main_kernel_label(dtype, num_seqs):
+    kern = os.environ.get("PA_DECODE_KERNEL", "")
+    if dtype == "fp32" or kern == "valu":
+        return "decode_part_valu, vector ALU"
+    if kern == "partition" or num_seqs > 4096:
+        return "decode_part_wave / decode_part_mfma, matrix cores"
+    return "decode_stream, the even split over all wavefronts, matrix cores"
+
+
+def main():
+    args = parse()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path has no "
+              "multi-GPU mode: sequences or KV heads shard across GPUs with no exchange inside "
+              "attention, so run one process per GPU.", file=sys.stderr)
+        sys.exit(2)
+    if args.decode_kernel != "auto":
+        # read by the library at each pa_decode call
+        os.environ["PA_DECODE_KERNEL"] = args.decode_kernel
+
+    if args.config in HOST_NAMES:
+        main_host(args)
+        return
+    if args.config in SWAP_NAMES:
+        import torch
+
+        torch.cuda.set_device(0)
+        main_swap(args)
+        return
+    if args.config in PREFILL_NAMES:
+        import torch
+
+        torch.cuda.set_device(0)
+        main_prefill(args)
+        return
+
+    import torch
+
+    import paged_kv_cache_117_amd  # noqa: F401  (fails loudly when libpa.so is missing)
+
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    # The box's device-copy rate first: it is reported beside the decode rate,
+    # and its ~0.1 s of HBM-bound work also brings the GPU's clocks up before
+    # the warm-up steps.
     cg = copy_bandwidth(torch)
+    psize = args.partition_size if args.partition_size is not None else WORKLOAD_PARTITION.get(args.config, 0)
+    cpu_budget = 0.0 if args.no_cpu_baseline else args.cpu_seconds
+    core = decode_bench(torch, args.config, args, psize, args.steps, args.warmup, cpu_budget)
+    res = {
+        "metric": METRIC,
+        "value": core.pop("value"),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": core.pop("steps"),
+        "warmup": core.pop("warmup"),
+        "ms_per_step": core.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": core.pop("dtype"),
+        "data": "synthetic",
+        "config": core.pop("config"),
+    }
+    cpu = core.pop("cpu_baseline", None)
+    res.update(core)
     res["device_copy_gbps"] = round(cg, 1)
     res["decode_frac_of_copy"] = round(res["decode_kv_gbps"] / cg, 4)
-    rec = traffic_record(args.config)
-    if rec is not None and rec.get("config") == args.config:
-        # counters cover the dominant kernel; the reduce adds its piece reads and output writes
-        res["roofline"]["traffic"] = rec["traffic_bytes_per_launch"]
-        res["traffic_note"] = ("HBM bytes per dominant-kernel launch from rocprofv3 FETCH_SIZE/WRITE_SIZE "
-                               "scaled by a 1 GiB copy; algorithmic bytes per launch: %d" % io_bytes)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, tables, args.cpu_seconds)
-        res["cpu_baseline_1thread"] = cpu_one_thread(w, tables, min(5.0, args.cpu_seconds / 2))
+    res["pages_context"] = PAGES_CONTEXT
+    # The second target workload (Qwen2.5-72B layer, 512-position partitions)
+    # beside the headline, measured the same way in the same run.
+    if args.config == "c2" and not args.no_second:
+        sub = decode_bench(torch, "c5", args, WORKLOAD_PARTITION["c5"], args.steps, args.warmup, 0.0)
+        res["c5"] = {k: sub[k] for k in ("value", "hbm_peak_frac", "ms_per_step", "seq_steps_per_s", "decode_ms",
+                                          "decode_main_kernel_ms", "decode_call_hbm_frac", "roofline",
+                                          "traffic_note", "warmup", "steps", "dtype")}
+        res["c5"]["workload"] = sub["config"]["workload"]
+        res["c5"]["kv_bytes_per_step"] = sub["config"]["kv_bytes_per_step"]
+        res["c5"]["partition_size"] = sub["config"]["partition_size"]
+        res["c5"]["unit"] = "GB/s"
+    res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 
