@@ -337,37 +337,77 @@ __device__ __forceinline__ void fill_rows(void* out, size_t row0, int nh, bool b
 }
 
 // The two-tile pipeline of one wave over its tiles k = 0..cnt-1 (cnt >= 1):
-// issue(k, K, V) loads tile k, consume(k, K, V, valid) computes it.  Every
-// issue is unconditional (indices past the end re-read the last tile, an L2
-// hit), so the loads stay in a fixed order and each consume waits only for
-// its own tile.  The scheduling barriers keep each tile's work and its
-// prefetch in program order (left alone, the scheduler hoists the next
-// tile's MFMAs above this tile's PV, so a consume waits for both buffers),
-// and the compiler memory barriers keep the prologue's A before B as in the
-// loop (else the wait counts, merged over both paths, make A wait for half
-// of B).  The pool pointers behind `issue` must not be __restrict__: loads
-// through restrict pointers may move across those barriers.
-template <typename KBuf, typename VBuf, typename Issue, typename Consume>
+// issue(k, K, V) loads tile k, consume(k, K, V, valid) computes it.  Inside
+// the loop every issue is unconditional and names an existing tile, so the
+// loads stay in a fixed order and each consume waits only for its own tile;
+// the last one to three tiles are consumed after the loop on straight-line
+// paths of their own (exact wait counts on each), with no load past the last
+// tile (a load the wave never consumes still delays the wave's end by a
+// memory round trip).  With cnt = 1 the prologue loads tile 0 into both
+// buffers.  The scheduling barriers keep each tile's work and its prefetch
+// in program order (left alone, the scheduler hoists the next tile's MFMAs
+// above this tile's PV, so a consume waits for both buffers), and the
+// compiler memory barriers keep the prologue's A before B as in the loop
+// (else the wait counts, merged over both paths, make A wait for half of B).
+// The pool pointers behind `issue` must not be __restrict__: loads through
+// restrict pointers may move across those barriers.  `preloaded`: the caller
+// has already issued tiles 0 and min(1, cnt-1) into A and B.
+// kExactTail = false keeps one loop for the whole walk instead (the last
+// iterations re-read the last tile, consuming it as empty): half the code
+// and fewer live registers, which the partition kernels need to keep four
+// waves per SIMD.
+template <bool kExactTail = true, typename KBuf, typename VBuf, typename Issue, typename Consume>
 __device__ __forceinline__ void pipeline(int cnt, KBuf& kA, VBuf& vA, KBuf& kB, VBuf& vB, Issue&& issue,
-                                         Consume&& consume) {
+                                         Consume&& consume, bool preloaded = false) {
   const int last = cnt - 1;
   __builtin_amdgcn_sched_barrier(0);
-  issue(0, kA, vA);
+  if (!preloaded) {
+    issue(0, kA, vA);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    issue(min(1, last), kB, vB);
+  }
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-  issue(min(1, last), kB, vB);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-  for (int k = 0; k < cnt; k += 2) {
+  if constexpr (!kExactTail) {
+    for (int k = 0; k < cnt; k += 2) {
+      consume(k, kA, vA, true);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(min(k + 2, last), kA, vA);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(k + 1, kB, vB, k + 1 < cnt);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(min(k + 3, last), kB, vB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return;
+  }
+  int k = 0;
+  for (; k + 3 < cnt; k += 2) {  // tiles k+2 and k+3 exist
     consume(k, kA, vA, true);
     __builtin_amdgcn_sched_barrier(0);
-    issue(min(k + 2, last), kA, vA);
+    issue(k + 2, kA, vA);
     __builtin_amdgcn_sched_barrier(0);
-    consume(k + 1, kB, vB, k + 1 < cnt);
+    consume(k + 1, kB, vB, true);
     __builtin_amdgcn_sched_barrier(0);
-    issue(min(k + 3, last), kB, vB);
+    issue(k + 3, kB, vB);
     __builtin_amdgcn_sched_barrier(0);
   }
+  // cnt - k tiles remain (1, 2 or 3): A holds tile k, B tile k + 1 (or a
+  // copy of tile k when cnt = 1)
+  const int r = cnt - k;
+  consume(k, kA, vA, true);
+  __builtin_amdgcn_sched_barrier(0);
+  if (r == 3) {
+    issue(k + 2, kA, vA);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(k + 1, kB, vB, true);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(k + 2, kA, vA, true);
+  } else if (r == 2) {
+    consume(k + 1, kB, vB, true);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // What both kernels share once a workgroup knows its (sequence, head group):
@@ -406,7 +446,7 @@ struct Body {
     if (cnt > 0) {
       uint4 kA[KS], kB[KS];
       VVec vA[4], vB[4];
-      pipeline(
+      pipeline<false>(
           cnt, kA, vA, kB, vB,
           [&](int k, uint4(&kr)[KS], VVec(&vr)[4]) {
             const size_t off = (size_t)(unsigned)__builtin_amdgcn_readlane(myid, k) * (16 * ROWB);
@@ -721,6 +761,19 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
   int tdone = 0;                // and its tiles staged by earlier chunks
   bool first = true;            // the wave's first piece (slot 2w)
 
+  // The wave's first two tiles are known already: tiles tb0 and tb0 + 1 of
+  // segment (s, hsub).  Their table entries are loaded now, the first chunk
+  // is planned while they travel, and the two tile loads go out before the
+  // chunk's staging loads (they then overlap the staging round trip instead
+  // of following it).  Lane 0 holds tile tb0's entry, lane 1 the next one
+  // (clamped to the sequence's tiles; used only when that tile is in the
+  // wave's first piece).
+  const int L0 = uni(s_len[s]);
+  const int tb0 = uin * unit;
+  const int kvh0 = nsub == 1 ? hsub : hsub / nsub;
+  const int pre_id = bt[(size_t)s * maxb + (min(tb0 + (lane & 1), ((L0 + 15) >> 4) - 1) >> lm)];
+  bool first_chunk = true;
+
   Piece* pcs = s_pc[wave];
   unsigned* desc = s_desc[wave];
   uint16_t (*sq)[QROW] = s_q[wave];
@@ -855,6 +908,38 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+    // ---- The first chunk's first two tiles, from the entries loaded before
+    // planning: the chunk's tile 0 is tb0, its tile 1 is tb0 + 1 when the
+    // first piece has two tiles (tile 0 again when the chunk has one tile);
+    // otherwise the pipeline's prologue issues them as usual.  Descriptors
+    // are the ones staging computes below (an invalid id reads block 0,
+    // never dereferenced past the pool; staging marks the piece bad).
+    bool preloaded = false;
+    if (first_chunk) {
+      first_chunk = false;
+      const int nt0 = uni(pcs[0].nt);
+      if (nt0 >= 2 || ntc == 1) {
+        const int tb1 = ntc == 1 ? tb0 : tb0 + 1;
+        int idA = __builtin_amdgcn_readlane(pre_id, 0);
+        int idB = __builtin_amdgcn_readlane(pre_id, ntc == 1 ? 0 : 1);
+        idA = (idA >= 0 && idA < num_blocks) ? idA : 0;
+        idB = (idB >= 0 && idB < num_blocks) ? idB : 0;
+        const unsigned mask = (1u << lm) - 1u;
+        const unsigned rowA = ((unsigned)(idA * Hkv + kvh0) << lm) | ((unsigned)tb0 & mask);
+        const unsigned rowB = ((unsigned)(idB * Hkv + kvh0) << lm) | ((unsigned)tb1 & mask);
+        __builtin_amdgcn_sched_barrier(0);
+        T::load(kp + (size_t)rowA * (16 * ROWB), vp + (size_t)rowA * (16 * ROWB), grp, col,
+                min(15, L0 - 1 - 16 * tb0), kA, vA);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        T::load(kp + (size_t)rowB * (16 * ROWB), vp + (size_t)rowB * (16 * ROWB), grp, col,
+                min(15, L0 - 1 - 16 * tb1), kB, vB);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        preloaded = true;
+      }
+    }
+
     // ---- Stage: block ids and query rows, all loads in flight together.
     constexpr int ND = kChunkTiles / 64;
     constexpr int NQ = (kChunkQRows * QCH + 63) / 64;
@@ -972,7 +1057,8 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
               qsrc = &sq[col < cp_nh ? cp_qrow + col : kChunkQRows][grp * 8];
             }
           }
-        });
+        },
+        preloaded);
   }
 }
 
