@@ -124,6 +124,33 @@ pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* 
                       int max_context_len, float scale, pa_dtype_t dtype, int partition_size,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and errors as pa_decode minus
+ * the workspace: the partials of split sequences go to a scratch array the
+ * library holds in device memory, PA_DECODE_NOALLOC_SCRATCH_BYTES per GPU,
+ * reserved when the library's device code is loaded on that GPU and kept
+ * until the process ends.  The call allocates nothing (no hipMalloc, no
+ * allocating library routine).  Sizes whose partials do not fit the scratch
+ * return PA_ERR_WORKSPACE before any launch; with 16-bit KV and up to 4096
+ * sequences (the even split) the need is two slots of up to 16 query rows
+ * per wavefront of the launch plus 8 bytes per (sequence, head group),
+ * e.g. 4 MiB for the Llama-3.1-8B layer at 64 sequences.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents (nothing in it needs clearing between calls): calls that
+ * overlap in time on one GPU -- on different streams, or from different
+ * threads -- race and their results are undefined.  Serialise them (one
+ * stream, or events between streams).
+ */
+#define PA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+pa_status_t pa_decode_noalloc(void* out, const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                              int block_size, int num_blocks, int max_blocks_per_seq,
+                              int max_context_len, float scale, pa_dtype_t dtype, int partition_size,
+                              void* stream);
+
 /* Bytes of workspace pa_decode needs for these sizes and any dtype: partials
  * of the partitions (none when every sequence fits one partition) and, for
  * batches of up to 4096 sequences, the pieces of the even split (a fixed

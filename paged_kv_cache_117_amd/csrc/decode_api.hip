@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "decode_kernels.h"
 #include "pa_internal.h"
@@ -66,42 +67,85 @@ extern "C" size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int n
   return need;
 }
 
-extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
-                                 const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
-                                 int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
-                                 int max_blocks_per_seq, int max_context_len, float scale, pa_dtype_t dtype,
-                                 int partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Scratch of pa_decode_noalloc: a file-scope device array (one copy per GPU,
+// held until the process ends).  Host code never passes the array's name to
+// a kernel (on the host it is only a stand-in for the symbol): its device
+// address is looked up once per device with hipGetSymbolAddress, with that
+// device current, and the looked-up pointer is what the kernels receive.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = PA_DECODE_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch size");
+__device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device (looked up on the
+// first call there), or NULL with the failing status in *st.
+void* scratch_ptr(pa_status_t* st) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    *st = pa::fail(PA_ERR_LAUNCH, "pa_decode_noalloc: no current device (or device id %d >= %d)", dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      *st = pa::fail(PA_ERR_LAUNCH, "pa_decode_noalloc: hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                     hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// pa_decode's body.  `workspace` NULL with `use_scratch`: the partials go to
+// the device's scratch array, laid out for the wavefronts this launch uses.
+pa_status_t decode_impl(const char* who, void* out, const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads,
+                        int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                        int max_context_len, float scale, pa_dtype_t dtype, int partition_size, void* workspace,
+                        size_t workspace_bytes, void* stream, bool use_scratch) {
   using namespace pa;
   clear_error();
   if (dtype != PA_FP32 && dtype != PA_FP16 && dtype != PA_BF16)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: unknown dtype %d", (int)dtype);
+    return fail(PA_ERR_UNSUPPORTED, "%s: unknown dtype %d", who, (int)dtype);
   // The kernels walk 16-slot tiles (one MFMA operand); a block holds 2^lm of them.
   int lm = -1;
   for (int k = 0; k <= 3; ++k)
     if (block_size == 16 << k) lm = k;
-  if (lm < 0) return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d (16, 32, 64 or 128)", block_size);
-  if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d (64 or 128)", head_dim);
+  if (lm < 0) return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (16, 32, 64 or 128)", who, block_size);
+  if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128)", who, head_dim);
   if (num_seqs < 0 || num_seqs > 65535)
-    return fail(PA_ERR_SHAPE, "pa_decode: num_seqs %d outside [0, 65535]", num_seqs);
+    return fail(PA_ERR_SHAPE, "%s: num_seqs %d outside [0, 65535]", who, num_seqs);
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
-    return fail(PA_ERR_SHAPE, "pa_decode: num_q_heads %d must be a positive multiple of num_kv_heads %d", num_q_heads,
+    return fail(PA_ERR_SHAPE, "%s: num_q_heads %d must be a positive multiple of num_kv_heads %d", who, num_q_heads,
                 num_kv_heads);
   if (num_blocks <= 0 || max_blocks_per_seq <= 0)
-    return fail(PA_ERR_SHAPE, "pa_decode: num_blocks %d, max_blocks_per_seq %d", num_blocks, max_blocks_per_seq);
+    return fail(PA_ERR_SHAPE, "%s: num_blocks %d, max_blocks_per_seq %d", who, num_blocks, max_blocks_per_seq);
   if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
-    return fail(PA_ERR_SHAPE, "pa_decode: max_context_len %d outside [0, max_blocks_per_seq*block_size = %lld]",
-                max_context_len, (long long)max_blocks_per_seq * block_size);
+    return fail(PA_ERR_SHAPE, "%s: max_context_len %d outside [0, max_blocks_per_seq*block_size = %lld]",
+                who, max_context_len, (long long)max_blocks_per_seq * block_size);
   const int psize = partition_size == 0 ? kDefaultPartition : partition_size;
   if (psize <= 0 || psize % 16 != 0)
-    return fail(PA_ERR_SHAPE, "pa_decode: partition_size %d must be a positive multiple of 16", partition_size);
-  if (!isfinite(scale)) return fail(PA_ERR_SHAPE, "pa_decode: scale is not finite");
+    return fail(PA_ERR_SHAPE, "%s: partition_size %d must be a positive multiple of 16", who, partition_size);
+  if (!isfinite(scale)) return fail(PA_ERR_SHAPE, "%s: scale is not finite", who);
   if (((int64_t)num_blocks * num_kv_heads << lm) > 0x7fffffffLL)
-    return fail(PA_ERR_SHAPE, "pa_decode: %d blocks of %d KV heads is too large", num_blocks, num_kv_heads);
+    return fail(PA_ERR_SHAPE, "%s: %d blocks of %d KV heads is too large", who, num_blocks, num_kv_heads);
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
-    return fail(PA_ERR_NULL, "pa_decode: NULL pointer");
+    return fail(PA_ERR_NULL, "%s: NULL pointer", who);
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
-    return fail(PA_ERR_SHAPE, "pa_decode: out, q and the pools must be 16-byte aligned");
+    return fail(PA_ERR_SHAPE, "%s: out, q and the pools must be 16-byte aligned", who);
 
   const int P = parts_for(max_context_len, psize);
   const int g = num_q_heads / num_kv_heads;
@@ -116,14 +160,37 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
   // MFMA partition kernels: 16-bit KV, partitions of at most 4096 positions
   // (a wave holds at most 64 block ids).  Everything else: the VALU kernel.
   const bool mfma = half && (use_stream || psize <= 4096);
+  // Balanced split: one workgroup of 4 independent wavefronts per CU (4
+  // wavefronts with two tiles in flight each keep a CU's share of HBM busy),
+  // and never more wavefronts than units.
+  int grid = 1;
+  if (use_stream) {
+    const int64_t units = stream_units_bound(num_seqs, num_q_heads, num_kv_heads, max_context_len, unit);
+    int64_t gr = cu_count();
+    if (gr > kStreamMaxWaves / 4) gr = kStreamMaxWaves / 4;
+    if (gr > (units + 3) / 4) gr = (units + 3) / 4;
+    grid = gr < 1 ? 1 : (int)gr;
+  }
   const WorkspaceLayout wl = workspace_layout(num_seqs, num_q_heads, head_dim, P);
-  const StreamLayout sl = stream_layout(num_seqs, num_q_heads, num_kv_heads, head_dim);
+  // The caller's workspace is sized without knowing the device (slots for
+  // kStreamMaxWaves wavefronts); the scratch array only for this launch's.
+  const StreamLayout sl =
+      stream_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, use_scratch ? (size_t)grid * 4 : kStreamMaxWaves);
   const size_t need = use_stream ? sl.total : wl.total;
+  if (use_scratch && need > 0) {
+    if (need > kScratchBytes)
+      return fail(PA_ERR_WORKSPACE, "%s: these sizes need %zu bytes of scratch, more than its %zu", who, need,
+                  kScratchBytes);
+    pa_status_t sst = PA_OK;
+    workspace = scratch_ptr(&sst);
+    if (!workspace) return sst;
+    workspace_bytes = kScratchBytes;
+  }
   if (need > 0) {
-    if (!workspace) return fail(PA_ERR_WORKSPACE, "pa_decode: needs %zu bytes of workspace, got NULL", need);
+    if (!workspace) return fail(PA_ERR_WORKSPACE, "%s: needs %zu bytes of workspace, got NULL", who, need);
     if (workspace_bytes < need)
-      return fail(PA_ERR_WORKSPACE, "pa_decode: needs %zu bytes of workspace, got %zu", need, workspace_bytes);
-    if (!aligned(workspace, 256)) return fail(PA_ERR_WORKSPACE, "pa_decode: workspace must be 256-byte aligned");
+      return fail(PA_ERR_WORKSPACE, "%s: needs %zu bytes of workspace, got %zu", who, need, workspace_bytes);
+    if (!aligned(workspace, 256)) return fail(PA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", who);
   }
 
   DecodeArgs a{};
@@ -164,15 +231,8 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
   a.lm = lm;
   a.stream = use_stream;
   if (use_stream) {
-    // One workgroup of 4 independent wavefronts per CU (4 wavefronts with
-    // two tiles in flight each keep a CU's share of HBM busy), and never
-    // more wavefronts than units.
     a.unit = unit;
-    const int64_t units = stream_units_bound(num_seqs, num_q_heads, num_kv_heads, max_context_len, unit);
-    int64_t grid = cu_count();
-    if (grid > kStreamMaxWaves / 4) grid = kStreamMaxWaves / 4;
-    if (grid > (units + 3) / 4) grid = (units + 3) / 4;
-    a.grid = grid < 1 ? 1 : (int)grid;
+    a.grid = grid;
     a.entries = 1;
   } else {
     // Partitions of up to 64 blocks: one wavefront each, and the
@@ -181,8 +241,8 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
     a.per_entry = a.wave_part ? 4 : 1;
     a.entries = (P + a.per_entry - 1) / a.per_entry;
     if ((int64_t)a.entries * num_kv_heads * a.nsub * num_seqs > 0x7fffffffLL)
-      return fail(PA_ERR_SHAPE, "pa_decode: launch of %lld workgroups is too large",
-                  (long long)a.entries * num_kv_heads * a.nsub * num_seqs);
+      return fail(PA_ERR_SHAPE, "%s: launch of %lld workgroups is too large",
+                  who, (long long)a.entries * num_kv_heads * a.nsub * num_seqs);
   }
 
   const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -196,6 +256,28 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
   else if (a.entries > 1)
     launch_decode_reduce(a, st);
   const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "pa_decode: launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "%s: launch failed: %s", who, hipGetErrorString(e));
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                                 int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                 int max_blocks_per_seq, int max_context_len, float scale, pa_dtype_t dtype,
+                                 int partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl("pa_decode", out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
+                     partition_size, workspace, workspace_bytes, stream, false);
+}
+
+extern "C" pa_status_t pa_decode_noalloc(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                         const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                                         int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                         int num_blocks, int max_blocks_per_seq, int max_context_len, float scale,
+                                         pa_dtype_t dtype, int partition_size, void* stream) {
+  return decode_impl("pa_decode_noalloc", out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
+                     partition_size, nullptr, 0, stream, true);
 }

@@ -69,14 +69,15 @@ constexpr int kStreamMaxWaves = 4096;
 inline int mfma_gmax(int g) { return g <= 4 ? 4 : g <= 8 ? 8 : 16; }
 
 // Workspace of the balanced split: pieces (o [slot][gmax][D], m and l
-// [slot][gmax]) for 2 * kStreamMaxWaves slots, then the segment records.
+// [slot][gmax]) for two slots per wavefront (2 * kStreamMaxWaves when the
+// device is not known), then the segment records.
 struct StreamLayout {
   size_t o_off, m_off, l_off, info_off, total;
 };
 
-inline StreamLayout stream_layout(size_t B, size_t Hq, size_t Hkv, size_t D) {
+inline StreamLayout stream_layout(size_t B, size_t Hq, size_t Hkv, size_t D, size_t max_waves = kStreamMaxWaves) {
   const size_t g = Hq / Hkv, gmax = (size_t)mfma_gmax((int)g), nsub = (g + gmax - 1) / gmax;
-  const size_t slots = 2 * (size_t)kStreamMaxWaves;
+  const size_t slots = 2 * max_waves;
   StreamLayout w{};
   w.o_off = 0;
   w.m_off = align256(slots * gmax * D * sizeof(float));
