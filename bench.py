@@ -223,7 +223,8 @@ def pmc_summary(args):
     from workloads import make_workload
 
     dec = lambda n: ("decode_stream" in n and "reduce" not in n) or "decode_part" in n
-    copy = lambda n: "copy" in n.lower() or "elementwise" in n.lower()
+    # the 1 GiB device copy itself (not the fill that creates its source)
+    copy = lambda n: "copybuffer" in n.lower() or ("copy" in n.lower() and "fill" not in n.lower())
     rd, nf = _counter_means(args.pmc_summary[0], dec)
     wr, _ = _counter_means(args.pmc_summary[1], dec)
     crd, _ = _counter_means(args.pmc_summary[2], copy)

@@ -159,11 +159,12 @@ struct Tile {
 
   // One (block, head) tile at `kb` / `vb`, non-temporal loads.  Offsets are
   // unsigned 32-bit so the loads take the scalar tile base plus a 32-bit
-  // vector offset.  V rows past `rmax` (the block's last filled slot)
-  // re-read that row: their weights are exactly 0 and the values are finite.
+  // vector offset.  K and V rows past `rmax` (the block's last filled slot)
+  // re-read that row (same cache lines, no extra memory traffic): their
+  // scores are masked, their weights exactly 0, and the values are finite.
   __device__ static __forceinline__ void load(const char* kb, const char* vb, int grp, int col, int rmax,
                                               uint4 (&kr)[KS], VVec (&vr)[4]) {
-    const uint32_t k_lane = col * ROWB + grp * 16;
+    const uint32_t k_lane = min(col, rmax) * ROWB + grp * 16;
     const uint32_t v_col = col * DPL * 2;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
