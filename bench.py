@@ -215,6 +215,30 @@ def _write_bytes(c):
     return 64 * c["TCC_EA0_WRREQ_64B_sum"] + 32 * (c["TCC_EA0_WRREQ_sum"] - c["TCC_EA0_WRREQ_64B_sum"])
 
 
+FUSE_MAX_KV_BYTES = 2 << 30  # pa_write_kv_decode's bound for the fused form (include/pa.h)
+
+
+def write_fused_in_kernel(w):
+    """Whether pa_write_kv_decode does its write inside the stream kernel for
+    workload `w` (the choice include/pa.h states: 16-bit KV, up to 4096
+    sequences, at most 2 GiB of K+V over num_seqs x max_context_len, no
+    kernel override); otherwise a launch of its own writes first."""
+    eb = {"fp32": 4, "fp16": 2, "bf16": 2}[w.dtype]
+    bound = w.num_seqs * w.max_context_len * w.num_kv_heads * w.head_dim * eb * 2
+    return (w.dtype != "fp32" and w.num_seqs <= 4096 and bound <= FUSE_MAX_KV_BYTES
+            and os.environ.get("PA_DECODE_KERNEL", "") in ("", "auto"))
+
+
+def main_kernel_bytes(w):
+    """Algorithmic bytes of the step's main kernel: the attention's, plus the
+    new rows read and written when the write runs inside it."""
+    from paged_kv_cache_117_amd import metrics
+
+    eb = metrics.ELEM_BYTES[w.dtype]
+    f = metrics.write_decode_io_bytes if write_fused_in_kernel(w) else metrics.decode_io_bytes
+    return f(w.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, eb, w.block_size)
+
+
 def pmc_summary(args):
     """HBM bytes per launch of the dominant decode kernel from the TCC request
     counters, each direction scaled by what the same counters read for a
@@ -222,7 +246,11 @@ def pmc_summary(args):
     from paged_kv_cache_117_amd import metrics
     from workloads import make_workload
 
-    dec = lambda n: ("decode_stream" in n and "reduce" not in n) or "decode_part" in n
+    w = make_workload(args.config, block_size=args.block_size)
+    # the step's main kernel: the stream kernel in the form the step runs
+    # (the bench's other passes also run plain pa_decode)
+    variant = ", true>" if write_fused_in_kernel(w) else ", false>"
+    dec = lambda n: ("decode_stream<" in n and variant in n) or "decode_part" in n
     # the 1 GiB device copy itself (not the fill that creates its source)
     copy = lambda n: "copybuffer" in n.lower() or ("copy" in n.lower() and "fill" not in n.lower())
     rd, nf = _counter_means(args.pmc_summary[0], dec)
@@ -235,9 +263,8 @@ def pmc_summary(args):
     read_b = _read_bytes(rd)
     write_b = _write_bytes(wr)
     psize = args.partition_size if args.partition_size is not None else WORKLOAD_PARTITION.get(args.config, 0)
-    w = make_workload(args.config, block_size=args.block_size)
     eb = metrics.ELEM_BYTES[w.dtype]
-    io = metrics.decode_io_bytes(w.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, eb, w.block_size)
+    io = main_kernel_bytes(w)
     kv = metrics.decode_kv_bytes(w.context_lens, w.num_kv_heads, w.head_dim, eb)
     traffic = read_b * r_scale + write_b * w_scale
     rec = {
@@ -327,6 +354,21 @@ def call_pass(torch, step, steps, R, evs):
         step(i % R, evs[i])
     torch.cuda.synchronize()
     return np.array([a.elapsed_time(b) for a, b in evs])
+
+
+def block_pass(torch, fn, steps, R, stream):
+    """Mean duration (ms) of fn(i % R) over `steps` back-to-back calls between
+    one event pair (after a few untimed ones), so no event sits between calls."""
+    for i in range(max(5, steps // 4)):
+        fn(i % R)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(steps):
+        fn(i % R)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
 
 
 def main_kernel_pass(torch, step, steps, R, kevs):
@@ -793,21 +835,42 @@ def decode_bench(torch, key, args, partition_size, steps, warmup, cpu_budget):
     stream = torch.cuda.current_stream()
 
     def step(r, ev=None, kev=None):
+        """The step as one call: pa_write_kv_decode stores each sequence's new
+        K/V at its last position and attends (after the copy-on-write copies)."""
+        s = sets[r]
+        if s["pairs"] is not None:
+            pa.copy_blocks(k_pool, v_pool, s["pairs"], stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        if kev is not None:
+            pa.time_next_main_kernel(*kev)  # events around the main kernel alone
+        pa.write_kv_decode(q, k_pool, v_pool, k_new, v_new, s["tables"], lens, w.scale, w.max_context_len,
+                           out=s["out"], partition_size=partition_size, workspace=s["ws"], stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    def call(r):
+        """pa_write_kv_decode alone (no copies)."""
+        s = sets[r]
+        pa.write_kv_decode(q, k_pool, v_pool, k_new, v_new, s["tables"], lens, w.scale, w.max_context_len,
+                           out=s["out"], partition_size=partition_size, workspace=s["ws"], stream=stream)
+
+    def decode_only(r):
+        """pa_decode alone (the attention of the unfused step)."""
+        s = sets[r]
+        pa.decode(q, k_pool, v_pool, s["tables"], lens, w.scale, w.max_context_len, out=s["out"],
+                  partition_size=partition_size, workspace=s["ws"], stream=stream)
+
+    def step_unfused(r):
+        """The same step as separate calls: pa_write_kv, then pa_decode."""
         s = sets[r]
         if s["pairs"] is not None:
             pa.copy_blocks(k_pool, v_pool, s["pairs"], stream=stream)
         pa.write_kv(k_pool, v_pool, k_new, v_new, s["slots"], stream=stream)
-        if ev is not None:
-            ev[0].record(stream)
-        if kev is not None:
-            pa.time_next_main_kernel(*kev)  # events around the main decode kernel alone
-        pa.decode(q, k_pool, v_pool, s["tables"], lens, w.scale, w.max_context_len, out=s["out"],
-                  partition_size=partition_size, workspace=s["ws"], stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+        decode_only(r)
 
     warmup = warm_up(torch, lambda i: step(i % R), warmup)
-    evs, kevs = timing_events(torch, steps, stream)
+    _, kevs = timing_events(torch, steps, stream)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -819,17 +882,24 @@ def decode_bench(torch, key, args, partition_size, steps, warmup, cpu_budget):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
-    dec_ms = call_pass(torch, step, steps, R, evs)
-    kern_avg = main_kernel_pass(torch, step, steps, R, kevs)
     ms_step = total_ms / steps
+    # passes of their own after the timed region (same sets): the library
+    # calls back to back, the unfused step, the main kernel alone
+    call_ms = block_pass(torch, call, steps, R, stream)
+    decode_only_ms = block_pass(torch, decode_only, steps, R, stream)
+    ms_step_unfused = block_pass(torch, step_unfused, steps, R, stream)
+    kern_avg = main_kernel_pass(torch, step, steps, R, kevs)
 
     kv_bytes = metrics.decode_kv_bytes(w.context_lens, w.num_kv_heads, w.head_dim, eb)
     unique_kv_bytes = metrics.decode_unique_kv_bytes(tables, w.context_lens, w.num_kv_heads, w.head_dim, eb,
                                                      w.block_size)
-    io_bytes = metrics.decode_io_bytes(w.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, eb,
-                                       w.block_size)
+    io_bytes = main_kernel_bytes(w)
+    call_io_bytes = metrics.write_decode_io_bytes(w.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, eb,
+                                                  w.block_size)
+    dec_io_bytes = metrics.decode_io_bytes(w.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, eb,
+                                           w.block_size)
     value = kv_bytes / (ms_step * 1e-3) / 1e9
-    dec_avg = float(dec_ms.mean())
+    dec_avg = call_ms
     achieved = io_bytes / (kern_avg * 1e-3) / 1e9
     res = {
         "value": round(value, 2),
@@ -851,13 +921,22 @@ def decode_bench(torch, key, args, partition_size, steps, warmup, cpu_budget):
         },
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
         "seq_steps_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
+        # the step as separate pa_write_kv + pa_decode calls (same sets, own timed region)
+        "unfused_ms_per_step": round(ms_step_unfused, 5),
+        "unfused_hbm_peak_frac": round(kv_bytes / (ms_step_unfused * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        # the pa_write_kv_decode call (its main kernel + the merge of cut
+        # sequences; the write inside the kernel, or a launch of its own beyond
+        # the fused form's size bound), back to back
         "decode_ms": round(dec_avg, 5),
-        "decode_ms_median": round(float(np.median(dec_ms)), 5),
         "decode_kv_gbps": round(kv_bytes / (dec_avg * 1e-3) / 1e9, 2),
+        # pa_decode alone (attention only, the new tokens already in the pool), back to back
+        "pa_decode_ms": round(decode_only_ms, 5),
+        "pa_decode_hbm_frac": round(dec_io_bytes / (decode_only_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         # the main kernel alone (events the library records right around it;
         # the whole call adds the merge kernel and the gap before it)
         "decode_main_kernel_ms": round(kern_avg, 5),
-        "decode_call_hbm_frac": round(io_bytes / (dec_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "decode_call_hbm_frac": round(call_io_bytes / (dec_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "write_fused_in_kernel": write_fused_in_kernel(w),
         # distinct physical blocks read (shared prefix blocks once): equals the
         # logical rate unless sequences share blocks
         "decode_unique_kv_gbps": round(unique_kv_bytes / (dec_avg * 1e-3) / 1e9, 2),
@@ -867,7 +946,7 @@ def decode_bench(torch, key, args, partition_size, steps, warmup, cpu_budget):
                                      if key in MODEL_LAYERS else None),
         "wall_s": round(wall, 3),
         "roofline": {
-            "kernel": "pa_decode main kernel (%s)" % main_kernel_label(w.dtype, w.num_seqs),
+            "kernel": "pa_write_kv_decode main kernel (%s)" % main_kernel_label(w.dtype, w.num_seqs),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
@@ -972,8 +1051,9 @@ def main():
     if args.config == "c2" and not args.no_second:
         sub = decode_bench(torch, "c5", args, WORKLOAD_PARTITION["c5"], args.steps, args.warmup, 0.0)
         res["c5"] = {k: sub[k] for k in ("value", "hbm_peak_frac", "ms_per_step", "seq_steps_per_s", "decode_ms",
-                                          "decode_main_kernel_ms", "decode_call_hbm_frac", "roofline",
-                                          "traffic_note", "warmup", "steps", "dtype")}
+                                          "decode_main_kernel_ms", "decode_call_hbm_frac", "pa_decode_ms",
+                                          "pa_decode_hbm_frac", "unfused_ms_per_step", "unfused_hbm_peak_frac",
+                                          "roofline", "traffic_note", "warmup", "steps", "dtype")}
         res["c5"]["workload"] = sub["config"]["workload"]
         res["c5"]["kv_bytes_per_step"] = sub["config"]["kv_bytes_per_step"]
         res["c5"]["partition_size"] = sub["config"]["partition_size"]

@@ -125,6 +125,44 @@ pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* 
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_write_kv_decode -- one decode step in one launch: each sequence's new
+ * token is written into the pool and attended to, as pa_write_kv followed
+ * by pa_decode would do, with the write fused into the attention kernel
+ * (PagedAttention and vLLM: Paging the KV Cache Like an OS, "Step 5": the
+ * write kernels are fused to cut launch overhead; PagedAttention
+ * (tensortonic), "5. Reading the Cache During Attention": the new key and
+ * value go to their block and offset, then the query attends to every valid
+ * position including the new one).
+ *
+ * For each sequence s with 1 <= L = context_lens[s] <= max_context_len, the
+ * new token is position L-1: its K and V rows k_new[s][h][:], v_new[s][h][:]
+ * are stored at block block_tables[s][(L-1) / block_size], slot
+ * (L-1) % block_size, for every KV head h, and out[s] is pa_decode's
+ * attention over positions 0..L-1 of the pool after that store.  The result
+ * is bit-identical to pa_write_kv with slot_mapping[s] = that slot followed
+ * by pa_decode with the same partition_size.  Sequences with L = 0, an
+ * out-of-range L or an out-of-range block id at position L-1 write nothing
+ * (their outputs are as in pa_decode: zero or NaN).
+ *
+ *   k_pool, v_pool   device, written at the new tokens' slots, read elsewhere
+ *   k_new, v_new     device, [num_seqs][num_kv_heads][head_dim], dtype; read
+ * All other arguments, the workspace (pa_decode_workspace_bytes) and the
+ * errors are pa_decode's.  The new tokens' slots must be distinct (each
+ * sequence owns its last block, which the block manager guarantees by
+ * copy-on-write).  With 16-bit KV, up to 4096 sequences and at most 2 GiB of
+ * K and V in num_seqs * max_context_len positions, the write is done by the
+ * attention kernel itself; otherwise (where the fused kernel's small cost
+ * per tile outweighs one launch) by a separate launch before it.
+ */
+pa_status_t pa_write_kv_decode(void* out, const void* q, void* k_pool, void* v_pool,
+                               const void* k_new, const void* v_new,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                               int block_size, int num_blocks, int max_blocks_per_seq,
+                               int max_context_len, float scale, pa_dtype_t dtype, int partition_size,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc).  Same arguments, results and errors as pa_decode minus

@@ -7,6 +7,7 @@ the library and fails with ImportError when it has not been built.
     decode(q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len)
     prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale, max_query_len, max_context_len)
     write_kv(k_pool, v_pool, k_new, v_new, slot_mapping)
+    write_kv_decode(q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, scale, max_context_len)
     copy_blocks(k_pool, v_pool, block_pairs)
     swap_blocks(dst_k, dst_v, src_k, src_v, block_pairs)   # device <-> pinned host pool
     BlockManager(num_blocks, block_size=16, free_order=None)
@@ -26,4 +27,5 @@ from .ops import (  # noqa: F401
     swap_blocks,
     time_next_main_kernel,
     write_kv,
+    write_kv_decode,
 )

@@ -27,6 +27,8 @@ _pi64 = _c.POINTER(_c.c_int64)
 SIGNATURES = {
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                          _f32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_write_kv_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                  _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
     "pa_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                  _f32, _i32, _i32, _vp]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),

@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "decode_kernels.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -63,6 +64,37 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(char* __restrict_
   uint4* d = reinterpret_cast<uint4*>(pool + (size_t)dst * block_bytes);
   const size_t n = block_bytes >> 4;
   for (size_t v = (size_t)blockIdx.y * kThreads + threadIdx.x; v < n; v += (size_t)gridDim.y * kThreads) d[v] = s[v];
+}
+
+// The fused step's write when its decode does not run the stream kernel:
+// each sequence's new K and V rows (k_new[s], v_new[s]) go to its last
+// position L-1, found through its block table (one workgroup per
+// sequence).  Sequences with L outside [1, max_ctx] or an out-of-range block
+// id write nothing.
+__global__ __launch_bounds__(kThreads) void write_last_kernel(char* __restrict__ kp, char* __restrict__ vp,
+                                                              const char* __restrict__ kn,
+                                                              const char* __restrict__ vn,
+                                                              const int32_t* __restrict__ bt,
+                                                              const int32_t* __restrict__ cl, int maxb, int max_ctx,
+                                                              int num_kv_heads, int row_bytes, int lbs,
+                                                              int num_blocks) {
+  const int s = blockIdx.x;
+  const int L = cl[s];
+  if (L < 1 || L > max_ctx) return;
+  const int pos = L - 1;
+  const int blk = bt[(size_t)s * maxb + (pos >> lbs)];
+  if (blk < 0 || blk >= num_blocks) return;
+  const int off = pos & ((1 << lbs) - 1);
+  const int per_row = row_bytes >> 4;
+  const int n = num_kv_heads * per_row;
+  for (int v = threadIdx.x; v < n; v += kThreads) {
+    const int h = v / per_row;
+    const int c = v - h * per_row;
+    const size_t dst = ((((size_t)blk * num_kv_heads + h) << lbs) + off) * (size_t)row_bytes + (size_t)c * 16;
+    const size_t src = ((size_t)s * num_kv_heads + h) * (size_t)row_bytes + (size_t)c * 16;
+    *reinterpret_cast<uint4*>(kp + dst) = *reinterpret_cast<const uint4*>(kn + src);
+    *reinterpret_cast<uint4*>(vp + dst) = *reinterpret_cast<const uint4*>(vn + src);
+  }
 }
 
 // Whole-block copies between two pools (device or pinned host memory, same
@@ -110,6 +142,15 @@ int elem_bytes(pa_dtype_t dt) { return dt == PA_FP32 ? 4 : (dt == PA_FP16 || dt 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
+
+void launch_write_last(void* k_pool, void* v_pool, const void* k_new, const void* v_new, const int32_t* bt,
+                       const int32_t* cl, int num_seqs, int maxb, int max_ctx, int num_kv_heads, int head_dim,
+                       int elem_bytes, int lbs, int num_blocks, hipStream_t st) {
+  hipLaunchKernelGGL(write_last_kernel, dim3(num_seqs), dim3(kThreads), 0, st, (char*)k_pool, (char*)v_pool,
+                     (const char*)k_new, (const char*)v_new, bt, cl, maxb, max_ctx, num_kv_heads,
+                     head_dim * elem_bytes, lbs, num_blocks);
+}
+
 }  // namespace pa
 
 extern "C" pa_status_t pa_write_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new,

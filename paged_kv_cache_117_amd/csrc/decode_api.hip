@@ -15,6 +15,9 @@
 namespace {
 
 constexpr int kDefaultPartition = 512;
+// pa_write_kv_decode fuses the write into the stream kernel up to this many
+// KV bytes per launch (bounded by num_seqs * max_context_len).
+constexpr uint64_t kFuseMaxKvBytes = 2ull << 30;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -114,7 +117,8 @@ pa_status_t decode_impl(const char* who, void* out, const void* q, const void* k
                         const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads,
                         int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
                         int max_context_len, float scale, pa_dtype_t dtype, int partition_size, void* workspace,
-                        size_t workspace_bytes, void* stream, bool use_scratch) {
+                        size_t workspace_bytes, void* stream, bool use_scratch, const void* k_new = nullptr,
+                        const void* v_new = nullptr) {
   using namespace pa;
   clear_error();
   if (dtype != PA_FP32 && dtype != PA_FP16 && dtype != PA_BF16)
@@ -142,10 +146,12 @@ pa_status_t decode_impl(const char* who, void* out, const void* q, const void* k
   if (((int64_t)num_blocks * num_kv_heads << lm) > 0x7fffffffLL)
     return fail(PA_ERR_SHAPE, "%s: %d blocks of %d KV heads is too large", who, num_blocks, num_kv_heads);
   if (num_seqs == 0) return PA_OK;
-  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
+  const bool fused = k_new != nullptr || v_new != nullptr;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || (fused && (!k_new || !v_new)))
     return fail(PA_ERR_NULL, "%s: NULL pointer", who);
-  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
-    return fail(PA_ERR_SHAPE, "%s: out, q and the pools must be 16-byte aligned", who);
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      (fused && (!aligned(k_new, 16) || !aligned(v_new, 16))))
+    return fail(PA_ERR_SHAPE, "%s: out, q, the pools and the new rows must be 16-byte aligned", who);
 
   const int P = parts_for(max_context_len, psize);
   const int g = num_q_heads / num_kv_heads;
@@ -153,10 +159,10 @@ pa_status_t decode_impl(const char* who, void* out, const void* q, const void* k
   // Units are single blocks unless a partition size is given.
   const bool half = dtype != PA_FP32 && !force_valu();
   const int unit = partition_size == 0 ? 1 : psize / 16;
-  // (its tile descriptors hold the tile row ((block * num_kv_heads + head) << lm) + tile in 28 bits)
+  // (its tile descriptors hold the tile row ((block * num_kv_heads + head) << lm) + tile in 27 bits)
   const bool use_stream = half && num_seqs <= kStreamMaxSeqs && !force_partition() &&
                           stream_units_bound(num_seqs, num_q_heads, num_kv_heads, max_context_len, unit) < (1 << 30) &&
-                          ((int64_t)num_blocks * num_kv_heads << lm) < (1 << 28);
+                          ((int64_t)num_blocks * num_kv_heads << lm) < (1 << 27);
   // MFMA partition kernels: 16-bit KV, partitions of at most 4096 positions
   // (a wave holds at most 64 block ids).  Everything else: the VALU kernel.
   const bool mfma = half && (use_stream || psize <= 4096);
@@ -246,6 +252,27 @@ pa_status_t decode_impl(const char* who, void* out, const void* q, const void* k
   }
 
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (fused) {
+    // The stream kernel's fused form costs a little on every tile (address
+    // selects for the one tile per sequence that holds its new token); the
+    // separate write launch costs a fixed ~4 us.  Measured on MI355X, fusing
+    // pays up to about 2 GiB of KV per launch (the Llama-3.1-8B layer at 64
+    // sequences: +2% per step) and not beyond (the Qwen2.5-72B layer at 128
+    // sequences of 4k-8k: -0.3%); the bound uses max_context_len.  Both forms
+    // give identical bits.  (The kernel also addresses the new rows with
+    // 32-bit byte offsets.)
+    const int eb = dtype == PA_FP32 ? 4 : 2;
+    const uint64_t kv_bound = (uint64_t)num_seqs * max_context_len * num_kv_heads * head_dim * eb * 2;
+    if (use_stream && kv_bound <= kFuseMaxKvBytes && (uint64_t)num_seqs * num_kv_heads * head_dim * eb < (1ull << 32)) {
+      // the stream kernel writes each sequence's new rows and attends to them
+      a.kn = static_cast<const char*>(k_new);
+      a.vn = static_cast<const char*>(v_new);
+    } else {
+      launch_write_last(const_cast<void*>(k_pool), const_cast<void*>(v_pool), k_new, v_new, block_tables,
+                        context_lens, num_seqs, max_blocks_per_seq, max_context_len, num_kv_heads, head_dim, eb,
+                        4 + lm, num_blocks, st);
+    }
+  }
   take_main_kernel_events(&a.ev_start, &a.ev_stop);
   if (mfma)
     launch_decode_mfma(a, st);
@@ -270,6 +297,21 @@ extern "C" pa_status_t pa_decode(void* out, const void* q, const void* k_pool, c
   return decode_impl("pa_decode", out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_q_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
                      partition_size, workspace, workspace_bytes, stream, false);
+}
+
+extern "C" pa_status_t pa_write_kv_decode(void* out, const void* q, void* k_pool, void* v_pool, const void* k_new,
+                                          const void* v_new, const int32_t* block_tables, const int32_t* context_lens,
+                                          int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                          int block_size, int num_blocks, int max_blocks_per_seq,
+                                          int max_context_len, float scale, pa_dtype_t dtype, int partition_size,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!k_new || !v_new) {
+    pa::clear_error();
+    return pa::fail(PA_ERR_NULL, "pa_write_kv_decode: NULL pointer");
+  }
+  return decode_impl("pa_write_kv_decode", out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
+                     partition_size, workspace, workspace_bytes, stream, false, k_new, v_new);
 }
 
 extern "C" pa_status_t pa_decode_noalloc(void* out, const void* q, const void* k_pool, const void* v_pool,

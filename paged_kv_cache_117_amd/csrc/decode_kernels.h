@@ -35,6 +35,11 @@ struct DecodeArgs {
   // KV).  B is then the number of query tokens, qst the [nseq + 1] row starts.
   const int32_t* qst;
   int nseq, max_q;
+  // Fused write (stream kernel): the step's new K/V rows [B][Hkv][D], read
+  // for each sequence's last position and stored into its pool slot; NULL
+  // for plain decode.
+  const char* kn;
+  const char* vn;
   // Caller's timing events for the main kernel (hipEvent_t, or NULL): passed
   // to its launch, so they take the kernel's own start and end.
   void* ev_start;
@@ -92,5 +97,12 @@ void launch_decode_valu(const DecodeArgs& a, hipStream_t st);   // any dtype
 void launch_decode_mfma(const DecodeArgs& a, hipStream_t st);   // fp16 / bf16, main kernel only
 void launch_decode_reduce(const DecodeArgs& a, hipStream_t st);
 void launch_decode_stream_reduce(const DecodeArgs& a, hipStream_t st);  // the balanced split's merge
+
+// Each sequence's new K/V rows to its last position through its block table
+// (the fused write and decode, when the decode runs another kernel than the
+// even split).  Launched on `st`.
+void launch_write_last(void* k_pool, void* v_pool, const void* k_new, const void* v_new, const int32_t* bt,
+                       const int32_t* cl, int num_seqs, int maxb, int max_ctx, int num_kv_heads, int head_dim,
+                       int elem_bytes, int lbs, int num_blocks, hipStream_t st);
 
 }  // namespace pa

@@ -184,6 +184,56 @@ struct Tile {
     }
   }
 
+  // The same tile for the fused write and decode: when `is_new` (the tile
+  // holds its sequence's last position, slot `rmax`, whose K and V rows are
+  // still at `knew` / `vnew`), rows at and past `rmax` come from there
+  // instead of the pool, so the tile computes exactly what it computes once
+  // the rows are in the pool.  Branch-free (per-lane address selects, the
+  // same load instructions for every tile): a branch here would define the
+  // tile registers on two paths and the copies at the join would make every
+  // tile wait for all loads in flight.
+  __device__ static __forceinline__ void load_sel(const char* kb, const char* vb, const char* knew, const char* vnew,
+                                                  bool is_new, int grp, int col, int rmax, uint4 (&kr)[KS],
+                                                  VVec (&vr)[4]) {
+    const char* kl = ((is_new && col >= rmax) ? knew : kb + (uint32_t)min(col, rmax) * ROWB) + grp * 16;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kl + k * 64));
+      kr[k] = make_uint4(t.x, t.y, t.z, t.w);
+    }
+    const uint32_t v_col = col * DPL * 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = min(grp * 4 + i, rmax);
+      const char* pv = ((is_new && r == rmax) ? vnew : vb + (uint32_t)r * ROWB) + v_col;
+      if constexpr (DPL == 8) {
+        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pv));
+        vr[i] = make_uint4(t.x, t.y, t.z, t.w);
+      } else {
+        const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(pv));
+        vr[i] = make_uint2(t.x, t.y);
+      }
+    }
+  }
+
+  // The new token's K and V rows of a tile loaded by load_sel, from the
+  // lanes that hold them, to slot `rmax` of the tile at `kb` / `vb`: lanes
+  // with col = rmax hold its K row (16 bytes per k-step and lane group),
+  // lanes of group rmax / 4 its V row (this lane's dims).
+  __device__ static __forceinline__ void store_new(char* kb, char* vb, int grp, int col, int rmax,
+                                                   const uint4 (&kr)[KS], const VVec (&vr)[4]) {
+    if (col == rmax) {
+#pragma unroll
+      for (int k = 0; k < KS; ++k) *reinterpret_cast<uint4*>(kb + (uint32_t)rmax * ROWB + grp * 16 + k * 64) = kr[k];
+    }
+    // (one predicated store per row slot, each with a static index: a
+    // selected vr[rmax & 3] would become a dynamic index, and the compiler
+    // would then keep the V tile in LDS)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (grp * 4 + i == rmax) *reinterpret_cast<VVec*>(vb + (uint32_t)rmax * ROWB + col * DPL * 2) = vr[i];
+  }
+
   // Scores (MFMA), online-softmax update, PV (MFMA) for one tile whose first
   // slot in this lane's group is token `tok0`; tokens at or past `lim` get
   // score -inf.  The QK B operand is read from the LDS query tile (`qsrc`:
@@ -673,23 +723,32 @@ struct Piece {
   int kvh;    // KV head
   int rb;     // last filled slot of chunk tile kk: min(15, rb - 16 kk)
   int kb;     // first chunk tile
+  int nrow;   // row of the sequence's new token for this KV head in k_new / v_new (s * Hkv + kvh)
 };
-constexpr int kWhole = 1, kEnds = 2, kFirstUnit = 4, kLastSlot = 8, kStarts = 16;
+constexpr int kWhole = 1, kEnds = 2, kFirstUnit = 4, kLastSlot = 8, kStarts = 16, kWriter = 32;
 
-template <int DT, int D, int GMAX>
-__global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, const void* __restrict__ q,
+// Tile descriptor in LDS: (tile row << 5) | (new-token tile << 4) | last filled slot.
+constexpr int kDescNew = 16;
+
+// One workgroup of four wavefronts per CU, one wavefront per SIMD: the
+// register file is the wave's alone (the compiler may use up to 512 VGPRs).
+template <int DT, int D, int GMAX, bool kFuse>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_stream(
+    void* __restrict__ out, const void* __restrict__ q,
                                                     const char* kp, const char* vp, const int32_t* __restrict__ bt,
                                                     const int32_t* __restrict__ cl, float* __restrict__ pc_o,
                                                     float* __restrict__ pc_m, float* __restrict__ pc_l,
                                                     int2* __restrict__ info, int B, int Hq, int Hkv, int g, int nsub,
                                                     int num_blocks, int maxb, int max_ctx, float qscale, int unit,
-                                                    int lm) {
+                                                    int lm, const char* kn, const char* vn) {
   using T = Tile<DT, D>;
   constexpr int KS = T::KS, DPL = T::DPL, ROWB = T::ROWB, QROW = T::QROW, QCH = T::QCH;
   using VVec = typename T::VVec;
   static_assert(GMAX <= 16, "one MFMA column per query head");
   __shared__ int s_len[kStreamMaxSeqs];  // context length, -1 when out of range
   __shared__ unsigned s_desc[kWaves][kChunkTiles];
+  // fused write: byte offset of each chunk tile's new-token row in k_new / v_new
+  __shared__ unsigned s_nrow[kFuse ? kWaves : 1][kFuse ? kChunkTiles : 1];
   __shared__ Piece s_pc[kWaves][kChunkPieces];
   __shared__ unsigned char s_own[kWaves][kChunkTiles];   // piece of each chunk tile
   __shared__ unsigned char s_qown[kWaves][kChunkQRows];  // piece of each query row
@@ -769,9 +828,11 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
   // of following it).  Lane 0 holds tile tb0's entry, lane 1 the next one
   // (clamped to the sequence's tiles; used only when that tile is in the
   // wave's first piece).
+  const int s0 = s;  // (the planning walker moves s on)
   const int L0 = uni(s_len[s]);
   const int tb0 = uin * unit;
   const int kvh0 = nsub == 1 ? hsub : hsub / nsub;
+  const int nt0_seq = (L0 + 15) >> 4;  // 16-slot tiles of s; the last holds its new token
   const int pre_id = bt[(size_t)s * maxb + (min(tb0 + (lane & 1), ((L0 + 15) >> 4) - 1) >> lm)];
   bool first_chunk = true;
 
@@ -833,7 +894,7 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
         const bool whole = uinj == 0 && kj == usj;
         const bool firstj = first && pidx == 0;
         int flags = (whole ? kWhole : 0) | (tbj + ctk == t1j ? kEnds : 0) | (firstj ? 0 : kLastSlot) |
-                    (tdj == 0 ? kStarts : 0);
+                    (tdj == 0 ? kStarts : 0) | (subj == 0 ? kWriter : 0);
         int np = 1;
         if (uinj == 0) {
           flags |= kFirstUnit;
@@ -857,6 +918,7 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
         pc.kvh = kvhj;
         pc.rb = Lj - 1 - (tbj - KBj) * 16;
         pc.kb = KBj;
+        pc.nrow = sj * Hkv + kvhj;
         for (int r = 0; r < nhj; ++r) s_qown[wave][QRj + r] = (unsigned char)pidx;
       }
       // Advance the walker: into the piece cut by the tile limit, else to
@@ -923,18 +985,28 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
         const int tb1 = ntc == 1 ? tb0 : tb0 + 1;
         int idA = __builtin_amdgcn_readlane(pre_id, 0);
         int idB = __builtin_amdgcn_readlane(pre_id, ntc == 1 ? 0 : 1);
-        idA = (idA >= 0 && idA < num_blocks) ? idA : 0;
-        idB = (idB >= 0 && idB < num_blocks) ? idB : 0;
+        const bool okA = idA >= 0 && idA < num_blocks, okB = idB >= 0 && idB < num_blocks;
+        const bool newA = kFuse && okA && tb0 == nt0_seq - 1, newB = kFuse && okB && tb1 == nt0_seq - 1;
+        idA = okA ? idA : 0;
+        idB = okB ? idB : 0;
         const unsigned mask = (1u << lm) - 1u;
         const unsigned rowA = ((unsigned)(idA * Hkv + kvh0) << lm) | ((unsigned)tb0 & mask);
         const unsigned rowB = ((unsigned)(idB * Hkv + kvh0) << lm) | ((unsigned)tb1 & mask);
+        const size_t nrow0 = ((size_t)s0 * Hkv + kvh0) * ROWB;
+        const int rmA = min(15, L0 - 1 - 16 * tb0), rmB = min(15, L0 - 1 - 16 * tb1);
         __builtin_amdgcn_sched_barrier(0);
-        T::load(kp + (size_t)rowA * (16 * ROWB), vp + (size_t)rowA * (16 * ROWB), grp, col,
-                min(15, L0 - 1 - 16 * tb0), kA, vA);
+        if constexpr (kFuse)
+          T::load_sel(kp + (size_t)rowA * (16 * ROWB), vp + (size_t)rowA * (16 * ROWB), kn + nrow0, vn + nrow0, newA,
+                      grp, col, rmA, kA, vA);
+        else
+          T::load(kp + (size_t)rowA * (16 * ROWB), vp + (size_t)rowA * (16 * ROWB), grp, col, rmA, kA, vA);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        T::load(kp + (size_t)rowB * (16 * ROWB), vp + (size_t)rowB * (16 * ROWB), grp, col,
-                min(15, L0 - 1 - 16 * tb1), kB, vB);
+        if constexpr (kFuse)
+          T::load_sel(kp + (size_t)rowB * (16 * ROWB), vp + (size_t)rowB * (16 * ROWB), kn + nrow0, vn + nrow0, newB,
+                      grp, col, rmB, kB, vB);
+        else
+          T::load(kp + (size_t)rowB * (16 * ROWB), vp + (size_t)rowB * (16 * ROWB), grp, col, rmB, kB, vB);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         preloaded = true;
@@ -981,12 +1053,16 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
       if (kk < ntc) {
         const Piece& pc = pcs[dpc[i]];
         int id = ids[i];
-        if (id < 0 || id >= num_blocks) {
+        const bool ok = id >= 0 && id < num_blocks;
+        if (!ok) {
           id = 0;
           atomicOr(&s_pc[wave][dpc[i]].bad, 1);
         }
         const unsigned row = ((unsigned)(id * Hkv + pc.kvh) << lm) | (unsigned)((pc.bto + kk) & ((1 << lm) - 1));
-        desc[kk] = (row << 4) | (unsigned)min(15, pc.rb - 16 * kk);
+        // the tile holding the sequence's last position (its new token, when fused)
+        const bool is_new = kFuse && ok && pc.rb - 16 * kk <= 15;
+        desc[kk] = (row << 5) | (is_new ? (unsigned)kDescNew : 0u) | (unsigned)min(15, pc.rb - 16 * kk);
+        if constexpr (kFuse) s_nrow[wave][kk] = (unsigned)pc.nrow * ROWB;
       }
     }
 #pragma unroll
@@ -1010,13 +1086,26 @@ __global__ __launch_bounds__(256) void decode_stream(void* __restrict__ out, con
         ntc, kA, vA, kB, vB,
         [&](int kk, uint4(&kr)[KS], VVec(&vr)[4]) {
           const unsigned d = (unsigned)uni((int)desc[kk]);
-          const size_t off = (size_t)(d >> 4) * (16 * ROWB);
-          T::load(kp + off, vp + off, grp, col, (int)(d & 15), kr, vr);
+          const size_t off = (size_t)(d >> 5) * (16 * ROWB);
+          if constexpr (kFuse) {
+            const size_t noff = (unsigned)uni((int)s_nrow[wave][kk]);
+            T::load_sel(kp + off, vp + off, kn + noff, vn + noff, (d & kDescNew) != 0, grp, col, (int)(d & 15), kr,
+                        vr);
+          } else {
+            T::load(kp + off, vp + off, grp, col, (int)(d & 15), kr, vr);
+          }
         },
         [&](int kk, const uint4(&kr)[KS], const VVec(&vr)[4], bool valid) {
           asm volatile("" ::: "memory");
-          const int lim = valid ? (int)(((unsigned)uni((int)desc[kk]) & 15) + 1) : 0;
+          const unsigned dk = (unsigned)uni((int)desc[kk]);
+          const int lim = valid ? (int)((dk & 15) + 1) : 0;
           T::consume(kr, vr, qsrc, 4 * grp, lim, qscale, x16, x32, m_run, l_run, acc);
+          if (kFuse && (dk & kDescNew) && (uni(pcs[cp].flags) & kWriter)) {
+            // the fused write: the new token's rows into their pool slot
+            // (one KV head's segment of query sub-group 0 writes them)
+            const size_t off = (size_t)(dk >> 5) * (16 * ROWB);
+            T::store_new(const_cast<char*>(kp) + off, const_cast<char*>(vp) + off, grp, col, (int)(dk & 15), kr, vr);
+          }
           if (valid && kk + 1 == cp_end) {
             const int flags = uni(pcs[cp].flags);
             if (flags & kEnds) {
@@ -1129,9 +1218,14 @@ __global__ __launch_bounds__(256) void decode_stream_reduce(void* __restrict__ o
 template <int DT, int D, int GMAX>
 void launch(const DecodeArgs& a, hipStream_t st) {
   if (a.stream) {
-    hipExtLaunchKernelGGL((decode_stream<DT, D, GMAX>), dim3(a.grid), dim3(256), 0, st, EV(a), 0, a.out, a.q, a.kp, a.vp, a.bt, a.cl,
-                       a.ws_o, a.ws_m, a.ws_l, a.info, a.B, a.Hq, a.Hkv, a.g, a.nsub, a.num_blocks, a.maxb, a.max_ctx,
-                       a.qscale, a.unit, a.lm);
+    if (a.kn)
+      hipExtLaunchKernelGGL((decode_stream<DT, D, GMAX, true>), dim3(a.grid), dim3(256), 0, st, EV(a), 0, a.out, a.q, a.kp,
+                         a.vp, a.bt, a.cl, a.ws_o, a.ws_m, a.ws_l, a.info, a.B, a.Hq, a.Hkv, a.g, a.nsub, a.num_blocks,
+                         a.maxb, a.max_ctx, a.qscale, a.unit, a.lm, a.kn, a.vn);
+    else
+      hipExtLaunchKernelGGL((decode_stream<DT, D, GMAX, false>), dim3(a.grid), dim3(256), 0, st, EV(a), 0, a.out, a.q, a.kp,
+                         a.vp, a.bt, a.cl, a.ws_o, a.ws_m, a.ws_l, a.info, a.B, a.Hq, a.Hkv, a.g, a.nsub, a.num_blocks,
+                         a.maxb, a.max_ctx, a.qscale, a.unit, a.lm, a.kn, a.vn);
     return;
   }
   const unsigned grid = (unsigned)a.entries * a.Hkv * a.nsub * a.B;

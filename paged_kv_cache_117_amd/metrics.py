@@ -84,3 +84,12 @@ def prefill_io_bytes(prior_lens, chunk_lens, num_q_heads: int, num_kv_heads: int
     toks = sum(int(T) for T in chunk_lens)
     return (ctx * kv_bytes_per_token(1, num_kv_heads, head_dim, elem_bytes)
             + 2 * toks * num_q_heads * head_dim * elem_bytes)
+
+
+def write_decode_io_bytes(context_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                          elem_bytes: int, block_size: int = 16) -> int:
+    """pa_write_kv_decode: decode_io_bytes plus each sequence's new K and V
+    rows read from k_new / v_new and written into the pool."""
+    B = len(context_lens)
+    return (decode_io_bytes(context_lens, num_q_heads, num_kv_heads, head_dim, elem_bytes, block_size)
+            + B * 2 * 2 * num_kv_heads * head_dim * elem_bytes)

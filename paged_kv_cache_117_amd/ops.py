@@ -130,6 +130,49 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_cont
     return out
 
 
+def write_kv_decode(q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, scale: float, max_context_len: int,
+                    out=None, partition_size: int = 0, workspace=None, stream=None):
+    """One decode step in one call (pa_write_kv_decode): each sequence's new
+    K/V rows are stored at its last position through its block table and
+    attended to.  Returns ``out`` [B][Hq][D]."""
+    _device_tensor(q, "q", ndim=3)
+    B, Hq, D = q.shape
+    _device_tensor(k_pool, "k_pool", q.dtype, 4)
+    _device_tensor(v_pool, "v_pool", q.dtype, 4)
+    if k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool shapes differ")
+    nb, Hkv, bs, Dk = k_pool.shape
+    if Dk != D:
+        raise ValueError(f"head_dim mismatch: q {D}, pools {Dk}")
+    _device_tensor(k_new, "k_new", q.dtype, 3)
+    _device_tensor(v_new, "v_new", q.dtype, 3)
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError(f"k_new/v_new must be [{B}][{Hkv}][{D}]")
+    _device_tensor(block_tables, "block_tables", torch.int32, 2)
+    _device_tensor(context_lens, "context_lens", torch.int32, 1)
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens rows must equal num_seqs")
+    ts = _launch_stream(stream)
+    if out is None:
+        out = _alloc_on(ts, lambda: torch.empty_like(q))
+    _device_tensor(out, "out", q.dtype, 3)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    need = decode_workspace_bytes(B, Hq, Hkv, D, max_context_len, partition_size)
+    if workspace is None and need:
+        workspace = _alloc_on(ts, lambda: torch.empty(need, dtype=torch.uint8, device=q.device))
+    if workspace is not None:
+        _device_tensor(workspace, "workspace")
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = LIB.pa_write_kv_decode(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_new.data_ptr(),
+                                v_new.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, bs,
+                                nb, block_tables.shape[1], int(max_context_len), float(scale), _dtype_code(q),
+                                int(partition_size), ws_ptr, ws_bytes, ts.cuda_stream)
+    check_status(st, "pa_write_kv_decode")
+    return out
+
+
 def prefill_workspace_bytes(num_seqs: int, num_tokens: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                             max_query_len: int, max_context_len: int, partition_size: int = 0) -> int:
     return int(LIB.pa_prefill_workspace_bytes(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,

@@ -1,0 +1,134 @@
+"""GPU: pa_write_kv_decode (the step's write fused into the decode launch)
+against pa_write_kv followed by pa_decode.
+
+The fused kernel reads each sequence's new token from k_new / v_new where the
+unfused decode reads it from the pool, in the same arithmetic order, so the
+outputs must agree bit for bit, and so must the whole pools afterwards (the
+fused write stores the same rows at the same slots and nothing else).  The
+unfused path is itself held to the fp64 oracle by test_gpu_decode.py; the
+fused output is also checked against the oracle here.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_117_amd as pa
+from harness import TOL, GpuStep, oracle_step, to_f64
+from workloads import make_custom, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def bits(t):
+    return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
+
+
+def both(g, partition_size=0, lens=None, tables=None, max_ctx=None):
+    """(unfused out, fused out, unfused pools, fused pools) from the same
+    pre-step pools (copy-on-write copies already applied to both)."""
+    w = g.w
+    lens = g.lens if lens is None else lens
+    tables = g.tables if tables is None else tables
+    max_ctx = w.max_context_len if max_ctx is None else max_ctx
+    if len(g.st.pairs):
+        pa.copy_blocks(g.k, g.v, g.pairs)
+    kf, vf = g.k.clone(), g.v.clone()
+    pa.write_kv(g.k, g.v, g.k_new, g.v_new, g.slots)
+    ou = pa.decode(g.q, g.k, g.v, tables, lens, w.scale, max_ctx, partition_size=partition_size)
+    of = pa.write_kv_decode(g.q, kf, vf, g.k_new, g.v_new, tables, lens, w.scale, max_ctx,
+                            partition_size=partition_size)
+    torch.cuda.synchronize()
+    return ou, of, (g.k, g.v), (kf, vf)
+
+
+def check(w, partition_size=0, oracle_rows=None):
+    print(f"[fused] {w.name} {w.dtype} B={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} "
+          f"bs={w.block_size} psize={partition_size}", flush=True)
+    g = GpuStep(w)
+    ou, of, pu, pf = both(g, partition_size)
+    assert torch.equal(bits(ou), bits(of)), "outputs differ"
+    assert torch.equal(bits(pu[0]), bits(pf[0])) and torch.equal(bits(pu[1]), bits(pf[1])), "pools differ"
+    rows = np.arange(w.num_seqs) if oracle_rows is None else np.asarray(oracle_rows)
+    _, _, _, want = oracle_step(w, rows=rows)
+    got = to_f64(of, w.dtype)[rows]
+    assert np.all(np.isfinite(got))
+    err = float(np.max(np.abs(got - want)))
+    assert err <= TOL[w.dtype], err
+
+
+@pytest.mark.parametrize("key,psize", [("c1", 0), ("c2", 0), ("c3", 0), ("c5", 512), ("c5", 0), ("c4", 0),
+                                       ("c4b", 0)])
+def test_full_size_configs(key, psize):
+    """(c3 and c5 exceed the fused kernel's size bound: their write runs as a
+    launch of its own; the g = 8, 512-position kernel is covered below.)"""
+    check(make_workload(key), psize)
+
+
+def test_qwen72b_shapes_fused_at_a_smaller_batch():
+    """The Qwen2.5-72B layer's shapes (g = 8, fp16, 512-position partitions)
+    with the write inside the stream kernel: 24 sequences of 4096-8192."""
+    lens = list(np.random.default_rng(233).integers(4096, 8193, size=24))
+    check(make_custom("fqwen", "fp16", lens, 64, 8, 128, seed=233), 512)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("g", [1, 4, 8, 32])
+def test_small_ragged(dtype, D, g):
+    # lengths 1 and 17 put the new token alone in a fresh tile; 16 and 512 at
+    # a tile's last slot; 2 in the wave's first tile pair
+    lens = [1, 2, 15, 16, 17, 511, 512, 513, 1100, 37, 3000]
+    check(make_custom(f"fsmall-g{g}", dtype, lens, 2 * g if g < 32 else 64, 2, D, seed=200 + g + D))
+
+
+@pytest.mark.parametrize("bs", [32, 64, 128])
+def test_block_sizes(bs):
+    lens = [1, 31, 32, 33, 200, 4000, 129]
+    check(make_custom(f"fbs{bs}", "bf16", lens, 16, 4, 128, seed=210 + bs, block_size=bs))
+
+
+@pytest.mark.parametrize("psize", [16, 512, 2048])
+def test_partition_sizes(psize):
+    check(make_custom("fpsize", "fp16", [3, 100, 700, 2049, 4096, 513], 16, 2, 128, seed=220), psize)
+
+
+@pytest.mark.parametrize("kernel", ["partition", "valu"])
+def test_other_kernels_write_before_decoding(kernel, monkeypatch):
+    """Without the even split (forced partition kernels or the VALU kernel)
+    the write runs as its own launch before the decode: same bits."""
+    monkeypatch.setenv("PA_DECODE_KERNEL", kernel)
+    check(make_custom(f"fother-{kernel}", "bf16", [1, 16, 17, 700, 2049], 8, 2, 128, seed=230))
+
+
+def test_large_batch_uses_the_partition_kernels():
+    rng = np.random.default_rng(231)
+    lens = list(rng.integers(1, 120, size=4100))
+    check(make_custom("fbig", "bf16", lens, 8, 2, 128, seed=231), oracle_rows=[0, 1, 4095, 4099])
+
+
+def test_sequences_without_a_valid_last_position_write_nothing():
+    """L = 0, L beyond max_context_len and an out-of-range block id at the
+    last position: outputs as pa_decode gives them (zero / NaN), and the fused
+    call leaves those sequences' would-be slots untouched."""
+    w = make_custom("fedge", "fp16", [40, 40, 40, 40, 40], 4, 2, 64, seed=232)
+    g = GpuStep(w)
+    lens = g.lens.clone()
+    lens[1] = 0
+    lens[2] = 41  # > max_context_len = 40
+    tables = g.tables.clone()
+    tables[3, 2] = w.num_blocks + 5  # position 39 is in block 2
+    k0, v0 = g.k.clone(), g.v.clone()
+    ou, of, pu, pf = both(g, lens=lens, tables=tables, max_ctx=40)
+    assert torch.equal(bits(ou), bits(of))
+    o = of.float().cpu().numpy()
+    assert np.all(o[1] == 0) and np.all(np.isnan(o[2])) and np.all(np.isnan(o[3]))
+    slots = g.st.slots
+    kf = pf[0].view(-1, w.num_kv_heads, w.block_size, w.head_dim)
+    for s in (1, 2, 3):  # nothing written for these
+        b, t = divmod(int(slots[s]), w.block_size)
+        assert torch.equal(bits(kf[b, :, t]), bits(k0[b, :, t]))
+    for s in (0, 4):  # written as pa_write_kv writes them
+        b, t = divmod(int(slots[s]), w.block_size)
+        assert torch.equal(bits(kf[b, :, t]), bits(pu[0][b, :, t]))
+        assert torch.equal(bits(pf[1][b, :, t]), bits(pu[1][b, :, t]))
