@@ -13,5 +13,4 @@ void clear_error();
 // request; both NULL when there is none.
 void take_main_kernel_events(void** start_event, void** stop_event);
 
-
 }  // namespace pa
