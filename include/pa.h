@@ -249,6 +249,10 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads
  * cores); fp32 with block_size 16, 32, 64 or 128 (VALU, one query token per
  * work item, never split); head_dim 64 or 128; any num_q_heads that is a
  * multiple of num_kv_heads.
+ * The environment variable PA_PREFILL_KERNEL=regs (read at each call)
+ * selects the kernel variant that stages K and V through registers instead
+ * of loading them straight into LDS, for measurements; same results within
+ * the tolerances.
  * Device-side contract violations are never dereferenced: a sequence with
  * T > L, L > max_blocks_per_seq * block_size, T > max_query_len, L >
  * max_context_len in a split launch, or a row range outside [0, num_tokens)

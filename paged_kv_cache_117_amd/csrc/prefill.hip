@@ -108,7 +108,39 @@ __device__ void nan_rows(void* out, int r0, int r1, int Hq, int h0, int nh, int 
   }
 }
 
-template <int DT, int D, int NC>
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// gfx950 transposing LDS read: within each group of 16 lanes, lane l receives
+// element l % 4 of the 8-byte reads of lanes 4k + l / 4, k = 0..3 (lane
+// layout measured on MI355X).  The four lanes 4k..4k+3 reading dims 4q..4q+3
+// of token k therefore give lane l dim l of tokens 0..3.
+__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(__attribute__((address_space(3))) const void*)p);
+  return __builtin_bit_cast(uint2, r);
+}
+
+// One 16-byte global->LDS load per lane: lane i's 16 bytes at `g` go to LDS
+// byte lds + 16 i (wave-uniform `lds`).  Issued as inline assembly on
+// purpose: the compiler's wait-count pass treats a pending global->LDS load
+// as a possible write to any LDS byte and makes every later LDS read wait
+// for it, which would serialise the next step's loads with this step's
+// reads of the other buffer; here the caller waits for the loads itself
+// (s_waitcnt vmcnt(0) before the barrier that ends the step).
+__device__ __forceinline__ void dma16(const void* g, const void* lds) {
+  const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l) : "memory", "m0");
+}
+
+// kDma = false: K and V go through registers into LDS (V transposed into the
+// PV operand's k-slot order by the threads).  kDma = true: both go straight
+// from global memory into LDS in token-row order (global->LDS 16-byte loads,
+// lane i of an instruction filling bytes 16 i of its 1 KiB), and the PV
+// operand is read with the transposing LDS read; no staging registers, no
+// staging ALU work.
+template <int DT, int D, int NC, bool kDma>
 __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   constexpr int ROW = D;                     // LDS row of K, elements (16-byte chunks XOR-swizzled)
   constexpr int KS = D / 32;                 // QK k-steps over the head dim
@@ -139,7 +171,12 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   // 4-byte writes (16 lanes, 16 consecutive rows, one column) then hit 16
   // distinct banks; the 16-byte reads measure two-way conflicts, which
   // costs less here than a 64-byte swizzled row whose writes conflict.
-  __shared__ __align__(16) uint16_t sV[2][kPairs * D][VROW];
+  __shared__ __align__(16) uint16_t sV[kDma ? 1 : 2][kDma ? 1 : kPairs * D][kDma ? 8 : VROW];
+  // kDma: V in token-row order, 16-byte chunk j of row r stored at chunk
+  // j ^ vkey(r), so the transposing reads of one instruction (16 rows, the
+  // same two chunks of each) spread over the banks.
+  __shared__ __align__(16) uint16_t sVn[kDma ? 2 : 1][kDma ? kStep : 1][kDma ? ROW : 8];
+  auto vkey = [](int r) { return 2 * (r & (D / 16 - 1)); };
   __shared__ int s_bad;
 
   // XCD-aware numbering.  The hardware deals workgroups round-robin over the
@@ -287,6 +324,35 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
     }
   };
 
+  // kDma: one step's K and V rows straight into LDS.  Per wavefront NI
+  // instructions for K and NI for V, each filling RPI consecutive token rows
+  // (1 KiB); lane i fills chunk i % CH of row i / CH and so loads the source
+  // chunk that belongs there (the swizzles are applied on the load side).
+  constexpr int RPI = 1024 / (D * 2);               // token rows per instruction
+  constexpr int NI = kStep / (RPI * kWaves);        // instructions per wave, K (and V)
+  static_assert(NI >= 1 && kStep % (RPI * kWaves) == 0, "whole instructions per wave");
+  auto dma_row = [&](int m) { return (wave * NI + m) * RPI + lane / CH; };  // this lane's row in the step
+  auto load_ids_dma = [&](int step, int (&ids)[NI]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NI; ++m) ids[m] = btrow[min(step * kStep + dma_row(m), L - 1) >> a.lbs];
+  };
+  auto dma = [&](int step, int buf, const int (&ids)[NI]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+      const int r = dma_row(m);
+      const int ch = lane % CH;
+      uint32_t id = (uint32_t)ids[m];
+      if (id >= (uint32_t)a.num_blocks) {
+        bad = true;
+        id = 0;
+      }
+      const int pos = min(step * kStep + r, L - 1);
+      const uint64_t row_off = (uint64_t)id * blk_bytes + (head_off + (uint32_t)(pos & bmask) * (D * 2));
+      dma16(kp + row_off + (ch ^ kkey(r)) * 16, &sK[buf][(wave * NI + m) * RPI][0]);
+      dma16(vp + row_off + (ch ^ vkey(r)) * 16, &sVn[buf][(wave * NI + m) * RPI][0]);
+    }
+  };
+
   float m_run[NC];
   float moff[NC];   // -m_run * qs: the weights' exponent offset
   f32x4 l_acc[NC];  // row sums of the rounded weights, from the matrix core (all four entries equal)
@@ -322,6 +388,25 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
         const uint4 ka = *reinterpret_cast<const uint4*>(&sK[buf][r0 + 16 * half + c][((4 * k + G) ^ kkey(c)) * 8]);
 #pragma unroll
         for (int n = 0; n < NC; ++n) sc[n][half] = mfma32<DT>(ka, qr[n][k], sc[n][half]);
+      }
+    }
+    // kDma: the pass's V operands (two transposing reads per output tile;
+    // lane 4k + q of group G reads dims 16u + 4q.. of token 16 h + 4G + k,
+    // h = 0, 1, so the lane receives dim 16u + c of the eight tokens of its
+    // k-slots) are read here, before the softmax, whose ALU work then covers
+    // their LDS latency.
+    uint4 vops[kDma ? DPL : 1];
+    if constexpr (kDma) {
+      const int q = c & 3, kt = c >> 2;
+      const int R0 = r0 + 4 * G + kt, R1 = R0 + 16;
+      const char* row0 = reinterpret_cast<const char*>(&sVn[buf][R0][0]) + 8 * (q & 1);
+      const char* row1 = reinterpret_cast<const char*>(&sVn[buf][R1][0]) + 8 * (q & 1);
+#pragma unroll
+      for (int u = 0; u < DPL; ++u) {
+        const int cc = 2 * u + (q >> 1);  // 16-byte chunk of dims 16u + 4q
+        const uint2 lo = lds_read_tr16(row0 + (cc ^ vkey(R0)) * 16);
+        const uint2 hi = lds_read_tr16(row1 + (cc ^ vkey(R1)) * 16);
+        vops[u] = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
     }
     // Scores of the lane's eight k-slots (k-slot e of lane group G is token
@@ -374,28 +459,23 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
       // row sums of the rounded weights: an all-ones A operand
       l_acc[n] = mfma32<DT>(ones, pb[n], l_acc[n]);
     }
-    // PV: the V^T operand of output tile u is one 16-byte LDS read.
+    // PV: the V^T operand of output tile u is one 16-byte LDS read (kDma:
+    // the operands read before the softmax).
 #pragma unroll
     for (int u = 0; u < DPL; ++u) {
-      const uint4 va = *reinterpret_cast<const uint4*>(&sV[buf][(r0 / kPair) * D + u * 16 + c][8 * G]);
+      uint4 va;
+      if constexpr (kDma) {
+        va = vops[u];
+      } else {
+        va = *reinterpret_cast<const uint4*>(&sV[buf][(r0 / kPair) * D + u * 16 + c][8 * G]);
+      }
 #pragma unroll
       for (int n = 0; n < NC; ++n) acc[n][u] = mfma32<DT>(va, pb[n], acc[n][u]);
     }
   };
 
   if (tid == 0) s_bad = 0;
-  int ids[PAIRS];
-  load_ids(step0, ids);
-  issue(step0, ids);
-  stash(0);
-  load_ids(step0 + 1, ids);  // ids of the next step are always one step ahead of its loads
-  __syncthreads();
-
-  for (int step = step0; step < nsteps; ++step) {
-    const int buf = (step - step0) & 1;
-    const bool more = step + 1 < nsteps;
-    if (more) issue(step + 1, ids);
-    if (step + 2 < nsteps) load_ids(step + 2, ids);
+  auto passes = [&](int step, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int pp = 0; pp < kPairs; ++pp) {
       const int t0 = step * kStep + pp * kPair;
@@ -406,8 +486,50 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
       else
         pass(std::false_type{}, buf, pp * kPair, t0);
     }
-    if (more) stash(buf ^ 1);
+  };
+  if constexpr (kDma) {
+    // The barrier after each step waits for this wave's loads into the other
+    // buffer (the compiler's fence before s_barrier) and for every wave to
+    // finish reading this one.
+    int ids[NI];
+    load_ids_dma(step0, ids);
+    dma(step0, 0, ids);
+    load_ids_dma(step0 + 1, ids);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NI; ++m) asm volatile("" ::"v"(ids[m]));
+    for (int step = step0; step < nsteps; ++step) {
+      const int buf = (step - step0) & 1;
+      if (step + 1 < nsteps) dma(step + 1, buf ^ 1, ids);
+      if (step + 2 < nsteps) load_ids_dma(step + 2, ids);
+      passes(step, buf);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads into the other buffer
+      __syncthreads();
+      // (the next step's table entries arrived with that wait; using them
+      // here lets the compiler retire their loads now, where nothing is
+      // outstanding, instead of waiting between the next step's asm loads,
+      // whose counts it cannot see)
+#pragma unroll
+      for (int m = 0; m < NI; ++m) asm volatile("" ::"v"(ids[m]));
+    }
+  } else {
+    int ids[PAIRS];
+    load_ids(step0, ids);
+    issue(step0, ids);
+    stash(0);
+    load_ids(step0 + 1, ids);  // ids of the next step are always one step ahead of its loads
+    __syncthreads();
+
+    for (int step = step0; step < nsteps; ++step) {
+      const int buf = (step - step0) & 1;
+      const bool more = step + 1 < nsteps;
+      if (more) issue(step + 1, ids);
+      if (step + 2 < nsteps) load_ids(step + 2, ids);
+      passes(step, buf);
+      if (more) stash(buf ^ 1);
+      __syncthreads();
+    }
   }
   if (bad) s_bad = 1;
   __syncthreads();
@@ -433,6 +555,32 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
 #pragma unroll
       for (int u = 0; u < DPL; ++u) f[j * DPL + u] = acc[n][u][j] * inv;
     const size_t row = (size_t)(q0 + i) * a.Hq + kvh * g + h;
+    if constexpr (kDma) {
+      // (the transposing reads give output tile u the contiguous dims
+      // 16u..16u+15: acc[n][u][j] is dim 16u + 4G + j)
+      if (a.P > 1) {
+        const size_t e = row * a.P + part;
+        float* dst = a.ws_o + e * D + 4 * G;
+#pragma unroll
+        for (int u = 0; u < DPL; ++u)
+          *reinterpret_cast<float4*>(dst + 16 * u) =
+              make_float4(acc[n][u][0] * inv, acc[n][u][1] * inv, acc[n][u][2] * inv, acc[n][u][3] * inv);
+        if (G == 0) {
+          a.ws_m[e] = wg_bad ? __builtin_nanf("") : m_run[n] * qs;
+          a.ws_l[e] = lt;
+        }
+      } else {
+        char* dst = reinterpret_cast<char*>(a.out) + (row * D + 4 * G) * 2;
+#pragma unroll
+        for (int u = 0; u < DPL; ++u) {
+          const float f8[8] = {acc[n][u][0] * inv, acc[n][u][1] * inv, acc[n][u][2] * inv, acc[n][u][3] * inv,
+                               0.f, 0.f, 0.f, 0.f};
+          const uint4 v = pack16<DT>(f8);
+          *reinterpret_cast<uint2*>(dst + 32 * u) = make_uint2(v.x, v.y);
+        }
+      }
+      continue;
+    }
     if (a.P > 1) {
       const size_t e = row * a.P + part;
       float* dst = a.ws_o + e * D + 4 * DPL * G;
@@ -529,8 +677,11 @@ __global__ __launch_bounds__(256) void prefill_reduce(PrefillArgs a) {
 template <int DT, int D, bool kMerge>
 void launch_nc(const PrefillArgs& a, hipStream_t st) {
   constexpr int HPB = 256 / (D / 4);
-  if (!kMerge)
-    hipExtLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC>), dim3(a.grid), dim3(256), 0, st,
+  if (!kMerge && a.dma)
+    hipExtLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC, true>), dim3(a.grid), dim3(256), 0, st,
+                          static_cast<hipEvent_t>(a.ev_start), static_cast<hipEvent_t>(a.ev_stop), 0, a);
+  else if (!kMerge)
+    hipExtLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC, false>), dim3(a.grid), dim3(256), 0, st,
                           static_cast<hipEvent_t>(a.ev_start), static_cast<hipEvent_t>(a.ev_stop), 0, a);
   else if (a.P > 1)
     hipLaunchKernelGGL((prefill_reduce<DT, D>), dim3(a.N, (a.Hq + HPB - 1) / HPB), dim3(256), 0, st, a);

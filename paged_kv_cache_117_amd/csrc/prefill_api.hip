@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "decode_kernels.h"
 #include "pa_internal.h"
@@ -203,6 +205,14 @@ extern "C" pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, 
     return fail(PA_ERR_SHAPE, "pa_prefill: launch of %lld workgroups is too large", (long long)grid);
   a.tiles = (int)tiles;
   a.grid = (int)grid;
+  // K/V straight from global memory into LDS, V read with the transposing
+  // LDS reads (3-6% faster on the prefill workloads than staging through
+  // registers); PA_PREFILL_KERNEL=regs selects the register-staged kernel
+  // (read at each call, for comparisons).
+  {
+    const char* k = getenv("PA_PREFILL_KERNEL");
+    a.dma = !(k && strcmp(k, "regs") == 0);
+  }
   const hipStream_t st = static_cast<hipStream_t>(stream);
   take_main_kernel_events(&a.ev_start, &a.ev_stop);
   launch_prefill_mfma(a, st);

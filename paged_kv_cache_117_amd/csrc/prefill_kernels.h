@@ -36,6 +36,7 @@ struct PrefillArgs {
   int lbs;        // log2(block_size)
   float qscale;   // |scale| * log2(e)
   pa_dtype_t dtype;
+  int dma;         // K/V straight from global memory into LDS, V read with transposing LDS reads
   void* ev_start;  // caller's timing events for prefill_mfma (hipEvent_t, or NULL)
   void* ev_stop;
 };

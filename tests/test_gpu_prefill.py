@@ -267,3 +267,34 @@ def test_fp32_bad_lengths_give_nan_rows():
     qs = w.query_start
     assert np.isnan(out[qs[1]:qs[2]]).all()
     assert np.array_equal(out[:qs[1]], good[:qs[1]])
+
+
+# The register-staged kernel variant (PA_PREFILL_KERNEL=regs, K/V staged in
+# LDS through registers, V read with plain LDS reads) stays correct beside the
+# default, which loads K/V straight into LDS and reads V transposed.
+@pytest.mark.parametrize("variant", ["regs", "dma"])
+@pytest.mark.parametrize("g,D,dtype", [(1, 128, "fp16"), (5, 64, "fp16"), (4, 128, "bf16"), (16, 64, "bf16")])
+def test_kernel_variants_every_row(monkeypatch, variant, g, D, dtype):
+    monkeypatch.setenv("PA_PREFILL_KERNEL", variant)
+    w = make_prefill_custom(f"v{variant}{g}_{D}", dtype, [0, 37, 300, 5], [150, 64, 33, 1], 2 * g, 2, D,
+                            seed=900 + g + D)
+    print(f"case variant={variant} g={g} D={D} {dtype}", flush=True)
+    _full_parity(w)
+
+
+@pytest.mark.parametrize("psize", [64, 512])
+def test_kernel_variants_agree_on_split_partitions(monkeypatch, psize):
+    """Both variants also feed the partition merge; each is within tolerance
+    of the oracle and of the other."""
+    w = make_prefill_custom(f"vsp{psize}", "bf16", [0, 300, 1000], [130, 40, 200], 8, 2, 128, seed=950 + psize)
+    g = GpuPrefillStep(w)
+    g.write()
+    res = {}
+    for variant in ("regs", "dma"):
+        monkeypatch.setenv("PA_PREFILL_KERNEL", variant)
+        res[variant] = to_f64(g.attend(partition_size=psize), "bf16")
+    st, k, v = oracle_prefill_pools(w)
+    want = oracle.prefill(w.q, k, v, st.tables, w.context_lens, w.query_start, w.scale, w.dtype)
+    for variant, got in res.items():
+        _check(got, want, "bf16", f"{variant} split {psize}")
+    assert np.abs(res["regs"] - res["dma"]).max() <= TOL["bf16"]
