@@ -96,6 +96,125 @@ __device__ __forceinline__ float max_groups(float x, int x16, int x32) {
   return fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, x))));
 }
 
+// Longest walk first within each XCD.  Every workgroup of one (sequence,
+// KV head) item runs on the same XCD (shared L2), but the workgroups of an
+// item walk very different numbers of positions (row tile t of a chunk
+// after `base` cached positions walks up to base + its last token), and
+// an order by tile index alone leaves a long tail on the XCDs whose last
+// workgroups are long ones.  So, for unsplit launches, workgroup rank k of
+// an XCD (its k-th workgroup in dispatch order) takes the k-th longest walk
+// of that XCD's items (ties: item, then tile, ascending).  A workgroup's
+// walk length is its step count (base + last row's token) / kStep + 1, and
+// within an item it does not decrease with the tile, so the number of an
+// item's tiles with at least v steps has a closed form; one wavefront
+// finds the k-th longest by a binary search over v on the sums of those
+// counts (every wavefront of the workgroup computes the same pick).
+// Unservable items take one workgroup each, ranked last, at the tile that
+// writes their NaN rows.
+constexpr int kLptPerLane = 4;  // items per lane: the in-kernel order covers up to 256 items per XCD
+
+struct LptItem {
+  int ntiles = 0;  // row tiles of a servable item
+  int base = 0;    // cached positions before the chunk
+  int rows = 0;    // chunk tokens x heads per KV head
+  bool used = false;
+  bool ok = false;  // servable
+};
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Tiles of the item walking at least v >= 1 steps.
+__device__ __forceinline__ int lpt_count(const LptItem& it, int v, int R, int g) {
+  if (!it.used) return 0;
+  if (!it.ok) return v <= 1 ? 1 : 0;
+  const int64_t need = (int64_t)(v - 1) * kStep - it.base;  // the last row's token must reach this
+  if (need <= 0) return it.ntiles;
+  const int64_t rows_needed = need * g;  // tile t's last row (t + 1) R - 1 must be >= this
+  if (rows_needed > it.rows - 1) return 0;
+  return it.ntiles - (int)(rows_needed / R);
+}
+
+// Rank k of XCD xcd -> (item, tile); false past the XCD's last workgroup.
+__device__ bool lpt_pick(const PrefillArgs& a, int xcd, int k, int per_xcd, int R, int& item_out, int& tile_out) {
+  const int lane = (int)threadIdx.x & 63;
+  const int items = a.B * a.Hkv;
+  const int c = (per_xcd + 63) >> 6;  // items per lane, lane-major
+  LptItem it[kLptPerLane];
+  int vmax = 0;
+#pragma unroll
+  for (int e = 0; e < kLptPerLane; ++e) {
+    const int j = lane * c + e;
+    if (e >= c || j >= per_xcd) continue;
+    const int item = j * 8 + xcd;
+    if (item >= items) continue;
+    const int s = item / a.Hkv;
+    const int q0 = a.qs[s], q1 = a.qs[s + 1], L = a.cl[s];
+    const int T = q1 - q0;
+    it[e].used = true;
+    it[e].ok = !(q0 < 0 || q1 < q0 || q1 > a.N || T > L || (int64_t)L > ((int64_t)a.maxb << a.lbs) || T > a.max_q);
+    if (it[e].ok) {
+      it[e].rows = T * a.g;
+      it[e].base = L - T;
+      it[e].ntiles = (it[e].rows + R - 1) / R;
+      if (it[e].ntiles > 0) vmax = max(vmax, (L - 1) / kStep + 1);
+    } else {
+      vmax = max(vmax, 1);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) vmax = max(vmax, __shfl_xor(vmax, o));
+  auto count = [&](int v) {
+    int n = 0;
+#pragma unroll
+    for (int e = 0; e < kLptPerLane; ++e) n += lpt_count(it[e], v, R, a.g);
+    return wave_sum(n);
+  };
+  if (vmax < 1 || k >= count(1)) return false;
+  int lo = 1, hi = vmax;  // count(lo) > k >= count(hi + 1)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (count(mid) > k)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const int r = k - count(lo + 1);  // rank among the walks of exactly lo steps
+  int cnt[kLptPerLane], mine = 0;
+#pragma unroll
+  for (int e = 0; e < kLptPerLane; ++e) {
+    cnt[e] = lpt_count(it[e], lo, R, a.g) - lpt_count(it[e], lo + 1, R, a.g);
+    mine += cnt[e];
+  }
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  const int excl = incl - mine;
+  const bool here = excl <= r && r < incl;
+  const int src = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(here));
+  int pick_item = 0, pick_tile = 0;
+  if (here) {
+    int rr = r - excl;
+#pragma unroll
+    for (int e = 0; e < kLptPerLane; ++e) {
+      if (rr >= 0 && rr < cnt[e]) {
+        pick_item = (lane * c + e) * 8 + xcd;
+        pick_tile = it[e].ok ? it[e].ntiles - lpt_count(it[e], lo, R, a.g) + rr : a.tiles - 1;
+      }
+      rr -= cnt[e];
+    }
+  }
+  item_out = __builtin_amdgcn_readlane(pick_item, src);
+  tile_out = __builtin_amdgcn_readlane(pick_tile, src);
+  return true;
+}
+
 // NaN into every element of query heads [h0, h0 + nh) of rows [r0, r1).
 template <int DT>
 __device__ void nan_rows(void* out, int r0, int r1, int Hq, int h0, int nh, int D) {
@@ -128,11 +247,17 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
 // for it, which would serialise the next step's loads with this step's
 // reads of the other buffer; here the caller waits for the loads itself
 // (s_waitcnt vmcnt(0) before the barrier that ends the step).
+// M0 is a reserved register, hence the compiler's warning about clobbering
+// it; these kernels use M0 for nothing else (their assembly holds no other
+// M0 write or read), and the statement sets it before its one use.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* g, const void* lds) {
   const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane(
       (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // kDma = false: K and V go through registers into LDS (V transposed into the
 // PV operand's k-slot order by the threads).  kDma = true: both go straight
@@ -183,17 +308,23 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   // 8 XCDs (workgroup b runs on XCD b % 8).  Work item (sequence, KV head)
   // number i goes to XCD i % 8, so all row tiles of one item share that
   // XCD's L2 while the items -- and with 8 KV heads, one head of every
-  // sequence -- are spread evenly over the XCDs.  Within an XCD the tiles
-  // are ordered latest rows (longest walks) first, across all its items.
-  // With P > 1 each row tile is further cut into P partitions of positions
-  // (latest tile first, its partitions in order).
+  // sequence -- are spread evenly over the XCDs.  Within an XCD an unsplit
+  // launch runs its workgroups longest walk first (lpt_pick; the plain tile
+  // order below beyond 256 items per XCD).  With P > 1 each row tile is cut
+  // into P partitions of positions, latest tile first, its partitions in
+  // order.
   const int items = a.B * a.Hkv;
   const int per_xcd = (items + 7) >> 3;  // items per XCD (upper bound)
   const int xcd = (int)(blockIdx.x & 7), local = (int)(blockIdx.x >> 3);
-  const int item = (local % per_xcd) * 8 + xcd;
-  const int tp = local / per_xcd;
-  const int tile = a.tiles - 1 - tp / a.P;
-  const int part = tp % a.P;
+  int item, tile, part = 0;
+  if (a.P == 1 && per_xcd <= 64 * kLptPerLane) {
+    if (!lpt_pick(a, xcd, local, per_xcd, R, item, tile)) return;
+  } else {
+    item = (local % per_xcd) * 8 + xcd;
+    const int tp = local / per_xcd;
+    tile = a.tiles - 1 - tp / a.P;
+    part = tp % a.P;
+  }
   if (item >= items) return;
   const int kvh = item % a.Hkv;
   const int s = item / a.Hkv;

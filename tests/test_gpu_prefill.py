@@ -298,3 +298,33 @@ def test_kernel_variants_agree_on_split_partitions(monkeypatch, psize):
     for variant, got in res.items():
         _check(got, want, "bf16", f"{variant} split {psize}")
     assert np.abs(res["regs"] - res["dma"]).max() <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("B,Hkv,g", [(150, 4, 2), (530, 4, 1)])
+def test_many_items_every_row(B, Hkv, g):
+    """Workgroups run longest walk first within each XCD: 150 x 4 items put
+    75 on each XCD (two per lane of the in-kernel order); 530 x 4 items
+    exceed its 256 per XCD and take the plain tile order.  Empty chunks and
+    one unservable sequence included."""
+    import paged_kv_cache_117_amd as pa
+
+    rng = np.random.default_rng(40 + B)
+    prior = rng.integers(0, 70, size=B)
+    chunk = rng.integers(0, 6, size=B)
+    chunk[::17] = 0
+    w = make_prefill_custom(f"many{B}", "bf16", prior, chunk, g * Hkv, Hkv, 64, seed=41 + B)
+    print(f"case many items B={B} Hkv={Hkv} g={g}", flush=True)
+    g_ = GpuPrefillStep(w)
+    g_.write()
+    lens = g_.lens.clone()
+    bad = int(np.nonzero(chunk)[0][3])
+    lens[bad] = int(chunk[bad]) - 1  # T > L: NaN rows for this sequence only
+    out = to_f64(pa.prefill(g_.q, g_.k, g_.v, g_.tables, lens, g_.qstart, w.scale, w.max_query_len,
+                            w.max_context_len), "bf16")
+    st, k, v = oracle_prefill_pools(w)
+    want = oracle.prefill(w.q, k, v, st.tables, w.context_lens, w.query_start, w.scale, w.dtype)
+    qs = w.query_start
+    assert np.isnan(out[qs[bad]:qs[bad + 1]]).all()
+    keep = np.ones(len(out), bool)
+    keep[qs[bad]:qs[bad + 1]] = False
+    _check(out[keep], want[keep], "bf16", f"many {B}")
