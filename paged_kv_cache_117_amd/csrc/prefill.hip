@@ -240,22 +240,21 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-// One 16-byte global->LDS load per lane: lane i's 16 bytes at `g` go to LDS
-// byte lds + 16 i (wave-uniform `lds`).  Issued as inline assembly on
-// purpose: the compiler's wait-count pass treats a pending global->LDS load
-// as a possible write to any LDS byte and makes every later LDS read wait
-// for it, which would serialise the next step's loads with this step's
-// reads of the other buffer; here the caller waits for the loads itself
-// (s_waitcnt vmcnt(0) before the barrier that ends the step).
-// M0 is a reserved register, hence the compiler's warning about clobbering
-// it; these kernels use M0 for nothing else (their assembly holds no other
-// M0 write or read), and the statement sets it before its one use.
+// One 16-byte global->LDS load per lane: lane i's 16 bytes at base + off_i
+// (`base` wave-uniform, in scalar registers; off_i a per-lane byte offset
+// below 2^31) go to LDS byte lds + 16 i (`lds` wave-uniform).  Issued as
+// inline assembly on purpose: the compiler's wait-count pass treats a
+// pending global->LDS load as a possible write to any LDS byte and makes
+// every later LDS read wait for it, which would serialise the next step's
+// loads with this step's reads of the other buffer; here the caller waits
+// for the loads itself (s_waitcnt vmcnt(0) before the barrier that ends the
+// step).  M0 is a reserved register, hence the compiler's warning about
+// clobbering it; these kernels use M0 for nothing else (their assembly holds
+// no other M0 write or read), and the statement sets it before its one use.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* g, const void* lds) {
-  const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane(
-      (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l) : "memory", "m0");
+__device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -455,32 +454,72 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
     }
   };
 
-  // kDma: one step's K and V rows straight into LDS.  Per wavefront NI
-  // instructions for K and NI for V, each filling RPI consecutive token rows
-  // (1 KiB); lane i fills chunk i % CH of row i / CH and so loads the source
-  // chunk that belongs there (the swizzles are applied on the load side).
-  constexpr int RPI = 1024 / (D * 2);               // token rows per instruction
-  constexpr int NI = kStep / (RPI * kWaves);        // instructions per wave, K (and V)
-  static_assert(NI >= 1 && kStep % (RPI * kWaves) == 0, "whole instructions per wave");
-  auto dma_row = [&](int m) { return (wave * NI + m) * RPI + lane / CH; };  // this lane's row in the step
-  auto load_ids_dma = [&](int step, int (&ids)[NI]) __attribute__((always_inline)) {
+  // kDma: one step's K and V rows straight into LDS.  Wavefront w fills rows
+  // [16 w, 16 w + 16) of the step with NI instructions for K and NI for V,
+  // each filling RPI consecutive rows (1 KiB); lane i fills chunk i % CH of
+  // row i / CH and so loads the source chunk that belongs there (the
+  // swizzles are applied on the load side).  Rows 0-7 and 8-15 of a wave
+  // each lie in one block (blocks hold a power of two >= 8 of slots), so an
+  // instruction's addresses are a wave-uniform base -- its half's first row
+  // in the block, in scalar registers -- plus a per-lane offset that is the
+  // same at every step.  Only a step whose rows pass L - 1 takes per-lane
+  // rows, clamped to L - 1 (V past the context must be finite: its weights
+  // are zero, and 0 * NaN would poison the row).
+  constexpr int RPI = 1024 / (D * 2);  // token rows per instruction
+  constexpr int NI = 16 / RPI;         // instructions per wave, K (and V)
+  static_assert(kStep == 16 * kWaves && NI % 2 == 0, "16 rows of a step per wavefront, two halves of 8");
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t koff[NI], voff[NI];  // instruction m: offset of this lane's chunk from its half's first row
 #pragma unroll
-    for (int m = 0; m < NI; ++m) ids[m] = btrow[min(step * kStep + dma_row(m), L - 1) >> a.lbs];
+  for (int m = 0; m < NI; ++m) {
+    const int h = m / (NI / 2);
+    const int r = (m % (NI / 2)) * RPI + lane / CH;  // row within the half
+    const int rs = 16 * wv + 8 * h + r;              // row within the step (swizzle key)
+    const int ch = lane % CH;
+    koff[m] = (uint32_t)(r * (D * 2) + (ch ^ kkey(rs)) * 16);
+    voff[m] = (uint32_t)(r * (D * 2) + (ch ^ vkey(rs)) * 16);
+  }
+  const uint32_t ldsK = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)&sK[0][0][0]);
+  const uint32_t ldsV = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)&sVn[0][0][0]);
+  constexpr uint32_t kBufBytes = kStep * ROW * 2;
+  // Table entries of the step's two halves: lane l reads the entry of row
+  // l % 8 of each half, clamped to L - 1 -- one block per half whichever row.
+  auto load_ids_dma = [&](int step, int (&ids)[2]) __attribute__((always_inline)) {
+    const int p = step * kStep + 16 * wv + (lane & 7);
+    ids[0] = btrow[min(p, L - 1) >> a.lbs];
+    ids[1] = btrow[min(p + 8, L - 1) >> a.lbs];
   };
-  auto dma = [&](int step, int buf, const int (&ids)[NI]) __attribute__((always_inline)) {
+  auto dma = [&](int step, int buf, const int (&ids)[2]) __attribute__((always_inline)) {
+    const int p0 = step * kStep + 16 * wv;
+    const bool whole = p0 + 15 < L;  // no row of the wave past L - 1
 #pragma unroll
-    for (int m = 0; m < NI; ++m) {
-      const int r = dma_row(m);
-      const int ch = lane % CH;
-      uint32_t id = (uint32_t)ids[m];
+    for (int h = 0; h < 2; ++h) {
+      uint32_t id = (uint32_t)__builtin_amdgcn_readfirstlane(ids[h]);
       if (id >= (uint32_t)a.num_blocks) {
         bad = true;
         id = 0;
       }
-      const int pos = min(step * kStep + r, L - 1);
-      const uint64_t row_off = (uint64_t)id * blk_bytes + (head_off + (uint32_t)(pos & bmask) * (D * 2));
-      dma16(kp + row_off + (ch ^ kkey(r)) * 16, &sK[buf][(wave * NI + m) * RPI][0]);
-      dma16(vp + row_off + (ch ^ vkey(r)) * 16, &sVn[buf][(wave * NI + m) * RPI][0]);
+      const int ph = p0 + 8 * h;
+      const uint32_t rb = whole ? (uint32_t)(ph & bmask) * (D * 2) : 0u;
+      const uint64_t off = (uint64_t)id * blk_bytes + head_off + rb;
+      const char* kb = kp + off;
+      const char* vb = vp + off;
+#pragma unroll
+      for (int mm = 0; mm < NI / 2; ++mm) {
+        const int m = h * (NI / 2) + mm;
+        uint32_t ko = koff[m], vo = voff[m];
+        if (!whole) {  // the lane's row, clamped, replaces its row in the half
+          const int r = mm * RPI + lane / CH;
+          const uint32_t dr = (uint32_t)(min(ph + r, L - 1) & bmask) * (D * 2) - (uint32_t)(r * (D * 2));
+          ko += dr;
+          vo += dr;
+        }
+        const uint32_t lrow = (uint32_t)(16 * wv + 8 * h + mm * RPI) * (ROW * 2) + (uint32_t)buf * kBufBytes;
+        dma16(kb, ko, ldsK + lrow);
+        dma16(vb, vo, ldsV + lrow);
+      }
     }
   };
 
@@ -622,14 +661,13 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
     // The barrier after each step waits for this wave's loads into the other
     // buffer (the compiler's fence before s_barrier) and for every wave to
     // finish reading this one.
-    int ids[NI];
+    int ids[2];
     load_ids_dma(step0, ids);
     dma(step0, 0, ids);
     load_ids_dma(step0 + 1, ids);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-#pragma unroll
-    for (int m = 0; m < NI; ++m) asm volatile("" ::"v"(ids[m]));
+    asm volatile("" ::"v"(ids[0]), "v"(ids[1]));
     for (int step = step0; step < nsteps; ++step) {
       const int buf = (step - step0) & 1;
       if (step + 1 < nsteps) dma(step + 1, buf ^ 1, ids);
@@ -641,8 +679,7 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
       // here lets the compiler retire their loads now, where nothing is
       // outstanding, instead of waiting between the next step's asm loads,
       // whose counts it cannot see)
-#pragma unroll
-      for (int m = 0; m < NI; ++m) asm volatile("" ::"v"(ids[m]));
+      asm volatile("" ::"v"(ids[0]), "v"(ids[1]));
     }
   } else {
     int ids[PAIRS];
