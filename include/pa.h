@@ -249,10 +249,14 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads
  * cores); fp32 with block_size 16, 32, 64 or 128 (VALU, one query token per
  * work item, never split); head_dim 64 or 128; any num_q_heads that is a
  * multiple of num_kv_heads.
- * The environment variable PA_PREFILL_KERNEL=regs (read at each call)
- * selects the kernel variant that stages K and V through registers instead
- * of loading them straight into LDS, for measurements; same results within
- * the tolerances.
+ * The library picks the workgroup width from the sizes passed: 8
+ * wavefronts over 256 query rows when the batch averages at least 256 rows
+ * per (sequence, KV head), num_tokens * (num_q_heads / num_kv_heads) >=
+ * 256 * num_seqs, else 4 wavefronts over 128 rows; both give the same bits.
+ * The environment variable PA_PREFILL_KERNEL (read at each call) forces a
+ * kernel, for measurements: "dma" (4 wavefronts), "w8" (8 wavefronts) or
+ * "regs" (K and V staged through registers instead of loaded straight into
+ * LDS; same results within the tolerances).
  * Device-side contract violations are never dereferenced: a sequence with
  * T > L, L > max_blocks_per_seq * block_size, T > max_query_len, L >
  * max_context_len in a split launch, or a row range outside [0, num_tokens)

@@ -57,7 +57,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;                 // wavefronts per workgroup (the 8-wavefront instance: kWideWaves)
 constexpr int kPair = 32;                 // positions per compute pass: two 16-slot halves
 constexpr int kPairs = 2;                 // passes per step (one barrier, one load batch)
 constexpr int kStep = kPair * kPairs;     // positions per step
@@ -264,8 +264,8 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t l
 // lane i of an instruction filling bytes 16 i of its 1 KiB), and the PV
 // operand is read with the transposing LDS read; no staging registers, no
 // staging ALU work.
-template <int DT, int D, int NC, bool kDma>
-__global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
+template <int DT, int D, int NC, bool kDma, int W>
+__global__ __launch_bounds__(64 * W) void prefill_mfma(PrefillArgs a) {
   constexpr int ROW = D;                     // LDS row of K, elements (16-byte chunks XOR-swizzled)
   constexpr int KS = D / 32;                 // QK k-steps over the head dim
   constexpr int DPL = D / 16;                // output dims per lane per row = PV MFMAs per column group
@@ -273,7 +273,8 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   constexpr int LOADS = kStep * CH / 256;    // chunks of K (and of V) per thread per step
   constexpr int PAIRS = LOADS / 2;           // (token pair, chunk) items per thread per step
   constexpr int VROW = kPair + 8;            // LDS row of V^T: one pass's 32 slots + 16 bytes of padding
-  constexpr int R = kWaves * 16 * NC;        // rows per workgroup
+  constexpr int R = W * 16 * NC;             // rows per workgroup
+  static_assert(W == kWaves || (kDma && W == kWideWaves), "register staging assumes 4 wavefronts");
   static_assert(PAIRS >= 1 && kStep * CH % 512 == 0, "token pairs must split evenly over the threads");
   static_assert(8 % DPL == 0, "a 16-byte chunk's dims map to whole V^T rows");
   static_assert(D == 64 || D == 128, "the swizzle keys were measured for these row lengths");
@@ -455,26 +456,29 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   };
 
   // kDma: one step's K and V rows straight into LDS.  Wavefront w fills rows
-  // [16 w, 16 w + 16) of the step with NI instructions for K and NI for V,
-  // each filling RPI consecutive rows (1 KiB); lane i fills chunk i % CH of
-  // row i / CH and so loads the source chunk that belongs there (the
-  // swizzles are applied on the load side).  Rows 0-7 and 8-15 of a wave
-  // each lie in one block (blocks hold a power of two >= 8 of slots), so an
-  // instruction's addresses are a wave-uniform base -- its half's first row
-  // in the block, in scalar registers -- plus a per-lane offset that is the
-  // same at every step.  Only a step whose rows pass L - 1 takes per-lane
-  // rows, clamped to L - 1 (V past the context must be finite: its weights
-  // are zero, and 0 * NaN would poison the row).
+  // [RW w, RW w + RW) of the step (RW = 64 / W) with NI instructions for K
+  // and NI for V, each filling RPI consecutive rows (1 KiB); lane i fills
+  // chunk i % CH of row i / CH and so loads the source chunk that belongs
+  // there (the swizzles are applied on the load side).  Every 8-row half of
+  // a wave's rows lies in one block (blocks hold a power of two >= 8 of
+  // slots), so an instruction's addresses are a wave-uniform base -- its
+  // half's first row in the block, in scalar registers -- plus a per-lane
+  // offset that is the same at every step.  Only a step whose rows pass
+  // L - 1 takes per-lane rows, clamped to L - 1 (V past the context must be
+  // finite: its weights are zero, and 0 * NaN would poison the row).
   constexpr int RPI = 1024 / (D * 2);  // token rows per instruction
-  constexpr int NI = 16 / RPI;         // instructions per wave, K (and V)
-  static_assert(kStep == 16 * kWaves && NI % 2 == 0, "16 rows of a step per wavefront, two halves of 8");
+  constexpr int RW = kStep / W;        // rows of a step per wavefront
+  constexpr int NH = RW / 8;           // 8-row halves per wavefront
+  constexpr int NI2 = 8 / RPI;         // instructions per half
+  constexpr int NI = NH * NI2;         // instructions per wave, K (and V)
+  static_assert(kStep % (8 * W) == 0 && NH >= 1 && NI2 >= 1, "whole 8-row halves per wavefront");
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   uint32_t koff[NI], voff[NI];  // instruction m: offset of this lane's chunk from its half's first row
 #pragma unroll
   for (int m = 0; m < NI; ++m) {
-    const int h = m / (NI / 2);
-    const int r = (m % (NI / 2)) * RPI + lane / CH;  // row within the half
-    const int rs = 16 * wv + 8 * h + r;              // row within the step (swizzle key)
+    const int h = m / NI2;
+    const int r = (m % NI2) * RPI + lane / CH;  // row within the half
+    const int rs = RW * wv + 8 * h + r;         // row within the step (swizzle key)
     const int ch = lane % CH;
     koff[m] = (uint32_t)(r * (D * 2) + (ch ^ kkey(rs)) * 16);
     voff[m] = (uint32_t)(r * (D * 2) + (ch ^ vkey(rs)) * 16);
@@ -484,43 +488,36 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   const uint32_t ldsV = (uint32_t)__builtin_amdgcn_readfirstlane(
       (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)&sVn[0][0][0]);
   constexpr uint32_t kBufBytes = kStep * ROW * 2;
-  // Table entries of the step's two halves: lane l reads the entry of row
-  // l % 8 of each half, clamped to L - 1 -- one block per half whichever row.
-  auto load_ids_dma = [&](int step, int (&ids)[2]) __attribute__((always_inline)) {
-    const int p = step * kStep + 16 * wv + (lane & 7);
-    ids[0] = btrow[min(p, L - 1) >> a.lbs];
-    ids[1] = btrow[min(p + 8, L - 1) >> a.lbs];
+  // Table entries of the step's halves: lane l reads the entry of row l % 8
+  // of each half, clamped to L - 1 -- one block per half whichever row.
+  auto load_ids_dma = [&](int step, int (&ids)[NH]) __attribute__((always_inline)) {
+    const int p = step * kStep + RW * wv + (lane & 7);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) ids[h] = btrow[min(p + 8 * h, L - 1) >> a.lbs];
   };
-  auto dma = [&](int step, int buf, const int (&ids)[2]) __attribute__((always_inline)) {
-    const int p0 = step * kStep + 16 * wv;
-    const bool whole = p0 + 15 < L;  // no row of the wave past L - 1
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t id = (uint32_t)__builtin_amdgcn_readfirstlane(ids[h]);
-      if (id >= (uint32_t)a.num_blocks) {
-        bad = true;
-        id = 0;
-      }
-      const int ph = p0 + 8 * h;
-      const uint32_t rb = whole ? (uint32_t)(ph & bmask) * (D * 2) : 0u;
-      const uint64_t off = (uint64_t)id * blk_bytes + head_off + rb;
-      const char* kb = kp + off;
-      const char* vb = vp + off;
-#pragma unroll
-      for (int mm = 0; mm < NI / 2; ++mm) {
-        const int m = h * (NI / 2) + mm;
-        uint32_t ko = koff[m], vo = voff[m];
-        if (!whole) {  // the lane's row, clamped, replaces its row in the half
-          const int r = mm * RPI + lane / CH;
-          const uint32_t dr = (uint32_t)(min(ph + r, L - 1) & bmask) * (D * 2) - (uint32_t)(r * (D * 2));
-          ko += dr;
-          vo += dr;
-        }
-        const uint32_t lrow = (uint32_t)(16 * wv + 8 * h + mm * RPI) * (ROW * 2) + (uint32_t)buf * kBufBytes;
-        dma16(kb, ko, ldsK + lrow);
-        dma16(vb, vo, ldsV + lrow);
-      }
+  // Instruction m (K and V; rows of half m / NI2) of step `step` into buffer buf.
+  auto dma_inst = [&](int step, int buf, const int (&ids)[NH], int m) __attribute__((always_inline)) {
+    const int h = m / NI2, mm = m % NI2;
+    const int p0 = step * kStep + RW * wv;
+    const bool whole = p0 + RW - 1 < L;  // no row of the wave past L - 1
+    uint32_t id = (uint32_t)__builtin_amdgcn_readfirstlane(ids[h]);
+    if (id >= (uint32_t)a.num_blocks) {
+      bad = true;
+      id = 0;
     }
+    const int ph = p0 + 8 * h;
+    const uint32_t rb = whole ? (uint32_t)(ph & bmask) * (D * 2) : 0u;
+    const uint64_t off = (uint64_t)id * blk_bytes + head_off + rb;
+    uint32_t ko = koff[m], vo = voff[m];
+    if (!whole) {  // the lane's row, clamped, replaces its row in the half
+      const int r = mm * RPI + lane / CH;
+      const uint32_t dr = (uint32_t)(min(ph + r, L - 1) & bmask) * (D * 2) - (uint32_t)(r * (D * 2));
+      ko += dr;
+      vo += dr;
+    }
+    const uint32_t lrow = (uint32_t)(RW * wv + 8 * h + mm * RPI) * (ROW * 2) + (uint32_t)buf * kBufBytes;
+    dma16(kp + off, ko, ldsK + lrow);
+    dma16(vp + off, vo, ldsV + lrow);
   };
 
   float m_run[NC];
@@ -536,7 +533,7 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
     for (int u = 0; u < DPL; ++u) acc[n][u] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One pass over 32 positions starting at t0 (LDS rows r0..r0+31).
+  // Passes of 32 positions starting at t0 (LDS rows r0..r0+31 of a step).
   // Lazy rescaling: the weights use a reference max m_run that is raised
   // only when some weight of the wave comes out above 2^kSlack (then every
   // row moves to its true running max and its weights are recomputed);
@@ -546,9 +543,9 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
   constexpr uint32_t kSlackBits = 0x43800000u;  // 2^kSlack = 256.0f, kSlack = 8
   constexpr uint32_t kOne2 = DT == PA_BF16 ? 0x3F803F80u : 0x3C003C00u;  // two 1.0s of the KV type
   const uint4 ones = make_uint4(kOne2, kOne2, kOne2, kOne2);
-  auto pass = [&](auto masked, int buf, int r0, int t0) __attribute__((always_inline)) {
-    constexpr bool kMasked = decltype(masked)::value;
-    f32x4 sc[NC][2];
+  // One pass in four parts (the direct-load kernel also runs two passes
+  // with their parts interleaved): scores, V operands, weights, products.
+  auto qk_scores = [&](int buf, int r0, f32x4 (&sc)[NC][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int n = 0; n < NC; ++n) sc[n][0] = sc[n][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -560,12 +557,14 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
         for (int n = 0; n < NC; ++n) sc[n][half] = mfma32<DT>(ka, qr[n][k], sc[n][half]);
       }
     }
-    // kDma: the pass's V operands (two transposing reads per output tile;
-    // lane 4k + q of group G reads dims 16u + 4q.. of token 16 h + 4G + k,
-    // h = 0, 1, so the lane receives dim 16u + c of the eight tokens of its
-    // k-slots) are read here, before the softmax, whose ALU work then covers
-    // their LDS latency.
-    uint4 vops[kDma ? DPL : 1];
+  };
+  // kDma: the pass's V operands (two transposing reads per output tile;
+  // lane 4k + q of group G reads dims 16u + 4q.. of token 16 h + 4G + k,
+  // h = 0, 1, so the lane receives dim 16u + c of the eight tokens of its
+  // k-slots), read before the softmax, whose ALU work then covers their LDS
+  // latency.
+  constexpr int VN = kDma ? DPL : 1;  // V operands held per pass
+  auto read_vops = [&](int buf, int r0, uint4 (&vops)[VN]) __attribute__((always_inline)) {
     if constexpr (kDma) {
       const int q = c & 3, kt = c >> 2;
       const int R0 = r0 + 4 * G + kt, R1 = R0 + 16;
@@ -579,13 +578,16 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
         vops[u] = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
     }
-    // Scores of the lane's eight k-slots (k-slot e of lane group G is token
-    // 16*(e/4) + 4G + e%4 of the pass), masked past each row's limit, and
-    // their weights 2^(x qs - m qs) against the rows' reference m.  Weights
-    // are >= 0, so their bit patterns order like unsigned integers: one
-    // integer max tells whether some weight of the lane passed 2^kSlack.
-    // Only then (rarely) are the rows' maxima gathered across the four lane
-    // groups, the accumulators rescaled and the weights recomputed.
+  };
+  // Scores of the lane's eight k-slots (k-slot e of lane group G is token
+  // 16*(e/4) + 4G + e%4 of the pass), masked past each row's limit, and
+  // their weights 2^(x qs - m qs) against the rows' reference m.  Weights
+  // are >= 0, so their bit patterns order like unsigned integers: one
+  // integer max tells whether some weight of the lane passed 2^kSlack.
+  // Only then (rarely) are the rows' maxima gathered across the four lane
+  // groups, the accumulators rescaled and the weights recomputed.
+  auto weights = [&](auto masked, const f32x4 (&sc)[NC][2], int t0, uint4 (&pb)[NC]) __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked)::value;
     float x[NC][8], p[NC][8];
     uint32_t pbits = 0;
 #pragma unroll
@@ -621,16 +623,17 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
         }
       }
     }
-    uint4 pb[NC];
 #pragma unroll
-    for (int n = 0; n < NC; ++n) {
+    for (int n = 0; n < NC; ++n)
       pb[n] = make_uint4(pack2<DT>(p[n][0], p[n][1]), pack2<DT>(p[n][2], p[n][3]), pack2<DT>(p[n][4], p[n][5]),
                          pack2<DT>(p[n][6], p[n][7]));
-      // row sums of the rounded weights: an all-ones A operand
-      l_acc[n] = mfma32<DT>(ones, pb[n], l_acc[n]);
-    }
-    // PV: the V^T operand of output tile u is one 16-byte LDS read (kDma:
-    // the operands read before the softmax).
+  };
+  // Row sums of the rounded weights (an all-ones A operand) and the PV
+  // products; the V^T operand of output tile u is one 16-byte LDS read
+  // (kDma: the operands read before the softmax).
+  auto products = [&](int buf, int r0, const uint4 (&pb)[NC], const uint4 (&vops)[VN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int n = 0; n < NC; ++n) l_acc[n] = mfma32<DT>(ones, pb[n], l_acc[n]);
 #pragma unroll
     for (int u = 0; u < DPL; ++u) {
       uint4 va;
@@ -642,6 +645,15 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
 #pragma unroll
       for (int n = 0; n < NC; ++n) acc[n][u] = mfma32<DT>(va, pb[n], acc[n][u]);
     }
+  };
+  // One pass over 32 positions starting at t0 (LDS rows r0..r0+31).
+  auto pass = [&](auto masked, int buf, int r0, int t0) __attribute__((always_inline)) {
+    f32x4 sc[NC][2];
+    uint4 vops[VN], pb[NC];
+    qk_scores(buf, r0, sc);
+    read_vops(buf, r0, vops);
+    weights(masked, sc, t0, pb);
+    products(buf, r0, pb, vops);
   };
 
   if (tid == 0) s_bad = 0;
@@ -661,25 +673,53 @@ __global__ __launch_bounds__(256) void prefill_mfma(PrefillArgs a) {
     // The barrier after each step waits for this wave's loads into the other
     // buffer (the compiler's fence before s_barrier) and for every wave to
     // finish reading this one.
-    int ids[2];
+    int ids[NH];
+    auto retire_ids = [&] {
+#pragma unroll
+      for (int h = 0; h < NH; ++h) asm volatile("" ::"v"(ids[h]));
+    };
     load_ids_dma(step0, ids);
-    dma(step0, 0, ids);
+#pragma unroll
+    for (int m = 0; m < NI; ++m) dma_inst(step0, 0, ids, m);
     load_ids_dma(step0 + 1, ids);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    asm volatile("" ::"v"(ids[0]), "v"(ids[1]));
+    retire_ids();
+    // The next step's loads are issued half before each pass: a wavefront's
+    // loads all at once would hold its instruction issue until the compute
+    // unit's load path has taken them (measured: 2-6% slower than halves;
+    // splitting each half again around the score products was slower
+    // still).
+    static_assert(kPairs == 2, "half of the next step's loads before each pass");
+    constexpr int kFirst = NI >= 2 ? NI / 2 : NI;  // instructions issued before pass 0
     for (int step = step0; step < nsteps; ++step) {
       const int buf = (step - step0) & 1;
-      if (step + 1 < nsteps) dma(step + 1, buf ^ 1, ids);
-      if (step + 2 < nsteps) load_ids_dma(step + 2, ids);
-      passes(step, buf);
+      const bool more = step + 1 < nsteps;
+      auto issue_next = [&](int pp) __attribute__((always_inline)) {
+        if (more) {
+#pragma unroll
+          for (int m = pp == 0 ? 0 : kFirst; m < (pp == 0 ? kFirst : NI); ++m) dma_inst(step + 1, buf ^ 1, ids, m);
+        }
+        if (pp == kPairs - 1 && step + 2 < nsteps) load_ids_dma(step + 2, ids);
+      };
+      const int ts = step * kStep;
+#pragma unroll
+      for (int pp = 0; pp < kPairs; ++pp) {
+        issue_next(pp);
+        const int t0 = ts + pp * kPair;
+        if (!(wave_on && t0 <= lim_w_hi)) continue;
+        if (t0 + kPair - 1 > lim_w_lo)
+          pass(std::true_type{}, buf, pp * kPair, t0);
+        else
+          pass(std::false_type{}, buf, pp * kPair, t0);
+      }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads into the other buffer
       __syncthreads();
       // (the next step's table entries arrived with that wait; using them
       // here lets the compiler retire their loads now, where nothing is
       // outstanding, instead of waiting between the next step's asm loads,
       // whose counts it cannot see)
-      asm volatile("" ::"v"(ids[0]), "v"(ids[1]));
+      retire_ids();
     }
   } else {
     int ids[PAIRS];
@@ -845,11 +885,14 @@ __global__ __launch_bounds__(256) void prefill_reduce(PrefillArgs a) {
 template <int DT, int D, bool kMerge>
 void launch_nc(const PrefillArgs& a, hipStream_t st) {
   constexpr int HPB = 256 / (D / 4);
-  if (!kMerge && a.dma)
-    hipExtLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC, true>), dim3(a.grid), dim3(256), 0, st,
+  if (!kMerge && a.kind == kPrefillWide)
+    hipExtLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC, true, kWideWaves>), dim3(a.grid), dim3(64 * kWideWaves), 0,
+                          st, static_cast<hipEvent_t>(a.ev_start), static_cast<hipEvent_t>(a.ev_stop), 0, a);
+  else if (!kMerge && a.kind == kPrefillDirect)
+    hipExtLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC, true, kWaves>), dim3(a.grid), dim3(64 * kWaves), 0, st,
                           static_cast<hipEvent_t>(a.ev_start), static_cast<hipEvent_t>(a.ev_stop), 0, a);
   else if (!kMerge)
-    hipExtLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC, false>), dim3(a.grid), dim3(256), 0, st,
+    hipExtLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC, false, kWaves>), dim3(a.grid), dim3(64 * kWaves), 0, st,
                           static_cast<hipEvent_t>(a.ev_start), static_cast<hipEvent_t>(a.ev_stop), 0, a);
   else if (a.P > 1)
     hipLaunchKernelGGL((prefill_reduce<DT, D>), dim3(a.N, (a.Hq + HPB - 1) / HPB), dim3(256), 0, st, a);

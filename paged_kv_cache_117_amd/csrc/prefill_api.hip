@@ -196,23 +196,32 @@ extern "C" pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, 
     a.ws_m = reinterpret_cast<float*>(ws + wl.m_off);
     a.ws_l = reinterpret_cast<float*>(ws + wl.l_off);
   }
+  // Kernel variant.  Both default kernels load K/V straight into LDS; the
+  // 8-wavefront one shares each step's K/V between 256 rows and is 2-10%
+  // faster when sequences bring that many rows per KV head, while a step
+  // of mostly short chunks (decode-like single tokens) keeps 128-row
+  // workgroups, two per compute unit (the wide kernel measured 16% slower
+  // there).  Only sizes the caller passes enter the choice: average query
+  // rows per (sequence, KV head) = num_tokens * g / num_seqs.
+  // PA_PREFILL_KERNEL=regs | dma | w8 forces one (read at each call, for
+  // comparisons).
+  a.kind = (int64_t)num_tokens * a.g >= (int64_t)kWideRows * num_seqs ? kPrefillWide : kPrefillDirect;
+  {
+    const char* k = getenv("PA_PREFILL_KERNEL");
+    if (k && strcmp(k, "regs") == 0) a.kind = kPrefillRegs;
+    if (k && strcmp(k, "dma") == 0) a.kind = kPrefillDirect;
+    if (k && strcmp(k, "w8") == 0) a.kind = kPrefillWide;
+  }
   // Grid: 8 XCDs x ceil(items / 8) work items x row tiles x partitions (the
   // kernel maps each workgroup to an item, tile and partition; see prefill.hip).
-  const int64_t tiles = ((int64_t)max_query_len * a.g + kPrefillRows - 1) / kPrefillRows;
+  const int64_t rows_per_wg = a.kind == kPrefillWide ? kWideRows : kPrefillRows;
+  const int64_t tiles = ((int64_t)max_query_len * a.g + rows_per_wg - 1) / rows_per_wg;
   const int64_t items = (int64_t)num_kv_heads * num_seqs;
   const int64_t grid = 8 * ((items + 7) / 8) * tiles * sp.P;
   if (grid > 0x7fffffffLL)
     return fail(PA_ERR_SHAPE, "pa_prefill: launch of %lld workgroups is too large", (long long)grid);
   a.tiles = (int)tiles;
   a.grid = (int)grid;
-  // K/V straight from global memory into LDS, V read with the transposing
-  // LDS reads (3-6% faster on the prefill workloads than staging through
-  // registers); PA_PREFILL_KERNEL=regs selects the register-staged kernel
-  // (read at each call, for comparisons).
-  {
-    const char* k = getenv("PA_PREFILL_KERNEL");
-    a.dma = !(k && strcmp(k, "regs") == 0);
-  }
   const hipStream_t st = static_cast<hipStream_t>(stream);
   take_main_kernel_events(&a.ev_start, &a.ev_stop);
   launch_prefill_mfma(a, st);

@@ -13,6 +13,14 @@ namespace pa {
 // kernel; a workgroup of 4 wavefronts takes 64 * kPrefillNC rows.
 constexpr int kPrefillNC = 2;
 constexpr int kPrefillRows = 64 * kPrefillNC;
+// Kernel variants of the 16-bit path: K/V staged through registers into
+// LDS; loaded straight into LDS by 4-wavefront workgroups of kPrefillRows
+// rows; the same with 8-wavefront workgroups of kWideRows rows (one per
+// compute unit, two wavefronts per SIMD, each step's K/V shared by twice the
+// rows).
+constexpr int kPrefillRegs = 0, kPrefillDirect = 1, kPrefillWide = 2;
+constexpr int kWideWaves = 8;
+constexpr int kWideRows = 64 * kPrefillNC * 2;
 
 struct PrefillArgs {
   void* out;
@@ -36,7 +44,7 @@ struct PrefillArgs {
   int lbs;        // log2(block_size)
   float qscale;   // |scale| * log2(e)
   pa_dtype_t dtype;
-  int dma;         // K/V straight from global memory into LDS, V read with transposing LDS reads
+  int kind;        // kPrefillRegs, kPrefillDirect or kPrefillWide
   void* ev_start;  // caller's timing events for prefill_mfma (hipEvent_t, or NULL)
   void* ev_stop;
 };

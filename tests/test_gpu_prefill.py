@@ -269,10 +269,12 @@ def test_fp32_bad_lengths_give_nan_rows():
     assert np.array_equal(out[:qs[1]], good[:qs[1]])
 
 
-# The register-staged kernel variant (PA_PREFILL_KERNEL=regs, K/V staged in
-# LDS through registers, V read with plain LDS reads) stays correct beside the
-# default, which loads K/V straight into LDS and reads V transposed.
-@pytest.mark.parametrize("variant", ["regs", "dma"])
+# The kernel variants stay correct beside each other: PA_PREFILL_KERNEL=regs
+# (K/V staged in LDS through registers, V read with plain LDS reads), dma
+# (K/V loaded straight into LDS, V read transposed) and w8 (the same with
+# 8-wavefront workgroups of 256 rows); the library picks dma or w8 from the
+# launch's sizes.
+@pytest.mark.parametrize("variant", ["regs", "dma", "w8"])
 @pytest.mark.parametrize("g,D,dtype", [(1, 128, "fp16"), (5, 64, "fp16"), (4, 128, "bf16"), (16, 64, "bf16")])
 def test_kernel_variants_every_row(monkeypatch, variant, g, D, dtype):
     monkeypatch.setenv("PA_PREFILL_KERNEL", variant)
@@ -290,7 +292,7 @@ def test_kernel_variants_agree_on_split_partitions(monkeypatch, psize):
     g = GpuPrefillStep(w)
     g.write()
     res = {}
-    for variant in ("regs", "dma"):
+    for variant in ("regs", "dma", "w8"):
         monkeypatch.setenv("PA_PREFILL_KERNEL", variant)
         res[variant] = to_f64(g.attend(partition_size=psize), "bf16")
     st, k, v = oracle_prefill_pools(w)
@@ -298,6 +300,7 @@ def test_kernel_variants_agree_on_split_partitions(monkeypatch, psize):
     for variant, got in res.items():
         _check(got, want, "bf16", f"{variant} split {psize}")
     assert np.abs(res["regs"] - res["dma"]).max() <= TOL["bf16"]
+    assert np.array_equal(res["dma"], res["w8"])
 
 
 @pytest.mark.parametrize("B,Hkv,g", [(150, 4, 2), (530, 4, 1)])
@@ -328,3 +331,25 @@ def test_many_items_every_row(B, Hkv, g):
     keep = np.ones(len(out), bool)
     keep[qs[bad]:qs[bad + 1]] = False
     _check(out[keep], want[keep], "bf16", f"many {B}")
+
+
+@pytest.mark.parametrize("key", ["p0", "p1", "p3", "p4"])
+def test_8_wavefront_kernel_bit_identical_to_4_wavefront_kernel(monkeypatch, key):
+    """Per row the 8-wavefront kernel (w8) does the arithmetic of the
+    4-wavefront direct-load kernel in the same order (same 32-row wavefront
+    groups, passes in position order, the same rescale decisions), so the
+    outputs agree to the bit; only the workgroups' tiles differ (256 rows,
+    not 128).  The default call picks one of the two."""
+    import torch
+
+    w = make_prefill_workload(key)
+    print(f"case w8 == dma {key}", flush=True)
+    g = GpuPrefillStep(w)
+    g.write()
+    out = {"auto": g.attend().clone()}
+    for variant in ("dma", "w8"):
+        monkeypatch.setenv("PA_PREFILL_KERNEL", variant)
+        out[variant] = g.attend().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(out["dma"].view(torch.int16), out["w8"].view(torch.int16))
+    assert torch.equal(out["dma"].view(torch.int16), out["auto"].view(torch.int16))
