@@ -545,7 +545,13 @@ __global__ __launch_bounds__(64 * W) void prefill_mfma(PrefillArgs a) {
   const uint4 ones = make_uint4(kOne2, kOne2, kOne2, kOne2);
   // One pass in four parts (the direct-load kernel also runs two passes
   // with their parts interleaved): scores, V operands, weights, products.
+  // Wave priority: a wavefront's matrix phases (score and PV products) run
+  // at priority 1, its softmax at 0, so that where the two wavefronts of a
+  // SIMD compete for issue the one feeding the matrix core wins (measured
+  // +2-3% on the prefill workloads; without it the older wavefront wins every
+  // tie).
   auto qk_scores = [&](int buf, int r0, f32x4 (&sc)[NC][2]) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int n = 0; n < NC; ++n) sc[n][0] = sc[n][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -588,6 +594,7 @@ __global__ __launch_bounds__(64 * W) void prefill_mfma(PrefillArgs a) {
   // groups, the accumulators rescaled and the weights recomputed.
   auto weights = [&](auto masked, const f32x4 (&sc)[NC][2], int t0, uint4 (&pb)[NC]) __attribute__((always_inline)) {
     constexpr bool kMasked = decltype(masked)::value;
+    __builtin_amdgcn_s_setprio(0);
     float x[NC][8], p[NC][8];
     uint32_t pbits = 0;
 #pragma unroll
@@ -632,6 +639,7 @@ __global__ __launch_bounds__(64 * W) void prefill_mfma(PrefillArgs a) {
   // products; the V^T operand of output tile u is one 16-byte LDS read
   // (kDma: the operands read before the softmax).
   auto products = [&](int buf, int r0, const uint4 (&pb)[NC], const uint4 (&vops)[VN]) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int n = 0; n < NC; ++n) l_acc[n] = mfma32<DT>(ones, pb[n], l_acc[n]);
 #pragma unroll
@@ -713,6 +721,7 @@ __global__ __launch_bounds__(64 * W) void prefill_mfma(PrefillArgs a) {
         else
           pass(std::false_type{}, buf, pp * kPair, t0);
       }
+      __builtin_amdgcn_s_setprio(0);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads into the other buffer
       __syncthreads();
       // (the next step's table entries arrived with that wait; using them
