@@ -303,20 +303,22 @@ def test_kernel_variants_agree_on_split_partitions(monkeypatch, psize):
     assert np.array_equal(res["dma"], res["w8"])
 
 
+@pytest.mark.parametrize("variant", ["dma", "w8"])
 @pytest.mark.parametrize("B,Hkv,g", [(150, 4, 2), (530, 4, 1)])
-def test_many_items_every_row(B, Hkv, g):
+def test_many_items_every_row(monkeypatch, variant, B, Hkv, g):
     """Workgroups run longest walk first within each XCD: 150 x 4 items put
     75 on each XCD (two per lane of the in-kernel order); 530 x 4 items
     exceed its 256 per XCD and take the plain tile order.  Empty chunks and
     one unservable sequence included."""
     import paged_kv_cache_117_amd as pa
 
+    monkeypatch.setenv("PA_PREFILL_KERNEL", variant)
     rng = np.random.default_rng(40 + B)
     prior = rng.integers(0, 70, size=B)
     chunk = rng.integers(0, 6, size=B)
     chunk[::17] = 0
     w = make_prefill_custom(f"many{B}", "bf16", prior, chunk, g * Hkv, Hkv, 64, seed=41 + B)
-    print(f"case many items B={B} Hkv={Hkv} g={g}", flush=True)
+    print(f"case many items B={B} Hkv={Hkv} g={g} {variant}", flush=True)
     g_ = GpuPrefillStep(w)
     g_.write()
     lens = g_.lens.clone()
@@ -353,3 +355,14 @@ def test_8_wavefront_kernel_bit_identical_to_4_wavefront_kernel(monkeypatch, key
     torch.cuda.synchronize()
     assert torch.equal(out["dma"].view(torch.int16), out["w8"].view(torch.int16))
     assert torch.equal(out["dma"].view(torch.int16), out["auto"].view(torch.int16))
+
+
+@pytest.mark.parametrize("bs,D,dtype", [(8, 128, "bf16"), (8, 64, "fp16"), (128, 128, "fp16")])
+def test_8_wavefront_kernel_block_sizes_every_row(monkeypatch, bs, D, dtype):
+    """The 8-wavefront kernel loads 8-row halves from one block each: at 8
+    slots a half is exactly one block, at 128 sixteen halves share one."""
+    monkeypatch.setenv("PA_PREFILL_KERNEL", "w8")
+    w = make_prefill_custom(f"w8bs{bs}_{D}", dtype, [0, 45, 300, 7], [140, 64, 37, 1], 8, 2, D,
+                            seed=960 + bs + D, block_size=bs)
+    print(f"case w8 bs={bs} D={D} {dtype}", flush=True)
+    _full_parity(w)
