@@ -8,32 +8,34 @@
 // group, rho = i * g + h (h = query head within the group), so one pass over
 // a K/V tile serves every query head that shares it.
 //
-// One workgroup (4 wavefronts) takes one (sequence, KV head, tile of R = 64 *
-// NC rows); each wave owns 16 * NC rows as NC matrix columns groups of 16.
+// One workgroup of W wavefronts (4, or 8 when the batch brings at least 256
+// query rows per (sequence, KV head)) takes one (sequence, KV head, tile of
+// R = 32 W rows); each wave owns 32 rows as two matrix column groups of 16.
 // The workgroup walks the positions 0..(largest p of its rows) in steps of
-// 32 (two 16-slot blocks):
-//  * K and V of the step go from the pool to a double-buffered LDS tile
-//    (16-byte loads, consecutive threads on consecutive bytes, rows padded
-//    by 16 bytes so the operand reads below are free of bank conflicts); the
+// 64, each computed as two passes of 32:
+//  * K and V of the step go from the pool straight into one of two LDS
+//    buffers (global->LDS 16-byte loads, 16-byte chunks XOR-swizzled on the
+//    load side so the operand reads below are free of bank conflicts); the
 //    next step's loads are in flight while the current one computes.
 //  * Scores S^T = K Q^T with v_mfma_f32_16x16x32: the K rows (A operand,
 //    lane (G, c) reads token c at dims 32k + 8G) come from LDS, the query
 //    rows (B operand) sit in registers for the whole walk.  Lane (G, c) gets
-//    S[token 4G + j][row c] for each 16-token half of the step.
+//    S[token 4G + j][row c] for each 16-token half of the pass.
 //  * Online softmax per row in base 2.  The running max is kept in raw score
 //    units, so each weight is one fma and one exp2: p = 2^(s*qs - m*qs),
 //    qs = |scale| * log2(e) (a negative scale flips the query's sign bits,
-//    which is exact).  Only steps that cross a row's causal limit apply the
+//    which is exact).  Only passes that cross a row's causal limit apply the
 //    mask.
 //  * PV transposed, O^T = V^T P^T, again with v_mfma_f32_16x16x32: lane
 //    group G's eight k-slots are tokens 4G..4G+3 of the first half and of
 //    the second half, which are exactly the eight weights the lane holds
-//    from the score layout.  V is staged in LDS already transposed into that
-//    k-slot order (each thread loads two consecutive tokens and packs their
-//    values pairwise), so the V operand of each output tile is one 16-byte
-//    LDS read, shared by all of the wave's column groups.  The output keeps the query
-//    row in the lane's column, so the rescale by 2^(m_old - m_new) is
+//    from the score layout.  The V^T operand comes from the transposing LDS
+//    read (two per output tile, shared by the wave's column groups), so
+//    output tile u holds dims 16u..16u+15.  The output keeps the query row
+//    in the lane's column, so the rescale by 2^(m_old - m_new) is
 //    lane-local.
+// A register-staged variant (K/V through registers, V staged transposed in
+// LDS) is kept for comparison; it computes the same rows within rounding.
 //
 // Positions past L-1 inside the last step re-read position L-1 (finite;
 // masked).  Block ids outside [0, num_blocks) are never dereferenced: the
@@ -286,16 +288,17 @@ __global__ __launch_bounds__(64 * W) void prefill_mfma(PrefillArgs a) {
   // bank-conflict counter for these exact lane patterns on gfx950: rows
   // padded to 272 bytes measured 8 cycles (two-way conflicts); unpadded
   // rows with chunk j of row r stored at chunk j ^ kkey(r),
-  // kkey(r) = r mod (D / 8), measured 4, and so do the stash writes (lane =
-  // chunk of one token row).
+  // kkey(r) = r mod (D / 8), measured 4, and so do the stash writes of the
+  // register-staged variant (lane = chunk of one token row).
   __shared__ __align__(16) uint16_t sK[2][kStep][ROW];
-  // V transposed for the PV A operand: row (pass, u * 16 + c) holds head dim
-  // DPL * c + u of the pass's 32 positions in k-slot order (slot 8G + e is
-  // token 16 (e / 4) + 4G + e % 4), so lane (G, c) reads its operand for
-  // output tile u as one 16-byte chunk.  Rows are 80 bytes: the stash's
-  // 4-byte writes (16 lanes, 16 consecutive rows, one column) then hit 16
-  // distinct banks; the 16-byte reads measure two-way conflicts, which
-  // costs less here than a 64-byte swizzled row whose writes conflict.
+  // Register-staged variant: V transposed for the PV A operand: row
+  // (pass, u * 16 + c) holds head dim DPL * c + u of the pass's 32
+  // positions in k-slot order (slot 8G + e is token 16 (e / 4) + 4G + e % 4),
+  // so lane (G, c) reads its operand for output tile u as one 16-byte chunk.
+  // Rows are 80 bytes: the stash's 4-byte writes (16 lanes, 16 consecutive
+  // rows, one column) then hit 16 distinct banks; the 16-byte reads measure
+  // two-way conflicts, which costs less here than a 64-byte swizzled row
+  // whose writes conflict.
   __shared__ __align__(16) uint16_t sV[kDma ? 1 : 2][kDma ? 1 : kPairs * D][kDma ? 8 : VROW];
   // kDma: V in token-row order, 16-byte chunk j of row r stored at chunk
   // j ^ vkey(r), so the transposing reads of one instruction (16 rows, the
