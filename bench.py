@@ -116,7 +116,8 @@ def parse():
                     help="pa_decode kernel override (PA_DECODE_KERNEL): valu = vector-ALU kernel for 16-bit KV "
                          "too, partition = matrix-core partition kernels instead of the even split")
     ap.add_argument("--no-second", action="store_true",
-                    help="c2 only: skip the Qwen2.5-72B (c5) sub-record of the default run")
+                    help="c2 only: skip the Qwen2.5-72B decode (c5) and Llama-3.1-8B prefill (p1) "
+                         "sub-records of the default run")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("READ_CSV", "WRITE_CSV", "COPY_READ_CSV", "COPY_WRITE_CSV"),
@@ -484,11 +485,18 @@ def main_prefill(args):
     pa_prefill over every sequence's context."""
     import torch
 
+    cpu_budget = 0.0 if args.no_cpu_baseline else args.cpu_seconds
+    res = prefill_bench(torch, args.config, args, args.steps, args.warmup, cpu_budget, args.partition_size or 0)
+    print(json.dumps(res), flush=True)
+
+
+def prefill_bench(torch, key, args, steps, warmup, cpu_budget, pf_psize):
+    """The chunked-prefill measurement of `key` (the record main_prefill prints)."""
     import paged_kv_cache_117_amd as pa
     from paged_kv_cache_117_amd import metrics
     from workloads import make_prefill_workload
 
-    w = make_prefill_workload(args.config, block_size=args.block_size)
+    w = make_prefill_workload(key, block_size=args.block_size)
     eb = metrics.ELEM_BYTES[w.dtype]
     tdt = {"fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
     order = w.perm if args.placement == "shuffled" else np.arange(w.num_blocks, dtype=np.int32)
@@ -524,7 +532,6 @@ def main_prefill(args):
     k_new, v_new = dev(w.k_new, True), dev(w.v_new, True)
     lens = dev(w.context_lens.astype(np.int32))
     qstart = dev(w.query_start.astype(np.int32))
-    pf_psize = args.partition_size or 0
     ws_bytes = pa.prefill_workspace_bytes(w.num_seqs, w.num_tokens, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                           w.max_query_len, w.max_context_len, pf_psize)
     sets = []
@@ -547,22 +554,22 @@ def main_prefill(args):
         if ev is not None:
             ev[1].record(stream)
 
-    args.warmup = warm_up(torch, lambda i: step(i % R), args.warmup)
-    evs, kevs = timing_events(torch, args.steps, stream)
+    warmup = warm_up(torch, lambda i: step(i % R), warmup)
+    evs, kevs = timing_events(torch, steps, stream)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(i % R)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    pf_ms = call_pass(torch, step, args.steps, R, evs)
+    ms_step = t_start.elapsed_time(t_end) / steps
+    pf_ms = call_pass(torch, step, steps, R, evs)
     pf_avg = float(pf_ms.mean())
-    kern_avg = main_kernel_pass(torch, step, args.steps, R, kevs)
+    kern_avg = main_kernel_pass(torch, step, steps, R, kevs)
     flops = metrics.prefill_flops(w.prior_lens, w.chunk_lens, w.num_q_heads, w.head_dim)
     io = metrics.prefill_io_bytes(w.prior_lens, w.chunk_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, eb)
     peak = MFMA_PEAK_TFLOPS[w.dtype]
@@ -573,8 +580,8 @@ def main_prefill(args):
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -582,8 +589,8 @@ def main_prefill(args):
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {
-            "workload": PREFILL_NAMES[args.config],
-            "key": args.config,
+            "workload": PREFILL_NAMES[key],
+            "key": key,
             "num_seqs": w.num_seqs,
             "num_tokens": w.num_tokens,
             "flops_per_step": flops,
@@ -616,9 +623,9 @@ def main_prefill(args):
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = prefill_cpu_baseline(w, tables, args.cpu_seconds)
-    print(json.dumps(res), flush=True)
+    if cpu_budget > 0:
+        res["cpu_baseline"] = prefill_cpu_baseline(w, tables, cpu_budget)
+    return res
 
 
 def main_swap(args):
@@ -1058,6 +1065,15 @@ def main():
         res["c5"]["kv_bytes_per_step"] = sub["config"]["kv_bytes_per_step"]
         res["c5"]["partition_size"] = sub["config"]["partition_size"]
         res["c5"]["unit"] = "GB/s"
+        # and the chunked-prefill path (f1) on the Llama-3.1-8B chunk layer:
+        # its own warm-up by time (the matrix-bound load after the two
+        # memory-bound ones) and at least 50 timed steps
+        pre = prefill_bench(torch, "p1", args, max(args.steps, 50), None, 0.0, 0)
+        res["p1"] = {k: pre[k] for k in ("value", "unit", "mfma_peak_frac", "ms_per_step", "prefill_ms",
+                                          "prefill_main_kernel_ms", "prefill_call_mfma_frac", "roofline",
+                                          "warmup", "steps", "dtype")}
+        res["p1"]["workload"] = pre["config"]["workload"]
+        res["p1"]["flops_per_step"] = pre["config"]["flops_per_step"]
     res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
