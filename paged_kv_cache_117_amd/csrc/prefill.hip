@@ -119,29 +119,58 @@ struct LptItem {
   int ntiles = 0;  // row tiles of a servable item
   int base = 0;    // cached positions before the chunk
   int rows = 0;    // chunk tokens x heads per KV head
+  int tmax = 0;    // last chunk token, (rows - 1) / g
+  int q0 = 0, q1 = 0, L = 0;  // the sequence's query range and length, as read
   bool used = false;
   bool ok = false;  // servable
 };
 
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+// Inclusive scans over the wavefront's 64 lanes with DPP (row shifts by 1,
+// 2, 4, 8 inside each row of 16 lanes, lanes before the row start taking 0,
+// then row 0's last lane into row 1 and row 2's into row 3, then row 1's
+// last lane into rows 2 and 3): six VALU steps, where each step of a lane
+// shuffle is a round trip through the LDS crossbar.  The pick below runs
+// about ten wave-wide sums per workgroup before any of its loads can go
+// out, so their latency is part of every workgroup's start.  Max takes
+// values >= 0 (0 stands for the missing lanes).
+__device__ __forceinline__ int wave_scan_add(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return x;
 }
+__device__ __forceinline__ int wave_scan_max(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));
+  return x;
+}
+__device__ __forceinline__ int wave_sum(int x) { return __builtin_amdgcn_readlane(wave_scan_add(x), 63); }
 
-// Tiles of the item walking at least v >= 1 steps.
+// Tiles of the item walking at least v >= 1 steps (v at most one past the
+// item's longest walk, so (v - 1) * kStep stays within the context length
+// plus a step).  need = (v - 1) kStep - base is the chunk token the walk
+// must reach: none of the item's tiles when need > tmax, else those whose
+// last row (t + 1) R - 1 reaches row need * g (all when need <= 0).  An
+// unservable item (base = tmax = ntiles = 0) counts one tile at v = 1.
+// Straight-line selects (the clamp keeps need * g <= rows - 1): the search
+// evaluates this for four items per lane about ten times per workgroup.
 __device__ __forceinline__ int lpt_count(const LptItem& it, int v, int R, int g) {
-  if (!it.used) return 0;
-  if (!it.ok) return v <= 1 ? 1 : 0;
-  const int64_t need = (int64_t)(v - 1) * kStep - it.base;  // the last row's token must reach this
-  if (need <= 0) return it.ntiles;
-  const int64_t rows_needed = need * g;  // tile t's last row (t + 1) R - 1 must be >= this
-  if (rows_needed > it.rows - 1) return 0;
-  return it.ntiles - (int)(rows_needed / R);
+  const int need = (v - 1) * kStep - it.base;
+  const int tiles = it.ntiles - min(max(need, 0), it.tmax) * g / R;
+  return !it.used || need > it.tmax ? 0 : (it.ok ? tiles : 1);
 }
 
-// Rank k of XCD xcd -> (item, tile); false past the XCD's last workgroup.
-__device__ bool lpt_pick(const PrefillArgs& a, int xcd, int k, int per_xcd, int R, int& item_out, int& tile_out) {
+// Rank k of XCD xcd -> (item, tile) and the item's sequence's query_start
+// entries and length as read here; false past the XCD's last workgroup.
+__device__ bool lpt_pick(const PrefillArgs& a, int xcd, int k, int per_xcd, int R, int& item_out, int& tile_out,
+                         int& q0_out, int& q1_out, int& L_out) {
   const int lane = (int)threadIdx.x & 63;
   const int items = a.B * a.Hkv;
   const int c = (per_xcd + 63) >> 6;  // items per lane, lane-major
@@ -156,10 +185,14 @@ __device__ bool lpt_pick(const PrefillArgs& a, int xcd, int k, int per_xcd, int 
     const int s = item / a.Hkv;
     const int q0 = a.qs[s], q1 = a.qs[s + 1], L = a.cl[s];
     const int T = q1 - q0;
+    it[e].q0 = q0;
+    it[e].q1 = q1;
+    it[e].L = L;
     it[e].used = true;
     it[e].ok = !(q0 < 0 || q1 < q0 || q1 > a.N || T > L || (int64_t)L > ((int64_t)a.maxb << a.lbs) || T > a.max_q);
     if (it[e].ok) {
       it[e].rows = T * a.g;
+      it[e].tmax = (it[e].rows - 1) / a.g;
       it[e].base = L - T;
       it[e].ntiles = (it[e].rows + R - 1) / R;
       if (it[e].ntiles > 0) vmax = max(vmax, (L - 1) / kStep + 1);
@@ -167,8 +200,7 @@ __device__ bool lpt_pick(const PrefillArgs& a, int xcd, int k, int per_xcd, int 
       vmax = max(vmax, 1);
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) vmax = max(vmax, __shfl_xor(vmax, o));
+  vmax = __builtin_amdgcn_readlane(wave_scan_max(vmax), 63);
   auto count = [&](int v) {
     int n = 0;
 #pragma unroll
@@ -191,16 +223,11 @@ __device__ bool lpt_pick(const PrefillArgs& a, int xcd, int k, int per_xcd, int 
     cnt[e] = lpt_count(it[e], lo, R, a.g) - lpt_count(it[e], lo + 1, R, a.g);
     mine += cnt[e];
   }
-  int incl = mine;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
+  const int incl = wave_scan_add(mine);
   const int excl = incl - mine;
   const bool here = excl <= r && r < incl;
   const int src = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(here));
-  int pick_item = 0, pick_tile = 0;
+  int pick_item = 0, pick_tile = 0, pq0 = 0, pq1 = 0, pL = 0;
   if (here) {
     int rr = r - excl;
 #pragma unroll
@@ -208,12 +235,18 @@ __device__ bool lpt_pick(const PrefillArgs& a, int xcd, int k, int per_xcd, int 
       if (rr >= 0 && rr < cnt[e]) {
         pick_item = (lane * c + e) * 8 + xcd;
         pick_tile = it[e].ok ? it[e].ntiles - lpt_count(it[e], lo, R, a.g) + rr : a.tiles - 1;
+        pq0 = it[e].q0;
+        pq1 = it[e].q1;
+        pL = it[e].L;
       }
       rr -= cnt[e];
     }
   }
   item_out = __builtin_amdgcn_readlane(pick_item, src);
   tile_out = __builtin_amdgcn_readlane(pick_tile, src);
+  q0_out = __builtin_amdgcn_readlane(pq0, src);
+  q1_out = __builtin_amdgcn_readlane(pq1, src);
+  L_out = __builtin_amdgcn_readlane(pL, src);
   return true;
 }
 
@@ -320,8 +353,10 @@ __global__ __launch_bounds__(64 * W) void prefill_mfma(PrefillArgs a) {
   const int per_xcd = (items + 7) >> 3;  // items per XCD (upper bound)
   const int xcd = (int)(blockIdx.x & 7), local = (int)(blockIdx.x >> 3);
   int item, tile, part = 0;
-  if (a.P == 1 && per_xcd <= 64 * kLptPerLane) {
-    if (!lpt_pick(a, xcd, local, per_xcd, R, item, tile)) return;
+  int q0 = 0, q1 = 0, L = 0;
+  const bool picked = a.P == 1 && per_xcd <= 64 * kLptPerLane;
+  if (picked) {
+    if (!lpt_pick(a, xcd, local, per_xcd, R, item, tile, q0, q1, L)) return;
   } else {
     item = (local % per_xcd) * 8 + xcd;
     const int tp = local / per_xcd;
@@ -333,7 +368,11 @@ __global__ __launch_bounds__(64 * W) void prefill_mfma(PrefillArgs a) {
   const int s = item / a.Hkv;
   if (s >= a.B) return;
 
-  const int q0 = a.qs[s], q1 = a.qs[s + 1], L = a.cl[s];
+  if (!picked) {  // (the pick read these already)
+    q0 = a.qs[s];
+    q1 = a.qs[s + 1];
+    L = a.cl[s];
+  }
   const int T = q1 - q0;
   const int g = a.g;
   if (q0 < 0 || q1 < q0 || q1 > a.N || T > L || (int64_t)L > ((int64_t)a.maxb << a.lbs) || T > a.max_q ||
