@@ -304,12 +304,13 @@ def test_kernel_variants_agree_on_split_partitions(monkeypatch, psize):
 
 
 @pytest.mark.parametrize("variant", ["dma", "w8"])
-@pytest.mark.parametrize("B,Hkv,g", [(150, 4, 2), (530, 4, 1)])
+@pytest.mark.parametrize("B,Hkv,g", [(150, 4, 2), (512, 4, 1), (514, 4, 1), (530, 4, 1)])
 def test_many_items_every_row(monkeypatch, variant, B, Hkv, g):
     """Workgroups run longest walk first within each XCD: 150 x 4 items put
-    75 on each XCD (two per lane of the in-kernel order); 530 x 4 items
-    exceed its 256 per XCD and take the plain tile order.  Empty chunks and
-    one unservable sequence included."""
+    75 on each XCD (two per lane of the in-kernel order); 512 x 4 put
+    exactly its 256 (four per lane); 514 x 4 (257 per XCD) and 530 x 4
+    exceed it and take the plain tile order.  Empty chunks and one
+    unservable sequence included."""
     import paged_kv_cache_117_amd as pa
 
     monkeypatch.setenv("PA_PREFILL_KERNEL", variant)
