@@ -182,6 +182,44 @@ def copy_bandwidth(torch, nbytes=1 << 30, reps=200):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+READ_PROBE_GRIDS = {"sequential": (256, 512, 1024, 2048), "gather_4k": (256, 512, 1024)}
+
+
+def read_ceiling(torch, nbytes=1 << 31, reps=20):
+    """The box's read-only HBM ceiling from the library's read probe
+    (pa_probe_read): a sequential sweep, and whole 4 KiB chunks gathered in a
+    seeded random order -- the decode kernels' access shape, one KV head's
+    16-slot tile per chunk.  Bytes read per second, best over a few launch
+    sizes (HIP events around `reps` launches after one untimed launch)."""
+    import paged_kv_cache_117_amd as pa
+
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    order = torch.randperm(nbytes // 4096, device="cuda", generator=gen).to(torch.int32)
+    wg_max = max(max(v) for v in READ_PROBE_GRIDS.values())
+    sink = torch.empty(wg_max * 256, dtype=torch.int32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    for mode, grids in READ_PROBE_GRIDS.items():
+        best, best_wg = 0.0, 0
+        for wg in grids:
+            co = order if mode == "gather_4k" else None
+            pa.probe_read(buf, sink, wg, co)
+            e0.record()
+            for _ in range(reps):
+                pa.probe_read(buf, sink, wg, co)
+            e1.record()
+            torch.cuda.synchronize()
+            gbs = nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+            if gbs > best:
+                best, best_wg = gbs, wg
+        out[f"{mode}_gbps"] = round(best, 1)
+        out[f"{mode}_workgroups"] = best_wg
+    del buf, order, sink
+    return out
+
+
 def _counter_means(path, kernel_pred):
     vals = {}
     with open(path) as f:
@@ -1030,7 +1068,8 @@ def main():
     # and its ~0.1 s of HBM-bound work also brings the GPU's clocks up before
     # the warm-up steps.
     cg = copy_bandwidth(torch)
-    psize = args.partition_size if args.partition_size is not None else WORKLOAD_PARTITION.get(args.config, 0)
+    rc = read_ceiling(torch)
+    psize =args.partition_size if args.partition_size is not None else WORKLOAD_PARTITION.get(args.config, 0)
     cpu_budget = 0.0 if args.no_cpu_baseline else args.cpu_seconds
     core = decode_bench(torch, args.config, args, psize, args.steps, args.warmup, cpu_budget)
     res = {
@@ -1052,6 +1091,10 @@ def main():
     res.update(core)
     res["device_copy_gbps"] = round(cg, 1)
     res["decode_frac_of_copy"] = round(res["decode_kv_gbps"] / cg, 4)
+    res["read_ceiling"] = dict(rc)
+    res["read_ceiling"]["main_kernel_frac_of_gather"] = round(res["roofline"]["achieved"] / rc["gather_4k_gbps"], 4)
+    res["read_ceiling"]["note"] = ("read-only probe kernels on this box (pa_probe_read): the main kernel's "
+                                   "algorithmic bytes per second over the 4 KiB random-gather rate")
     res["pages_context"] = PAGES_CONTEXT
     # The second target workload (Qwen2.5-72B layer, 512-position partitions)
     # beside the headline, measured the same way in the same run.
@@ -1065,6 +1108,7 @@ def main():
         res["c5"]["kv_bytes_per_step"] = sub["config"]["kv_bytes_per_step"]
         res["c5"]["partition_size"] = sub["config"]["partition_size"]
         res["c5"]["unit"] = "GB/s"
+        res["c5"]["main_kernel_frac_of_gather"] = round(sub["roofline"]["achieved"] / rc["gather_4k_gbps"], 4)
         # and the chunked-prefill path (f1) on the Llama-3.1-8B chunk layer:
         # its own warm-up by time (the matrix-bound load after the two
         # memory-bound ones) and at least 50 timed steps

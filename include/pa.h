@@ -261,8 +261,12 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads
  * T > L, L > max_blocks_per_seq * block_size, T > max_query_len, L >
  * max_context_len in a split launch, or a row range outside [0, num_tokens)
  * gets NaN rows (those inside [0, num_tokens)); a block id outside
- * [0, num_blocks) makes the rows that would read it NaN.  `out` must not
- * alias any input or the workspace.
+ * [0, num_blocks) makes the rows that would read it NaN.  The launch is
+ * sized from the sizes passed assuming query_start keeps its rules (the
+ * chunks together hold at most num_tokens tokens); for a query_start that
+ * decreases somewhere, which rows are written is unspecified (nothing
+ * outside the given buffers is read or written).  `out` must not alias any
+ * input or the workspace.
  */
 pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, const void* v_pool,
                        const int32_t* block_tables, const int32_t* context_lens,
@@ -287,6 +291,30 @@ pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, const void*
  * its argument checks leaves the request pending.
  */
 pa_status_t pa_time_next_main_kernel(void* start_event, void* stop_event);
+
+/*
+ * pa_probe_read -- read-bandwidth probe (instrumentation, not part of the
+ * pages' method): the measured ceiling that the decode kernels' HBM rates are
+ * read against.  Reads device memory with 16-byte non-temporal loads and
+ * stores one 32-bit digest per thread so the reads cannot be dropped.
+ *   buf          device, `bytes` bytes (a multiple of 4096), 16-byte aligned;
+ *                read only
+ *   mode 0       sequential: a grid-stride sweep over the whole buffer
+ *   mode 1       4 KiB gather: wavefront w of W reads whole 4 KiB chunks
+ *                chunk_order[w], chunk_order[w + W], ... (four chunks in
+ *                flight), the access shape of gathering one KV head's
+ *                16-slot tiles (16 x 128 dims x 2 bytes) from scattered
+ *                blocks; entries outside [0, bytes / 4096) are skipped
+ *   chunk_order  device, int32 [num_chunks] (mode 1 only; may be NULL for
+ *                mode 0)
+ *   workgroups   launch size (256 threads each), 1 .. 2^20
+ *   sink         device, uint32 [workgroups * 256], written
+ * Returns PA_ERR_UNSUPPORTED for another mode, PA_ERR_SHAPE / PA_ERR_NULL for
+ * bad sizes or pointers, PA_ERR_LAUNCH if the launch fails; nothing is
+ * allocated.
+ */
+pa_status_t pa_probe_read(const void* buf, size_t bytes, const int32_t* chunk_order, int num_chunks,
+                          int mode, int workgroups, uint32_t* sink, void* stream);
 
 /* Bytes of workspace pa_prefill needs for these sizes (0 when the launch is
  * not split); depends on sizes only, not on the device or the dtype.

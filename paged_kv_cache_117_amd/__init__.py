@@ -24,6 +24,7 @@ from .ops import (  # noqa: F401
     decode_workspace_bytes,
     prefill,
     prefill_workspace_bytes,
+    probe_read,
     swap_blocks,
     time_next_main_kernel,
     write_kv,

@@ -41,6 +41,7 @@ SIGNATURES = {
     "pa_last_error": (_c.c_char_p, []),
     "pa_abi_version": (_i32, []),
     "pa_time_next_main_kernel": (_i32, [_vp, _vp]),
+    "pa_probe_read": (_i32, [_vp, _sz, _vp, _i32, _i32, _i32, _vp, _vp]),
     "pa_bm_create": (_vp, [_i32, _i32, _pi32]),
     "pa_bm_destroy": (None, [_vp]),
     "pa_bm_add_seq": (_i32, [_vp, _i64]),

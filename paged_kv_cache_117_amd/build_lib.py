@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpa.so")
 
-HIP_SOURCES = ["decode.hip", "decode_mfma.hip", "decode_api.hip", "cache_ops.hip", "prefill.hip", "prefill_api.hip"]
+HIP_SOURCES = ["decode.hip", "decode_mfma.hip", "decode_api.hip", "cache_ops.hip", "prefill.hip", "prefill_api.hip",
+               "probe.hip"]
 CPP_SOURCES = ["block_manager.cpp", "sha256.cpp", "errors.cpp"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 

@@ -113,7 +113,7 @@ __device__ __forceinline__ float max_groups(float x, int x16, int x32) {
 // counts (every wavefront of the workgroup computes the same pick).
 // Unservable items take one workgroup each, ranked last, at the tile that
 // writes their NaN rows.
-constexpr int kLptPerLane = 4;  // items per lane: the in-kernel order covers up to 256 items per XCD
+// (kLptPerLane items per lane: the in-kernel order covers up to 256 items per XCD)
 
 struct LptItem {
   int ntiles = 0;  // row tiles of a servable item

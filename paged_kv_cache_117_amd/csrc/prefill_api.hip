@@ -212,12 +212,30 @@ extern "C" pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, 
     if (k && strcmp(k, "dma") == 0) a.kind = kPrefillDirect;
     if (k && strcmp(k, "w8") == 0) a.kind = kPrefillWide;
   }
-  // Grid: 8 XCDs x ceil(items / 8) work items x row tiles x partitions (the
-  // kernel maps each workgroup to an item, tile and partition; see prefill.hip).
+  // Grid: 8 XCDs x ranks per XCD.  In the tile order (split launches, or
+  // more than 64 * kLptPerLane items per XCD) rank r names an item, a row
+  // tile and a partition: ceil(items / 8) x row tiles of max_query_len x
+  // partitions.  In the longest-first order rank k is the XCD's k-th longest
+  // walk and ranks past the XCD's last walk exit at once, so the grid need
+  // only cover the walks that can exist.  Since query_start is non-decreasing
+  // from 0 to num_tokens, the sequences' chunks hold num_tokens tokens in
+  // all, one XCD holds at most m = ceil(Hkv / 8) KV heads of a sequence, and
+  // each of its items rounds up to whole row tiles once: at most
+  // ceil(m * num_tokens * g / R) + ceil(items / 8) walks per XCD.  A step
+  // of mostly single-token sequences beside a few long chunks then launches
+  // about as many workgroups as it has walks instead of max_query_len's
+  // tiles for every sequence.
   const int64_t rows_per_wg = a.kind == kPrefillWide ? kWideRows : kPrefillRows;
   const int64_t tiles = ((int64_t)max_query_len * a.g + rows_per_wg - 1) / rows_per_wg;
   const int64_t items = (int64_t)num_kv_heads * num_seqs;
-  const int64_t grid = 8 * ((items + 7) / 8) * tiles * sp.P;
+  const int64_t per_xcd = (items + 7) / 8;
+  int64_t ranks = per_xcd * tiles * sp.P;
+  if (sp.P == 1 && per_xcd <= 64 * kLptPerLane) {
+    const int64_t m = (num_kv_heads + 7) / 8;
+    const int64_t walks = (m * num_tokens * a.g + rows_per_wg - 1) / rows_per_wg + per_xcd;
+    if (walks < ranks) ranks = walks;
+  }
+  const int64_t grid = 8 * ranks;
   if (grid > 0x7fffffffLL)
     return fail(PA_ERR_SHAPE, "pa_prefill: launch of %lld workgroups is too large", (long long)grid);
   a.tiles = (int)tiles;

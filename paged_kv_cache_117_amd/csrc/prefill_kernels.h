@@ -39,7 +39,7 @@ struct PrefillArgs {
   float* ws_o;    // P > 1: [N * Hq][P][D] normalised partial rows
   float* ws_m;    // P > 1: [N * Hq][P] reference max, base-2 domain
   float* ws_l;    // P > 1: [N * Hq][P] sum of weights
-  int grid;       // workgroups launched: 8 * ceil(B * Hkv / 8) * tiles * P
+  int grid;       // workgroups launched: 8 x ranks per XCD (see prefill_grid_ranks)
   int neg_scale;  // scale < 0: the kernel flips the query's sign
   int lbs;        // log2(block_size)
   float qscale;   // |scale| * log2(e)
@@ -51,6 +51,10 @@ struct PrefillArgs {
 
 // Positions per step of the prefill kernel (partitions are whole steps).
 constexpr int kPrefillStep = 64;
+
+// Work items (sequence, KV head) per lane of the kernel's longest-walk-first
+// pick: unsplit launches with up to 64 * kLptPerLane items per XCD use it.
+constexpr int kLptPerLane = 4;
 
 // Workspace of a split launch: partial rows, then maxima, then sums.
 struct PrefillWorkspace {

@@ -317,5 +317,24 @@ def time_next_main_kernel(start, stop) -> None:
     check_status(LIB.pa_time_next_main_kernel(handles[0], handles[1]), "pa_time_next_main_kernel")
 
 
+def probe_read(buf, sink, workgroups: int, chunk_order=None, stream=None) -> None:
+    """pa_probe_read: read ``buf`` (a contiguous device tensor of a multiple of
+    4096 bytes) sequentially (``chunk_order`` None) or as whole 4 KiB chunks
+    in the order ``chunk_order`` (device int32) gives; ``sink`` is a device
+    int32 tensor of at least ``workgroups * 256`` elements."""
+    _device_tensor(buf, "buf")
+    _device_tensor(sink, "sink", torch.int32)
+    nbytes = buf.numel() * buf.element_size()
+    if sink.numel() < workgroups * 256:
+        raise ValueError(f"sink holds {sink.numel()} words, the launch writes {workgroups * 256}")
+    if chunk_order is None:
+        mode, order, n = 0, None, 0
+    else:
+        _device_tensor(chunk_order, "chunk_order", torch.int32, 1)
+        mode, order, n = 1, chunk_order.data_ptr(), chunk_order.numel()
+    check_status(LIB.pa_probe_read(buf.data_ptr(), nbytes, order, n, mode, int(workgroups), sink.data_ptr(),
+                                   _stream_handle(stream)), "pa_probe_read")
+
+
 def _as_ptr(arr, ctype):
     return arr.ctypes.data_as(ctypes.POINTER(ctype))

@@ -203,3 +203,18 @@ def test_decode_noalloc_host_validation():
     st = LIB.pa_decode_noalloc(None, p, p, p, p, p, 4, 8, 2, 128, 16, 1, 8, 64, ctypes.c_float(0.1), 2, 0, None)
     assert st == 1
     assert LIB.pa_decode_noalloc(p, p, p, p, p, p, 0, 8, 2, 128, 16, 1, 8, 64, ctypes.c_float(0.1), 2, 0, None) == 0
+
+
+def test_probe_read_host_validation():
+    """pa_probe_read refuses bad modes, sizes and pointers on the host (the
+    fake pointer below is never dereferenced: every call fails before a
+    launch)."""
+    p = 4096
+    assert L.pa_probe_read(p, 8192, p, 2, 2, 1, p, None) == 3  # mode
+    assert L.pa_probe_read(p, 4095, None, 0, 0, 1, p, None) == 2  # not whole 4 KiB chunks
+    assert L.pa_probe_read(p, 0, None, 0, 0, 1, p, None) == 2
+    assert L.pa_probe_read(p, 8192, None, 0, 0, 0, p, None) == 2  # workgroups
+    assert L.pa_probe_read(p + 8, 8192, None, 0, 0, 1, p, None) == 2  # alignment
+    assert L.pa_probe_read(None, 8192, None, 0, 0, 1, p, None) == 1
+    assert L.pa_probe_read(p, 8192, None, 4, 1, 1, p, None) == 1  # gather without an order
+    assert L.pa_probe_read(p, 8192, p, -1, 1, 1, p, None) == 2

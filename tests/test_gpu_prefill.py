@@ -367,3 +367,46 @@ def test_8_wavefront_kernel_block_sizes_every_row(monkeypatch, bs, D, dtype):
                             seed=960 + bs + D, block_size=bs)
     print(f"case w8 bs={bs} D={D} {dtype}", flush=True)
     _full_parity(w)
+
+
+def _walk_bound_cases():
+    rng = np.random.default_rng(77)
+    # Hkv = 1: sequence s is XCD s mod 8's item, and every chunk sits on XCD 0
+    # (129 rows: two 128-row tiles each, the rounding the bound allows for)
+    c1 = np.zeros(40, np.int64)
+    c1[::8] = 129
+    # Hkv = 12: two KV heads of a sequence on one XCD (m = 2)
+    c2 = np.array([300, 1, 1, 1, 1, 1, 1, 77, 1, 1])
+    # two long chunks beside single tokens (a mixed chunked-prefill step)
+    c3 = np.ones(40, np.int64)
+    c3[[5, 22]] = 257
+    return {
+        "one_xcd_g1": (rng.integers(0, 300, size=40), c1, 1, 1, 64, "fp16"),
+        "hkv12_g2": (rng.integers(0, 600, size=10), c2, 24, 12, 64, "bf16"),
+        "singles_and_chunks": (rng.integers(0, 900, size=40), c3, 32, 8, 128, "bf16"),
+    }
+
+
+@pytest.mark.parametrize("variant", ["dma", "w8"])
+@pytest.mark.parametrize("case", ["one_xcd_g1", "hkv12_g2", "singles_and_chunks"])
+def test_launch_covers_every_walk_every_row(monkeypatch, variant, case):
+    """Unsplit launches in the longest-first order size their grid by the
+    walks the batch can hold (chunks of num_tokens tokens in all), not by
+    max_query_len's row tiles for every sequence: batches whose walks all sit
+    on one XCD, with two KV heads of a sequence per XCD, or with single
+    tokens beside long chunks, every row against the oracle -- also when
+    max_query_len overstates the longest chunk."""
+    import paged_kv_cache_117_amd as pa
+
+    monkeypatch.setenv("PA_PREFILL_KERNEL", variant)
+    prior, chunk, Hq, Hkv, D, dtype = _walk_bound_cases()[case]
+    w = make_prefill_custom(f"walks_{case}", dtype, prior, chunk, Hq, Hkv, D, seed=780 + len(case))
+    print(f"case walk bound {case} {variant}", flush=True)
+    g = GpuPrefillStep(w)
+    g.write()
+    st, k, v = oracle_prefill_pools(w)
+    want = oracle.prefill(w.q, k, v, st.tables, w.context_lens, w.query_start, w.scale, w.dtype)
+    for max_q in (w.max_query_len, int(w.query_start[-1])):
+        out = to_f64(pa.prefill(g.q, g.k, g.v, g.tables, g.lens, g.qstart, w.scale, max_q, w.max_context_len),
+                     dtype)
+        _check(out, want, dtype, f"{case} {variant} max_query_len={max_q}")
