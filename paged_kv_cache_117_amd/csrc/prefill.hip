@@ -48,6 +48,7 @@
 
 #include <type_traits>
 
+#include "decode_tile.h"
 #include "pa_device.h"
 #include "prefill_kernels.h"
 
@@ -293,6 +294,145 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t l
 }
 #pragma clang diagnostic pop
 
+// Decode-shaped items: a (sequence, KV head) whose rows fit one matrix
+// column group (T * g <= 16 -- single tokens of a mixed step, or a few) on
+// blocks of at least 16 slots.  Through the 64-position LDS steps such an
+// item keeps one step of K/V in flight per workgroup and computes 16 rows
+// per pass for its few real ones; here it runs like the decode kernels
+// instead: the first four wavefronts deal the partition's 16-slot tiles
+// round-robin (wave w takes tiles w, w + 4, ...), each loading K and V
+// straight into its matrix operands with two tiles in flight (the Tile
+// machinery of the decode path), so a workgroup keeps four times the bytes
+// in flight.  Row rho = i g + h (token i, query head h) is the matrix column
+// of lane c = rho; each lane masks past its own row's causal limit.  The
+// running maxima start at -FLT_MAX (finite): a wave whose first tiles lie
+// wholly past a row's limit then keeps that row's weights at exactly 0
+// instead of forming -inf - -inf.  The waves' (m, l, normalised rows) are
+// merged in LDS with weights l 2^(m - M) and written as the rows (one
+// partition) or as the partition's partials, in the main path's format.
+//   sq    LDS, 16 x (D + 8) 16-bit: the query tile, followed by the waves'
+//         m and l and their invalid-block flags
+//   srow  LDS, 4 x 16 x D floats: the waves' normalised rows
+template <int DT, int D, int W>
+__device__ __forceinline__ void short_rows(const PrefillArgs& a, int s, int kvh, int q0, int T, int L, int rows,
+                                           int step0, int nsteps, int part, char* sq_bytes, float* srow) {
+  using Tl = Tile<DT, D>;
+  constexpr int KS = Tl::KS, QROW = Tl::QROW, QCH = Tl::QCH, ROWB = Tl::ROWB;
+  using VVec = typename Tl::VVec;
+  constexpr int NW = W < 4 ? W : 4;  // wavefronts that take tiles
+  uint16_t(*sq)[QROW] = reinterpret_cast<uint16_t(*)[QROW]>(sq_bytes);
+  float(*sm)[16] = reinterpret_cast<float(*)[16]>(sq_bytes + 16 * QROW * 2);
+  float(*sl)[16] = sm + NW;
+  int* sbad = reinterpret_cast<int*>(sl + NW);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uni(tid >> 6);
+  const int grp = lane >> 4, col = lane & 15;
+  const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;
+  const int g = a.g;
+  const int base = L - T;
+
+  // Query rows 0..rows-1 (row rho: token rho / g, head kvh g + rho % g),
+  // zero past them.
+  for (int idx = tid; idx < 16 * QCH; idx += 64 * W) {
+    const int r = idx / QCH, ch = idx - r * QCH;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < rows)
+      v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.q) +
+                                          ((size_t)(q0 + r / g) * a.Hq + kvh * g + r % g) * ROWB + ch * 16);
+    *reinterpret_cast<uint4*>(&sq[r][ch * 8]) = v;
+  }
+  lds_barrier();
+
+  // This partition's positions [t_lo, t_hi) in 16-slot tiles [tb_lo, tb_hi).
+  const int lm = a.lbs - 4;
+  const int t_lo = step0 * kStep, t_hi = min(nsteps * kStep, L);
+  const int tb_lo = t_lo >> 4, ntile = ((t_hi + 15) >> 4) - tb_lo;
+  const int cnt = wave < NW && ntile > wave ? (ntile - wave + NW - 1) / NW : 0;
+  // Positions at or past lim are masked in this lane's column (its row's
+  // position + 1; padding columns copy the last row so they stay finite).
+  const int lim = base + min(col, rows - 1) / g + 1;
+  const float qsg = a.neg_scale ? -a.qscale : a.qscale;  // scale * log2(e)
+  const uint16_t* qsrc = &sq[col][grp * 8];
+  const int32_t* btrow = a.bt + (size_t)s * a.maxb;
+  float m_run = -__FLT_MAX__, l_run = 0.f;
+  f32x4 acc[Tl::DPL];
+#pragma unroll
+  for (int u = 0; u < Tl::DPL; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bool bad = false;
+  uint4 kA[KS], kB[KS];
+  VVec vA[4], vB[4];
+  for (int k0 = 0; k0 < cnt; k0 += 64) {  // table entries 64 tiles at a time
+    const int c = min(64, cnt - k0);
+    const int first = tb_lo + wave + k0 * NW;  // logical tile of this group's k = 0
+    bool badg;
+    const int myid = load_ids(btrow, c, a.num_blocks, [&](int k) { return first + k * NW; }, badg, a.Hkv, kvh, lm);
+    bad |= badg;
+    pipeline(
+        c, kA, vA, kB, vB,
+        [&](int k, uint4(&kr)[KS], VVec(&vr)[4]) {
+          const size_t off = (size_t)(unsigned)__builtin_amdgcn_readlane(myid, k) * (16 * ROWB);
+          Tl::load(a.kp + off, a.vp + off, grp, col, min(15, L - 1 - (first + k * NW) * 16), kr, vr);
+        },
+        [&](int k, const uint4(&kr)[KS], const VVec(&vr)[4], bool valid) {
+          asm volatile("" ::: "memory");
+          Tl::consume(kr, vr, qsrc, (first + k * NW) * 16 + grp * 4, valid ? lim : 0, qsg, x16, x32, m_run, l_run,
+                      acc);
+        });
+  }
+  // (each wave stages into its own slots, past the query tile: no barrier
+  // before, one before the merge reads them)
+  if (wave < NW) {
+    Tl::stage(m_run, l_run, acc, cnt > 0, grp, col, rows, x16, x32, sm[wave], sl[wave], srow + wave * 16 * D);
+    if (lane == 0) sbad[wave] = bad;
+  }
+  lds_barrier();
+  bool any_bad = false;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) any_bad |= sbad[w] != 0;
+  const float nan = __builtin_nanf("");
+  // One thread per (row, 4 dims): the merged row, then its store.
+  for (int idx = tid; idx < rows * (D / 4); idx += 64 * W) {
+    const int r = idx / (D / 4), d = (idx - r * (D / 4)) * 4;
+    float M = sm[0][r];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm[w][r]);
+    float den = 0.f, num[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float wt = sl[w][r] * fast_exp2(sm[w][r] - M);  // 0 for a wave without positions of this row
+      den += wt;
+      if (sl[w][r] > 0.f) {
+        const float4 o = *reinterpret_cast<const float4*>(srow + (w * 16 + r) * D + d);
+        num[0] = fmaf(wt, o.x, num[0]);
+        num[1] = fmaf(wt, o.y, num[1]);
+        num[2] = fmaf(wt, o.z, num[2]);
+        num[3] = fmaf(wt, o.w, num[3]);
+      }
+    }
+    if (a.P > 1 && base + r / g < t_lo) continue;  // the row does not reach this partition
+    const float inv = any_bad ? nan : 1.f / den;
+    const size_t row = (size_t)(q0 + r / g) * a.Hq + kvh * g + r % g;
+    if (a.P == 1) {
+      float f[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] = num[i] * inv;
+#pragma unroll
+      for (int i = 4; i < 8; ++i) f[i] = 0.f;
+      const uint4 v = pack16<DT>(f);
+      *reinterpret_cast<uint2*>(reinterpret_cast<char*>(a.out) + (row * D + d) * 2) = make_uint2(v.x, v.y);
+    } else {
+      const size_t e = row * a.P + part;
+      *reinterpret_cast<float4*>(a.ws_o + e * D + d) = make_float4(num[0] * inv, num[1] * inv, num[2] * inv,
+                                                                   num[3] * inv);
+      if (d == 0) {
+        a.ws_m[e] = any_bad ? nan : M;
+        a.ws_l[e] = den;
+      }
+    }
+  }
+}
+
 // kDma = false: K and V go through registers into LDS (V transposed into the
 // PV operand's k-slot order by the threads).  kDma = true: both go straight
 // from global memory into LDS in token-row order (global->LDS 16-byte loads,
@@ -399,6 +539,13 @@ __global__ __launch_bounds__(64 * W) void prefill_mfma(PrefillArgs a) {
   const int step0 = part * a.psteps;  // this partition's steps [step0, nsteps)
   const int nsteps = a.P > 1 ? min(nsteps_all, step0 + a.psteps) : nsteps_all;
   if (step0 >= nsteps) return;  // no row of the tile reaches this partition
+  if constexpr (kDma) {
+    if (rows <= 16 && a.lbs >= 4) {  // (whole-workgroup branch)
+      short_rows<DT, D, W>(a, s, kvh, q0, T, L, rows, step0, nsteps, part, reinterpret_cast<char*>(&sK[0][0][0]),
+                           reinterpret_cast<float*>(&sVn[0][0][0]));
+      return;
+    }
+  }
   const int rho_w0 = tile * R + wave * 16 * NC;
   const bool wave_on = rho_w0 < rows;
   const int lim_w_lo = base + min(rho_w0, rows - 1) / g;

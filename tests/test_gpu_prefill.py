@@ -410,3 +410,71 @@ def test_launch_covers_every_walk_every_row(monkeypatch, variant, case):
         out = to_f64(pa.prefill(g.q, g.k, g.v, g.tables, g.lens, g.qstart, w.scale, max_q, w.max_context_len),
                      dtype)
         _check(out, want, dtype, f"{case} {variant} max_query_len={max_q}")
+
+
+# Items whose rows fit one 16-row matrix column group (T * g <= 16) on blocks
+# of 16 or more slots run decode-shaped inside the prefill kernel (four
+# wavefronts deal the 16-slot tiles, K and V straight into the matrix
+# operands, per-row causal limits in the lane's column).  (prior, chunk,
+# Hq, Hkv, D, dtype, block size) per case; every row against the oracle.
+SHORT_ROW_CASES = {
+    # single tokens beside chunks, Llama-like heads
+    "singles_g4": ([0, 700, 33, 1500, 15, 4000, 64, 0], [300, 1, 1, 1, 1, 1, 1, 1], 32, 8, 128, "bf16", 16),
+    # T = 2 after 31 cached positions: the tile holding position 32 lies
+    # wholly past rows 0-3's limit, and it is the only tile of wave 2
+    "t2_tile_past_limit": ([31, 31, 95, 0], [2, 2, 2, 2], 8, 2, 128, "fp16", 16),
+    # g = 1: 16 rows exactly (this path) next to 17 (the matrix-tile path)
+    "rows_16_and_17": ([40, 200, 900, 3], [16, 17, 1, 5], 2, 2, 64, "bf16", 16),
+    # g = 8 (two tokens fill the column group), blocks of 32 and of 128 slots
+    "g8_bs32": ([100, 2000, 513, 7], [2, 1, 2, 1], 16, 2, 128, "fp16", 32),
+    "g4_bs128": ([129, 3000, 1, 700], [1, 3, 4, 1], 8, 2, 64, "bf16", 128),
+    # blocks of 8 slots keep the matrix-tile path
+    "singles_bs8": ([100, 300, 17, 0], [1, 1, 2, 1], 8, 2, 128, "bf16", 8),
+    # a context past 64 tiles per wavefront: table entries in two groups
+    "long_single": ([5200, 4200, 64], [1, 2, 1], 8, 2, 128, "bf16", 16),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SHORT_ROW_CASES))
+def test_short_row_items_every_row(case):
+    prior, chunk, Hq, Hkv, D, dtype, bs = SHORT_ROW_CASES[case]
+    w = make_prefill_custom(f"short_{case}", dtype, prior, chunk, Hq, Hkv, D, seed=500 + len(case), block_size=bs)
+    print(f"case short rows {case}", flush=True)
+    _full_parity(w)
+
+
+@pytest.mark.parametrize("variant", ["dma", "w8"])
+@pytest.mark.parametrize("psize", [64, 512])
+def test_short_row_items_split_every_row(monkeypatch, variant, psize):
+    """Decode-shaped items in a split launch write partials in the main
+    path's format (normalised rows, base-2 max, sum) for the rows that reach
+    the partition; the merge reads them beside the chunks' partials."""
+    monkeypatch.setenv("PA_PREFILL_KERNEL", variant)
+    w = make_prefill_custom(f"short_split{psize}", "bf16", [2100, 0, 1337, 64, 700], [1, 300, 2, 1, 4], 16, 4, 128,
+                            seed=610 + psize)
+    print(f"case short rows split {psize} {variant}", flush=True)
+    g = GpuPrefillStep(w)
+    out = to_f64(g.run(partition_size=psize), w.dtype)
+    st, k, v = oracle_prefill_pools(w)
+    want = oracle.prefill(w.q, k, v, st.tables, w.context_lens, w.query_start, w.scale, w.dtype)
+    _check(out, want, w.dtype, f"short split {psize} {variant}")
+
+
+def test_short_row_item_with_bad_block_id_gives_nan_rows():
+    """An out-of-range block id in a decode-shaped item's table is never
+    dereferenced: that item's rows become NaN, the others are computed."""
+    import paged_kv_cache_117_amd as pa
+
+    w = make_prefill_custom("short_bad", "bf16", [300, 90, 500], [1, 1, 200], 8, 2, 128, seed=620)
+    print("case short rows bad block id", flush=True)
+    g = GpuPrefillStep(w)
+    g.write()
+    tables = g.tables.clone()
+    tables[0, 5] = w.num_blocks + 7
+    out = to_f64(pa.prefill(g.q, g.k, g.v, tables, g.lens, g.qstart, w.scale, w.max_query_len,
+                            w.max_context_len), w.dtype)
+    st, k, v = oracle_prefill_pools(w)
+    want = oracle.prefill(w.q, k, v, st.tables, w.context_lens, w.query_start, w.scale, w.dtype)
+    qs = w.query_start
+    assert np.isnan(out[qs[0]:qs[1]]).all()
+    _check(out[qs[1]:], want[qs[1]:], w.dtype, "short bad id: the other sequences")
