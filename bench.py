@@ -34,8 +34,11 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
 # Sources that define the decode kernels; a traffic record is valid only for these bytes.
+# What the decode kernels are built from: their sources and the headers they
+# include (the compile flags are hashed beside them, see kernel_fingerprint)
 KERNEL_SOURCES = ["paged_kv_cache_117_amd/csrc/decode_mfma.hip", "paged_kv_cache_117_amd/csrc/decode.hip",
-                  "paged_kv_cache_117_amd/csrc/decode_api.hip", "paged_kv_cache_117_amd/build_lib.py"]
+                  "paged_kv_cache_117_amd/csrc/decode_api.hip", "paged_kv_cache_117_amd/csrc/decode_tile.h",
+                  "paged_kv_cache_117_amd/csrc/decode_kernels.h", "paged_kv_cache_117_amd/csrc/pa_device.h"]
 METRIC = "paged decode attention KV-read GB/s (% of MI355X HBM peak); seq-steps/s"
 WARMUP_SECONDS = 0.2  # default warmup: GPU work before timing, for settled clocks
 # Layers of the models the decode workloads are shaped after (one layer is benchmarked); used only
@@ -127,10 +130,15 @@ def parse():
 
 
 def kernel_fingerprint():
+    """Hash of the decode kernels' sources and the HIP compile flags: a counter
+    record taken with other sources or flags no longer describes the kernel."""
+    from paged_kv_cache_117_amd import build_lib
+
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    h.update(" ".join(build_lib.HIP_FLAGS).encode())
     return h.hexdigest()[:16]
 
 
