@@ -78,6 +78,7 @@ PREFILL_NAMES = {
           "Hq=64, Hkv=8, D=128, block 16)",
     "p3": "mixed chunked-prefill step bf16, Llama shapes (4 chunks of 512 + 60 single tokens)",
     "p4": "prefix-cache continuation bf16, Llama shapes (4 seqs x 64 new tokens after U[24576,32704] cached)",
+    "p5": "mixed step with a long chunk bf16, Llama shapes (one 4096-token chunk + 127 single tokens after U[127,4095])",
 }
 
 

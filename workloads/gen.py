@@ -327,6 +327,8 @@ PREFILL_CONFIGS = {
     "p2": "Qwen2.5-72B layer, fp16: 4 seqs x 1024-token chunks, prior context U[0,7168], Hq=64, Hkv=8, D=128",
     "p3": "mixed step, Llama shapes, bf16: 4 chunks of 512 (prior U[0,3584]) + 60 single tokens (prior U[127,4095])",
     "p4": "prefix-cache continuation, Llama shapes, bf16: 4 seqs x 64 new tokens after U[24576,32704] cached",
+    "p5": "mixed step with a long chunk, Llama shapes, bf16: one 4096-token chunk (no prior) + 127 single tokens "
+          "(prior U[127,4095])",
 }
 
 
@@ -393,4 +395,9 @@ def make_prefill_workload(key: str, block_size: int = BLOCK_SIZE) -> PrefillWork
         return make_prefill_custom(
             "p4", "bf16", lambda r: (r.integers(24576, 32704, size=4, endpoint=True), np.full(4, 64)),
             None, 32, 8, 128, seed=14)
+    if key == "p5":
+        def lens5(r):
+            pri = np.concatenate([[0], r.integers(127, 4095, size=127, endpoint=True)])
+            return pri, np.concatenate([[4096], np.ones(127, np.int64)])
+        return make_prefill_custom("p5", "bf16", lens5, None, 32, 8, 128, seed=15)
     raise KeyError(key)
