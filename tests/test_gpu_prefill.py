@@ -109,7 +109,8 @@ def test_deterministic_and_placement_invariant():
     logical positions)."""
     import torch
 
-    w = make_prefill_custom("pl", "bf16", [40, 0, 77], [90, 33, 5], 8, 2, 128, seed=5)
+    # (the last two sequences have 4 and 12 rows: decode-shaped items)
+    w = make_prefill_custom("pl", "bf16", [40, 0, 77, 500, 61], [90, 33, 5, 1, 3], 8, 2, 128, seed=5)
     g = GpuPrefillStep(w)
     a = g.run().clone()
     b = g.attend().clone()
@@ -144,7 +145,8 @@ def test_single_token_chunks_match_decode_within_tolerance():
 
 @pytest.mark.parametrize("scale", [0.0, -0.0883883461356163, 0.5])
 def test_scales(scale):
-    w = make_prefill_custom("sc", "fp16", [10, 50], [40, 70], 8, 2, 64, seed=11)
+    # chunks of 40 and 70 tokens (matrix tiles) and of 1 and 3 (decode-shaped items)
+    w = make_prefill_custom("sc", "fp16", [10, 50, 300, 17], [40, 70, 1, 3], 8, 2, 64, seed=11)
     w.scale = float(np.float32(scale))
     _full_parity(w)
 
