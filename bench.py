@@ -139,7 +139,17 @@ def kernel_fingerprint():
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
-    h.update(" ".join(build_lib.HIP_FLAGS).encode())
+    # the flags without the include directories, whose absolute paths depend
+    # on where the checkout lives
+    flags, skip = [], False
+    for f in build_lib.HIP_FLAGS:
+        if skip:
+            skip = False
+        elif f == "-I":
+            skip = True
+        else:
+            flags.append(f)
+    h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 
