@@ -41,6 +41,10 @@ KERNEL_SOURCES = ["paged_kv_cache_117_amd/csrc/decode_mfma.hip", "paged_kv_cache
                   "paged_kv_cache_117_amd/csrc/decode_kernels.h", "paged_kv_cache_117_amd/csrc/pa_device.h"]
 METRIC = "paged decode attention KV-read GB/s (% of MI355X HBM peak); seq-steps/s"
 WARMUP_SECONDS = 0.2  # default warmup: GPU work before timing, for settled clocks
+# Calls in each measurement pass after the timed region (the call alone, the
+# unfused step, the main kernel alone): at least this many, whatever --steps
+# says, so that a short timed region still gets stable per-call figures.
+PASS_MIN_CALLS = 100
 # Layers of the models the decode workloads are shaped after (one layer is benchmarked); used only
 # to state the model's KV bytes per token next to the pages' sizing example.
 MODEL_LAYERS = {"c2": 32, "c3": 40, "c4": 32, "c4b": 32, "c5": 80}
@@ -612,7 +616,8 @@ def prefill_bench(torch, key, args, steps, warmup, cpu_budget, pf_psize):
             ev[1].record(stream)
 
     warmup = warm_up(torch, lambda i: step(i % R), warmup)
-    evs, kevs = timing_events(torch, steps, stream)
+    npass = max(steps, PASS_MIN_CALLS)  # the passes after the timed region
+    evs, kevs = timing_events(torch, npass, stream)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -624,9 +629,9 @@ def prefill_bench(torch, key, args, steps, warmup, cpu_budget, pf_psize):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / steps
-    pf_ms = call_pass(torch, step, steps, R, evs)
+    pf_ms = call_pass(torch, step, npass, R, evs)
     pf_avg = float(pf_ms.mean())
-    kern_avg = main_kernel_pass(torch, step, steps, R, kevs)
+    kern_avg = main_kernel_pass(torch, step, npass, R, kevs)
     flops = metrics.prefill_flops(w.prior_lens, w.chunk_lens, w.num_q_heads, w.head_dim)
     io = metrics.prefill_io_bytes(w.prior_lens, w.chunk_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, eb)
     peak = MFMA_PEAK_TFLOPS[w.dtype]
@@ -934,7 +939,8 @@ def decode_bench(torch, key, args, partition_size, steps, warmup, cpu_budget):
         decode_only(r)
 
     warmup = warm_up(torch, lambda i: step(i % R), warmup)
-    _, kevs = timing_events(torch, steps, stream)
+    npass = max(steps, PASS_MIN_CALLS)  # the passes after the timed region
+    _, kevs = timing_events(torch, npass, stream)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -949,10 +955,10 @@ def decode_bench(torch, key, args, partition_size, steps, warmup, cpu_budget):
     ms_step = total_ms / steps
     # passes of their own after the timed region (same sets): the library
     # calls back to back, the unfused step, the main kernel alone
-    call_ms = block_pass(torch, call, steps, R, stream)
-    decode_only_ms = block_pass(torch, decode_only, steps, R, stream)
-    ms_step_unfused = block_pass(torch, step_unfused, steps, R, stream)
-    kern_avg = main_kernel_pass(torch, step, steps, R, kevs)
+    call_ms = block_pass(torch, call, npass, R, stream)
+    decode_only_ms = block_pass(torch, decode_only, npass, R, stream)
+    ms_step_unfused = block_pass(torch, step_unfused, npass, R, stream)
+    kern_avg = main_kernel_pass(torch, step, npass, R, kevs)
 
     kv_bytes = metrics.decode_kv_bytes(w.context_lens, w.num_kv_heads, w.head_dim, eb)
     unique_kv_bytes = metrics.decode_unique_kv_bytes(tables, w.context_lens, w.num_kv_heads, w.head_dim, eb,
