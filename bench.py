@@ -385,11 +385,31 @@ def timing_events(torch, n, stream):
     return evs, kevs
 
 
+def settle_clocks(torch, seconds=0.1, nbytes=1 << 28):
+    """Device copies for `seconds` of GPU time right before the warm-up
+    steps.  The workload's host-side set-up leaves the GPU idle for a second
+    or more, and its clocks drop; they rise again over the first tens of
+    milliseconds of load, so a short explicit --warmup would time part of
+    that ramp.  Not a step: the warm-up and timed steps are counted as given."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            break
+    del src, dst
+
+
 def warm_up(torch, step, n=None):
     """Untimed steps before the timed region: exactly `n` when given, else at
     least 10 and at least WARMUP_SECONDS of GPU work (the GPU raises its
     clocks over the first tens of milliseconds of sustained load; a short
-    warmup times part of that ramp).  Returns the number of steps run."""
+    warmup times part of that ramp).  Returns the number of steps run.
+    Either way the clocks are first settled by a pass of device copies."""
+    settle_clocks(torch)
     i = 0
     if n is not None:
         for i in range(n):
