@@ -302,8 +302,9 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t l
 // instead: the first four wavefronts deal the partition's 16-slot tiles
 // round-robin (wave w takes tiles w, w + 4, ...), each loading K and V
 // straight into its matrix operands with two tiles in flight (the Tile
-// machinery of the decode path), so a workgroup keeps four times the bytes
-// in flight.  Row rho = i g + h (token i, query head h) is the matrix column
+// machinery of the decode path): 64 KiB of K/V in flight per workgroup
+// (4 wavefronts x 2 tiles x 8 KiB at D = 128) against the LDS path's one
+// 32 KiB step.  Row rho = i g + h (token i, query head h) is the matrix column
 // of lane c = rho; each lane masks past its own row's causal limit.  The
 // running maxima start at -FLT_MAX (finite): a wave whose first tiles lie
 // wholly past a row's limit then keeps that row's weights at exactly 0
@@ -344,7 +345,7 @@ __device__ __forceinline__ void short_rows(const PrefillArgs& a, int s, int kvh,
   }
   lds_barrier();
 
-  // This partition's positions [t_lo, t_hi) in 16-slot tiles [tb_lo, tb_hi).
+  // This partition's positions [t_lo, t_hi): 16-slot tiles tb_lo .. tb_lo + ntile - 1.
   const int lm = a.lbs - 4;
   const int t_lo = step0 * kStep, t_hi = min(nsteps * kStep, L);
   const int tb_lo = t_lo >> 4, ntile = ((t_hi + 15) >> 4) - tb_lo;
