@@ -47,7 +47,7 @@ WARMUP_SECONDS = 0.2  # default warmup: GPU work before timing, for settled cloc
 PASS_MIN_CALLS = 100
 # Layers of the models the decode workloads are shaped after (one layer is benchmarked); used only
 # to state the model's KV bytes per token next to the pages' sizing example.
-MODEL_LAYERS = {"c2": 32, "c3": 40, "c4": 32, "c4b": 32, "c5": 80}
+MODEL_LAYERS = {"c2": 32, "c3": 40, "c4": 32, "c4b": 32, "c5": 80, "c5tp8": 80}
 # Figures the source pages report, with the hardware they were measured on: context, not targets.
 PAGES_CONTEXT = {
     "kv_memory_holding_tokens": "20.4-38.2% in the contiguous-slab servers profiled by the SOSP 2023 "
@@ -61,7 +61,7 @@ PAGES_CONTEXT = {
                                  "the 26 GB of weights (PagedAttention: Virtual Memory for the KV Cache)",
 }
 # partition size a workload states (positions per partition); others use the automatic split
-WORKLOAD_PARTITION = {"c5": 512}
+WORKLOAD_PARTITION = {"c5": 512}  # (c5tp8: the automatic split; its partitions would be too few to balance)
 WORKLOAD_NAMES = {
     "c1": "tiny paged decode fp32 (4 seqs, L in {1,5,16,37}, Hq=Hkv=2, D=64)",
     "c2": "Llama-3.1-8B decode layer bf16 (B=64, Hq=32, Hkv=8, D=128, L~U[128,4096], block 16)",
@@ -69,6 +69,8 @@ WORKLOAD_NAMES = {
     "c4": "parallel-sampling prefix share bf16 (32 prompts x 8 samples, prefix 1024, tails U[0,512])",
     "c4b": "fork step bf16 (32 prompts x 8 samples, prefix 1000, copy-on-write of the partial block)",
     "c5": "Qwen2.5-72B decode layer fp16 (B=128, Hq=64, Hkv=8, D=128, L~U[4096,8192], 512-token partitions)",
+    "c5tp8": "one GPU's share of the Qwen2.5-72B decode layer at tensor parallel degree 8 fp16 (B=128, Hq=8, "
+             "Hkv=1, D=128, C5's lengths, automatic split)",
 }
 
 

@@ -90,8 +90,9 @@ def test_group_of_8_at_512_position_partitions(dtype, D):
 # launch configuration the benchmark times: the automatic split, and for the
 # Qwen2.5-72B layer also the 512-position partitions its configuration states
 # (each sequence of 4096-8192 positions spans 8-16 partitions, merged by the
-# log-sum-exp reduce).
-@pytest.mark.parametrize("key,psize", [("c2", 0), ("c3", 0), ("c5", 0), ("c5", 512)])
+# log-sum-exp reduce).  c5tp8 is one GPU's tensor-parallel share of that
+# layer (its one KV head and eight query heads) at the same lengths.
+@pytest.mark.parametrize("key,psize", [("c2", 0), ("c3", 0), ("c5", 0), ("c5", 512), ("c5tp8", 512), ("c5tp8", 0)])
 def test_full_size_all_rows(key, psize):
     w = make_workload(key)
     check(w, partition_size=psize)

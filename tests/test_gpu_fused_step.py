@@ -58,7 +58,7 @@ def check(w, partition_size=0, oracle_rows=None):
 
 
 @pytest.mark.parametrize("key,psize", [("c1", 0), ("c2", 0), ("c3", 0), ("c5", 512), ("c5", 0), ("c4", 0),
-                                       ("c4b", 0)])
+                                       ("c4b", 0), ("c5tp8", 0)])
 def test_full_size_configs(key, psize):
     """(c3 and c5 exceed the fused kernel's size bound: their write runs as a
     launch of its own; the g = 8, 512-position kernel is covered below.)"""

@@ -131,6 +131,8 @@ CONFIGS = {
     "c4": "prefix share, Llama shapes, bf16: 32 prompts x 8 samples, prefix 1024, tails U[0,512]",
     "c4b": "fork step, Llama shapes, bf16: 32 prompts x 8 samples, prefix 1000, first token after fork",
     "c5": "Qwen2.5-72B layer, fp16: B=128, Hq=64, Hkv=8, D=128, L~U[4096,8192], 512-token partitions",
+    "c5tp8": "one GPU's share of the Qwen2.5-72B layer at tensor parallel degree 8 (its KV head and 8 query "
+             "heads): C5's sequences and lengths with Hq=8, Hkv=1",
 }
 
 
@@ -254,6 +256,13 @@ def make_workload(key: str, block_size: int = BLOCK_SIZE) -> Workload:
         return make_custom(
             "c5", "fp16", lambda r: r.integers(4096, 8192, size=128, endpoint=True),
             64, 8, 128, seed=5, partition_size=512)
+    if key == "c5tp8":
+        # the same length draw as c5 (same seed and stream): one KV head's
+        # share, with the automatic split -- at one KV head C5's 512-position
+        # partitions are only 1.5 per wavefront, too coarse to balance
+        return make_custom(
+            "c5tp8", "fp16", lambda r: r.integers(4096, 8192, size=128, endpoint=True),
+            8, 1, 128, seed=5)
     raise KeyError(key)
 
 
