@@ -3,9 +3,9 @@
 Every case runs the whole step through the library -- block manager,
 pa_write_kv of the chunk, pa_prefill -- on pools whose unused elements are
 NaN, and compares with the oracle's float64 result element by element.
-Small cases are checked on every row; the full-size workloads on sampled
-rows (first, last and random rows of every sequence), which the oracle
-computes one at a time.
+Small cases are checked on every row, and so are the full-size P3, P4 and
+P5 steps; P1 and P2 on sampled rows (first, last and random rows of every
+sequence), which the oracle computes one at a time.
 """
 
 import numpy as np
@@ -480,3 +480,14 @@ def test_short_row_item_with_bad_block_id_gives_nan_rows():
     qs = w.query_start
     assert np.isnan(out[qs[0]:qs[1]]).all()
     _check(out[qs[1]:], want[qs[1]:], w.dtype, "short bad id: the other sequences")
+
+
+@pytest.mark.parametrize("key", ["p3", "p4", "p5"])
+def test_full_size_every_row(key):
+    """Every row of the mixed steps (P3, P5: decode-shaped single tokens beside
+    chunks, the walk-sized grid) and of the long continuation (P4: split walks
+    merged by the reduce) against the oracle; P1 and P2 are checked on sampled
+    rows above (the oracle needs minutes for all of theirs)."""
+    w = make_prefill_workload(key)
+    print(f"case {key} every row", flush=True)
+    _full_parity(w)
