@@ -678,6 +678,21 @@ def prefill_bench(torch, key, args, steps, warmup, cpu_budget, pf_psize):
     peak = MFMA_PEAK_TFLOPS[w.dtype]
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (kern_avg * 1e-3) / 1e12
+    # The roofline's bound is the larger of the two lower bounds on time: the
+    # flops at the matrix peak and the algorithmic bytes at the HBM peak.  A
+    # step whose arithmetic intensity (flops per byte) is below the ridge point
+    # peak_flops / peak_bytes (312 for 16-bit MFMA at 8 TB/s) -- a mixed step
+    # whose single-token rows stream most of the bytes, or a long continuation
+    # -- is bound by HBM, however much of its time is spent on the matrix cores.
+    t_mfma = flops / (peak * 1e12)
+    t_hbm = io / (HBM_PEAK_GBPS * 1e9)
+    kern_gbps = io / (kern_avg * 1e-3) / 1e9
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(kern_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(kern_gbps / HBM_PEAK_GBPS, 4)}
     res = {
         "metric": PREFILL_METRIC,
         "value": round(value, 2),
@@ -717,12 +732,12 @@ def prefill_bench(torch, key, args, steps, warmup, cpu_budget, pf_psize):
         "wall_s": round(wall, 3),
         "roofline": {
             "kernel": "pa_prefill main kernel (prefill_mfma)",
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
+            **roof,
             "traffic": None,
+            "arithmetic_intensity": round(flops / io, 1),
+            "ridge": round(peak * 1e12 / (HBM_PEAK_GBPS * 1e9), 1),
+            "mfma_frac": round(achieved / peak, 4),
+            "hbm_frac": round(kern_gbps / HBM_PEAK_GBPS, 4),
         },
         "cpu_baseline": None,
     }
