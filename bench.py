@@ -421,6 +421,29 @@ class LeadIn:
             self.dst.copy_(self.src)
 
 
+def roofline_bound(flops, nbytes, ms, peak_tflops, peak_gbps=HBM_PEAK_GBPS):
+    """Roofline record of a launch of `flops` algorithmic flops and `nbytes`
+    algorithmic bytes that took `ms`.  The bound is the larger of the two lower
+    bounds on its time, the flops at the matrix peak and the bytes at the HBM
+    peak: a launch whose arithmetic intensity (flops per byte) is below the
+    ridge point peak_flops / peak_bytes (312 for 16-bit MFMA at 8 TB/s) -- a
+    mixed step whose single-token rows stream most of the bytes, or a long
+    continuation -- is bound by HBM, however much of its time the matrix cores
+    take.  Both fractions are kept."""
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    if flops / (peak_tflops * 1e12) >= nbytes / (peak_gbps * 1e9):
+        rec = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak_tflops, "unit": "TFLOP/s",
+               "frac": round(tflops / peak_tflops, 4)}
+    else:
+        rec = {"bound": "hbm", "achieved": round(gbps, 1), "peak": peak_gbps, "unit": "GB/s",
+               "frac": round(gbps / peak_gbps, 4)}
+    rec.update({"arithmetic_intensity": round(flops / nbytes, 1),
+                "ridge": round(peak_tflops * 1e12 / (peak_gbps * 1e9), 1),
+                "mfma_frac": round(tflops / peak_tflops, 4), "hbm_frac": round(gbps / peak_gbps, 4)})
+    return rec
+
+
 def warm_up(torch, step, n=None):
     """Untimed steps before the timed region: exactly `n` when given, else at
     least 10 and at least WARMUP_SECONDS of GPU work (the GPU raises its
@@ -677,22 +700,7 @@ def prefill_bench(torch, key, args, steps, warmup, cpu_budget, pf_psize):
     io = metrics.prefill_io_bytes(w.prior_lens, w.chunk_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, eb)
     peak = MFMA_PEAK_TFLOPS[w.dtype]
     value = flops / (ms_step * 1e-3) / 1e12
-    achieved = flops / (kern_avg * 1e-3) / 1e12
-    # The roofline's bound is the larger of the two lower bounds on time: the
-    # flops at the matrix peak and the algorithmic bytes at the HBM peak.  A
-    # step whose arithmetic intensity (flops per byte) is below the ridge point
-    # peak_flops / peak_bytes (312 for 16-bit MFMA at 8 TB/s) -- a mixed step
-    # whose single-token rows stream most of the bytes, or a long continuation
-    # -- is bound by HBM, however much of its time is spent on the matrix cores.
-    t_mfma = flops / (peak * 1e12)
-    t_hbm = io / (HBM_PEAK_GBPS * 1e9)
-    kern_gbps = io / (kern_avg * 1e-3) / 1e9
-    if t_mfma >= t_hbm:
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4)}
-    else:
-        roof = {"bound": "hbm", "achieved": round(kern_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(kern_gbps / HBM_PEAK_GBPS, 4)}
+    roof = roofline_bound(flops, io, kern_avg, peak)
     res = {
         "metric": PREFILL_METRIC,
         "value": round(value, 2),
@@ -730,15 +738,7 @@ def prefill_bench(torch, key, args, steps, warmup, cpu_budget, pf_psize):
         "host_block_manager_ms": round(host_bm_ms, 3),
         **kv_util,
         "wall_s": round(wall, 3),
-        "roofline": {
-            "kernel": "pa_prefill main kernel (prefill_mfma)",
-            **roof,
-            "traffic": None,
-            "arithmetic_intensity": round(flops / io, 1),
-            "ridge": round(peak * 1e12 / (HBM_PEAK_GBPS * 1e9), 1),
-            "mfma_frac": round(achieved / peak, 4),
-            "hbm_frac": round(kern_gbps / HBM_PEAK_GBPS, 4),
-        },
+        "roofline": {"kernel": "pa_prefill main kernel (prefill_mfma)", **roof, "traffic": None},
         "cpu_baseline": None,
     }
     if cpu_budget > 0:

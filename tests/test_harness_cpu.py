@@ -50,3 +50,30 @@ def test_bench_kv_utilization_counts_shared_blocks_once():
     u = bench.kv_utilization(bm, [0, 1], tables, 16, 8)
     assert u["kv_blocks_in_use_frac"] == 3 / 8
     assert u["kv_slot_utilization"] == round((16 + 4 + 5) / 48, 4)
+
+
+def test_roofline_bound_follows_the_ridge_point():
+    """The prefill record's bound is the larger lower bound on time: flops at
+    2,500 TFLOP/s or bytes at 8,000 GB/s (ridge 312.5 flops per byte).  A
+    matrix-heavy launch (1,000 flops per byte) reports TFLOP/s against the
+    matrix peak, one below the ridge (100 flops per byte) GB/s against HBM,
+    and both fractions come out of the same time."""
+    import os
+    import sys
+
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+
+    # 1e12 flops over 1e9 bytes in 1 ms: 1,000 TFLOP/s and 1,000 GB/s
+    r = bench.roofline_bound(1e12, 1e9, 1.0, 2500.0)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
+    assert r["achieved"] == 1000.0 and r["frac"] == 0.4
+    assert r["mfma_frac"] == 0.4 and r["hbm_frac"] == 0.125
+    assert r["arithmetic_intensity"] == 1000.0 and r["ridge"] == 312.5
+    # 1e11 flops over 1e9 bytes in 0.25 ms: 400 TFLOP/s and 4,000 GB/s
+    r = bench.roofline_bound(1e11, 1e9, 0.25, 2500.0)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert r["achieved"] == 4000.0 and r["frac"] == 0.5
+    assert r["mfma_frac"] == 0.16 and r["hbm_frac"] == 0.5
+    # exactly at the ridge the matrix bound is taken
+    assert bench.roofline_bound(312.5e9, 1e9, 1.0, 2500.0)["bound"] == "mfma"
