@@ -121,7 +121,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--placement", choices=["shuffled", "sequential"], default="shuffled")
     ap.add_argument("--block-size", type=int, default=16,
-                    help="slots per KV block for the decode workloads (16, 32, 64, 128)")
+                    help="slots per KV block for the decode workloads (8, 16, 32, 64, 128; 8 runs pa_decode through the prefill kernel)")
     ap.add_argument("--decode-kernel", choices=["auto", "valu", "partition"], default="auto",
                     help="pa_decode kernel override (PA_DECODE_KERNEL): valu = vector-ALU kernel for 16-bit KV "
                          "too, partition = matrix-core partition kernels instead of the even split")
@@ -289,7 +289,7 @@ def write_fused_in_kernel(w):
     kernel override); otherwise a launch of its own writes first."""
     eb = {"fp32": 4, "fp16": 2, "bf16": 2}[w.dtype]
     bound = w.num_seqs * w.max_context_len * w.num_kv_heads * w.head_dim * eb * 2
-    return (w.dtype != "fp32" and w.num_seqs <= 4096 and bound <= FUSE_MAX_KV_BYTES
+    return (w.dtype != "fp32" and w.num_seqs <= 4096 and bound <= FUSE_MAX_KV_BYTES and w.block_size >= 16
             and os.environ.get("PA_DECODE_KERNEL", "") in ("", "auto"))
 
 
@@ -1075,7 +1075,7 @@ def decode_bench(torch, key, args, partition_size, steps, warmup, cpu_budget):
                                      if key in MODEL_LAYERS else None),
         "wall_s": round(wall, 3),
         "roofline": {
-            "kernel": "pa_write_kv_decode main kernel (%s)" % main_kernel_label(w.dtype, w.num_seqs),
+            "kernel": "pa_write_kv_decode main kernel (%s)" % main_kernel_label(w.dtype, w.num_seqs, w.block_size),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
@@ -1101,8 +1101,10 @@ def decode_bench(torch, key, args, partition_size, steps, warmup, cpu_budget):
     return res
 
 
-def main_kernel_label(dtype, num_seqs):
+def main_kernel_label(dtype, num_seqs, block_size=16):
     kern = os.environ.get("PA_DECODE_KERNEL", "")
+    if block_size == 8:
+        return "prefill_mfma over one query row per sequence (blocks of 8 slots), matrix cores"
     if dtype == "fp32" or kern == "valu":
         return "decode_part_valu, vector ALU"
     if kern == "partition" or num_seqs > 4096:

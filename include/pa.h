@@ -106,7 +106,10 @@ typedef enum {
  *                    contents need no initialisation and are clobbered
  *   stream           hipStream_t or NULL
  * Supported: block_size 16, 32, 64 or 128 (the kernels walk 16-slot tiles,
- * 2^k of them per block; 8 returns PA_ERR_UNSUPPORTED), head_dim 64 or 128,
+ * 2^k of them per block) and, for fp16/bf16 KV, 8: blocks of 8 slots run
+ * through pa_prefill's kernel with one query row per sequence (its
+ * workspace then fits in pa_decode_workspace_bytes; fp32 KV with 8 returns
+ * PA_ERR_UNSUPPORTED); head_dim 64 or 128,
  * any num_q_heads that is a multiple of num_kv_heads.  `out` must not alias
  * any input or the workspace.
  *

@@ -11,6 +11,7 @@
 
 #include "decode_kernels.h"
 #include "pa_internal.h"
+#include "prefill_kernels.h"
 
 namespace {
 
@@ -67,6 +68,10 @@ extern "C" size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int n
     const size_t st = pa::stream_layout(num_seqs, num_q_heads, num_kv_heads, head_dim).total;
     if (st > need) need = st;
   }
+  // (blocks of 8 slots: the prefill kernel's split; never more than the above)
+  const size_t rows8 =
+      pa::decode_rows_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size);
+  if (rows8 > need) need = rows8;
   return need;
 }
 
@@ -123,11 +128,17 @@ pa_status_t decode_impl(const char* who, void* out, const void* q, const void* k
   clear_error();
   if (dtype != PA_FP32 && dtype != PA_FP16 && dtype != PA_BF16)
     return fail(PA_ERR_UNSUPPORTED, "%s: unknown dtype %d", who, (int)dtype);
-  // The kernels walk 16-slot tiles (one MFMA operand); a block holds 2^lm of them.
+  // The kernels walk 16-slot tiles (one MFMA operand); a block holds 2^lm of
+  // them.  Blocks of 8 slots go through the prefill kernel, which walks
+  // token rows (16-bit KV).
   int lm = -1;
   for (int k = 0; k <= 3; ++k)
     if (block_size == 16 << k) lm = k;
-  if (lm < 0) return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (16, 32, 64 or 128)", who, block_size);
+  const bool rows8 = block_size == 8;
+  if (lm < 0 && !rows8)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (8, 16, 32, 64 or 128)", who, block_size);
+  if (rows8 && dtype == PA_FP32)
+    return fail(PA_ERR_UNSUPPORTED, "%s: fp32 KV takes block_size 16, 32, 64 or 128 (got 8)", who);
   if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128)", who, head_dim);
   if (num_seqs < 0 || num_seqs > 65535)
     return fail(PA_ERR_SHAPE, "%s: num_seqs %d outside [0, 65535]", who, num_seqs);
@@ -143,7 +154,8 @@ pa_status_t decode_impl(const char* who, void* out, const void* q, const void* k
   if (psize <= 0 || psize % 16 != 0)
     return fail(PA_ERR_SHAPE, "%s: partition_size %d must be a positive multiple of 16", who, partition_size);
   if (!isfinite(scale)) return fail(PA_ERR_SHAPE, "%s: scale is not finite", who);
-  if (((int64_t)num_blocks * num_kv_heads << lm) > 0x7fffffffLL)
+  if (rows8 ? (int64_t)num_kv_heads * head_dim * block_size * 4 > 0xffffffffLL
+            : ((int64_t)num_blocks * num_kv_heads << lm) > 0x7fffffffLL)
     return fail(PA_ERR_SHAPE, "%s: %d blocks of %d KV heads is too large", who, num_blocks, num_kv_heads);
   if (num_seqs == 0) return PA_OK;
   const bool fused = k_new != nullptr || v_new != nullptr;
@@ -152,6 +164,35 @@ pa_status_t decode_impl(const char* who, void* out, const void* q, const void* k
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
       (fused && (!aligned(k_new, 16) || !aligned(v_new, 16))))
     return fail(PA_ERR_SHAPE, "%s: out, q, the pools and the new rows must be 16-byte aligned", who);
+
+  if (rows8) {
+    // workspace first (nothing is launched when it is refused), then the
+    // write of a fused step, then the attention
+    const size_t need =
+        decode_rows_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size);
+    if (use_scratch && need > 0) {
+      if (need > kScratchBytes)
+        return fail(PA_ERR_WORKSPACE, "%s: these sizes need %zu bytes of scratch, more than its %zu", who, need,
+                    kScratchBytes);
+      pa_status_t sst = PA_OK;
+      workspace = scratch_ptr(&sst);
+      if (!workspace) return sst;
+      workspace_bytes = kScratchBytes;
+    }
+    if (need > 0) {
+      if (!workspace) return fail(PA_ERR_WORKSPACE, "%s: needs %zu bytes of workspace, got NULL", who, need);
+      if (workspace_bytes < need)
+        return fail(PA_ERR_WORKSPACE, "%s: needs %zu bytes of workspace, got %zu", who, need, workspace_bytes);
+      if (!aligned(workspace, 256)) return fail(PA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", who);
+    }
+    if (fused)
+      launch_write_last(const_cast<void*>(k_pool), const_cast<void*>(v_pool), k_new, v_new, block_tables,
+                        context_lens, num_seqs, max_blocks_per_seq, max_context_len, num_kv_heads, head_dim, 2, 3,
+                        num_blocks, static_cast<hipStream_t>(stream));
+    return decode_rows(who, out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                       head_dim, 3, num_blocks, max_blocks_per_seq, max_context_len, partition_size, scale, dtype,
+                       workspace, workspace_bytes, stream);
+  }
 
   const int P = parts_for(max_context_len, psize);
   const int g = num_q_heads / num_kv_heads;

@@ -116,6 +116,18 @@ __device__ __forceinline__ float max_groups(float x, int x16, int x32) {
 // writes their NaN rows.
 // (kLptPerLane items per lane: the in-kernel order covers up to 256 items per XCD)
 
+// Sequence s's query rows [q0, q1): query_start's entries, or with no
+// query_start one row per sequence (row s), the decode layout.
+__device__ __forceinline__ void seq_range(const PrefillArgs& a, int s, int& q0, int& q1) {
+  if (a.qs) {
+    q0 = a.qs[s];
+    q1 = a.qs[s + 1];
+  } else {
+    q0 = s;
+    q1 = s + 1;
+  }
+}
+
 struct LptItem {
   int ntiles = 0;  // row tiles of a servable item
   int base = 0;    // cached positions before the chunk
@@ -184,7 +196,9 @@ __device__ bool lpt_pick(const PrefillArgs& a, int xcd, int k, int per_xcd, int 
     const int item = j * 8 + xcd;
     if (item >= items) continue;
     const int s = item / a.Hkv;
-    const int q0 = a.qs[s], q1 = a.qs[s + 1], L = a.cl[s];
+    int q0, q1;
+    seq_range(a, s, q0, q1);
+    const int L = a.cl[s];
     const int T = q1 - q0;
     it[e].q0 = q0;
     it[e].q1 = q1;
@@ -251,15 +265,14 @@ __device__ bool lpt_pick(const PrefillArgs& a, int xcd, int k, int per_xcd, int 
   return true;
 }
 
-// NaN into every element of query heads [h0, h0 + nh) of rows [r0, r1).
+// `v` into every element of query heads [h0, h0 + nh) of rows [r0, r1).
 template <int DT>
-__device__ void nan_rows(void* out, int r0, int r1, int Hq, int h0, int nh, int D) {
-  const float nan = __builtin_nanf("");
+__device__ void fill_rows(void* out, int r0, int r1, int Hq, int h0, int nh, int D, float v) {
   const int per_row = nh * D;
   for (long i = threadIdx.x; i < (long)(r1 - r0) * per_row; i += blockDim.x) {
     const int r = r0 + (int)(i / per_row);
     const int e = (int)(i % per_row);
-    store_elem<DT>(out, ((size_t)r * Hq + h0) * D + e, nan);
+    store_elem<DT>(out, ((size_t)r * Hq + h0) * D + e, v);
   }
 }
 
@@ -510,18 +523,18 @@ __global__ __launch_bounds__(64 * W) void prefill_mfma(PrefillArgs a) {
   if (s >= a.B) return;
 
   if (!picked) {  // (the pick read these already)
-    q0 = a.qs[s];
-    q1 = a.qs[s + 1];
+    seq_range(a, s, q0, q1);
     L = a.cl[s];
   }
   const int T = q1 - q0;
   const int g = a.g;
   if (q0 < 0 || q1 < q0 || q1 > a.N || T > L || (int64_t)L > ((int64_t)a.maxb << a.lbs) || T > a.max_q ||
-      (a.P > 1 && L > a.max_ctx)) {
-    // Unservable sequence: NaN over whatever part of its row range exists.
+      ((a.P > 1 || !a.qs) && L > a.max_ctx)) {
+    // Unservable sequence: NaN over whatever part of its row range exists
+    // (in the decode layout an empty context gives a zero row instead).
     if (tile == a.tiles - 1 && part == 0) {
       const int r0 = min(max(q0, 0), a.N), r1 = min(max(q1, r0), a.N);
-      nan_rows<DT>(a.out, r0, r1, a.Hq, kvh * g, g, D);
+      fill_rows<DT>(a.out, r0, r1, a.Hq, kvh * g, g, D, !a.qs && L == 0 ? 0.f : __builtin_nanf(""));
     }
     return;
   }
@@ -1020,8 +1033,9 @@ template <int DT, int D>
 __global__ __launch_bounds__(256) void prefill_reduce(PrefillArgs a) {
   constexpr int HPB = 256 / (D / 4);  // heads per workgroup
   const int n = blockIdx.x;
-  // the token's sequence: the last s with query_start[s] <= n
-  int lo = 0, hi = a.B - 1;
+  // the token's sequence: the last s with query_start[s] <= n (row n's own
+  // sequence in the decode layout)
+  int lo = a.qs ? 0 : n, hi = a.qs ? a.B - 1 : n;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (a.qs[mid] <= n)
@@ -1030,7 +1044,9 @@ __global__ __launch_bounds__(256) void prefill_reduce(PrefillArgs a) {
       hi = mid - 1;
   }
   const int s = lo;
-  const int q0 = a.qs[s], q1 = a.qs[s + 1], L = a.cl[s];
+  int q0, q1;
+  seq_range(a, s, q0, q1);
+  const int L = a.cl[s];
   const int T = q1 - q0;
   if (n < q0 || n >= q1 || q0 < 0 || q1 > a.N || T > L || (int64_t)L > ((int64_t)a.maxb << a.lbs) ||
       T > a.max_q || L > a.max_ctx)

@@ -68,6 +68,104 @@ extern "C" size_t pa_prefill_workspace_bytes(int num_seqs, int num_tokens, int n
   return pa::prefill_workspace(num_tokens, num_q_heads, head_dim, sp.P).total;
 }
 
+namespace {
+
+// The matrix-core launch (main kernel, then the merge of a split launch)
+// once the arguments are checked and the split and workspace are settled.
+// query_start NULL: one query row per sequence (row s of q and out), the
+// decode layout.
+pa_status_t launch_rows(const char* who, void* out, const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+                        int num_seqs, int num_tokens, int num_q_heads, int num_kv_heads, int head_dim, int lbs,
+                        int num_blocks, int max_blocks_per_seq, int max_query_len, int max_context_len, float scale,
+                        pa_dtype_t dtype, const Split& sp, const pa::PrefillWorkspace& wl, void* workspace,
+                        void* stream) {
+  using namespace pa;
+  PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.kp = static_cast<const char*>(k_pool);
+  a.vp = static_cast<const char*>(v_pool);
+  a.bt = block_tables;
+  a.cl = context_lens;
+  a.qs = query_start;
+  a.B = num_seqs;
+  a.N = num_tokens;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.g = num_q_heads / num_kv_heads;
+  a.D = head_dim;
+  a.num_blocks = num_blocks;
+  a.maxb = max_blocks_per_seq;
+  a.max_q = max_query_len;
+  a.max_ctx = max_context_len;
+  a.lbs = lbs;
+  a.neg_scale = scale < 0.f;
+  a.qscale = fabsf(scale) * 1.4426950408889634f;
+  a.dtype = dtype;
+  a.P = sp.P;
+  a.psteps = sp.psteps;
+  if (wl.total) {
+    char* ws = static_cast<char*>(workspace);
+    a.ws_o = reinterpret_cast<float*>(ws + wl.o_off);
+    a.ws_m = reinterpret_cast<float*>(ws + wl.m_off);
+    a.ws_l = reinterpret_cast<float*>(ws + wl.l_off);
+  }
+  // Kernel variant.  Both default kernels load K/V straight into LDS; the
+  // 8-wavefront one shares each step's K/V between 256 rows and is 2-10%
+  // faster when sequences bring that many rows per KV head, while a step
+  // of mostly short chunks (decode-like single tokens) keeps 128-row
+  // workgroups, two per compute unit (the wide kernel measured 16% slower
+  // there).  Only sizes the caller passes enter the choice: average query
+  // rows per (sequence, KV head) = num_tokens * g / num_seqs.
+  // PA_PREFILL_KERNEL=regs | dma | w8 forces one (read at each call, for
+  // comparisons).
+  a.kind = (int64_t)num_tokens * a.g >= (int64_t)kWideRows * num_seqs ? kPrefillWide : kPrefillDirect;
+  {
+    const char* k = getenv("PA_PREFILL_KERNEL");
+    if (k && strcmp(k, "regs") == 0) a.kind = kPrefillRegs;
+    if (k && strcmp(k, "dma") == 0) a.kind = kPrefillDirect;
+    if (k && strcmp(k, "w8") == 0) a.kind = kPrefillWide;
+  }
+  // Grid: 8 XCDs x ranks per XCD.  In the tile order (split launches, or
+  // more than 64 * kLptPerLane items per XCD) rank r names an item, a row
+  // tile and a partition: ceil(items / 8) x row tiles of max_query_len x
+  // partitions.  In the longest-first order rank k is the XCD's k-th longest
+  // walk and ranks past the XCD's last walk exit at once, so the grid need
+  // only cover the walks that can exist.  Since query_start is non-decreasing
+  // from 0 to num_tokens, the sequences' chunks hold num_tokens tokens in
+  // all, one XCD holds at most m = ceil(Hkv / 8) KV heads of a sequence, and
+  // each of its items rounds up to whole row tiles once: at most
+  // ceil(m * num_tokens * g / R) + ceil(items / 8) walks per XCD.  A step
+  // of mostly single-token sequences beside a few long chunks then launches
+  // about as many workgroups as it has walks instead of max_query_len's
+  // tiles for every sequence.
+  const int64_t rows_per_wg = a.kind == kPrefillWide ? kWideRows : kPrefillRows;
+  const int64_t tiles = ((int64_t)max_query_len * a.g + rows_per_wg - 1) / rows_per_wg;
+  const int64_t items = (int64_t)num_kv_heads * num_seqs;
+  const int64_t per_xcd = (items + 7) / 8;
+  int64_t ranks = per_xcd * tiles * sp.P;
+  if (sp.P == 1 && per_xcd <= 64 * kLptPerLane) {
+    const int64_t m = (num_kv_heads + 7) / 8;
+    const int64_t walks = (m * num_tokens * a.g + rows_per_wg - 1) / rows_per_wg + per_xcd;
+    if (walks < ranks) ranks = walks;
+  }
+  const int64_t grid = 8 * ranks;
+  if (grid > 0x7fffffffLL)
+    return fail(PA_ERR_SHAPE, "%s: launch of %lld workgroups is too large", who, (long long)grid);
+  a.tiles = (int)tiles;
+  a.grid = (int)grid;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  take_main_kernel_events(&a.ev_start, &a.ev_stop);
+  launch_prefill_mfma(a, st);
+  launch_prefill_reduce(a, st);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return PA_OK;
+}
+
+}  // namespace
+
 extern "C" pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, const void* v_pool,
                                   const int32_t* block_tables, const int32_t* context_lens,
                                   const int32_t* query_start, int num_seqs, int num_tokens, int num_q_heads,
@@ -166,85 +264,35 @@ extern "C" pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, 
     return PA_OK;
   }
 
-  PrefillArgs a{};
-  a.out = out;
-  a.q = q;
-  a.kp = static_cast<const char*>(k_pool);
-  a.vp = static_cast<const char*>(v_pool);
-  a.bt = block_tables;
-  a.cl = context_lens;
-  a.qs = query_start;
-  a.B = num_seqs;
-  a.N = num_tokens;
-  a.Hq = num_q_heads;
-  a.Hkv = num_kv_heads;
-  a.g = num_q_heads / num_kv_heads;
-  a.D = head_dim;
-  a.num_blocks = num_blocks;
-  a.maxb = max_blocks_per_seq;
-  a.max_q = max_query_len;
-  a.max_ctx = max_context_len;
-  a.lbs = lbs;
-  a.neg_scale = scale < 0.f;
-  a.qscale = fabsf(scale) * 1.4426950408889634f;
-  a.dtype = dtype;
-  a.P = sp.P;
-  a.psteps = sp.psteps;
-  if (wl.total) {
-    char* ws = static_cast<char*>(workspace);
-    a.ws_o = reinterpret_cast<float*>(ws + wl.o_off);
-    a.ws_m = reinterpret_cast<float*>(ws + wl.m_off);
-    a.ws_l = reinterpret_cast<float*>(ws + wl.l_off);
-  }
-  // Kernel variant.  Both default kernels load K/V straight into LDS; the
-  // 8-wavefront one shares each step's K/V between 256 rows and is 2-10%
-  // faster when sequences bring that many rows per KV head, while a step
-  // of mostly short chunks (decode-like single tokens) keeps 128-row
-  // workgroups, two per compute unit (the wide kernel measured 16% slower
-  // there).  Only sizes the caller passes enter the choice: average query
-  // rows per (sequence, KV head) = num_tokens * g / num_seqs.
-  // PA_PREFILL_KERNEL=regs | dma | w8 forces one (read at each call, for
-  // comparisons).
-  a.kind = (int64_t)num_tokens * a.g >= (int64_t)kWideRows * num_seqs ? kPrefillWide : kPrefillDirect;
-  {
-    const char* k = getenv("PA_PREFILL_KERNEL");
-    if (k && strcmp(k, "regs") == 0) a.kind = kPrefillRegs;
-    if (k && strcmp(k, "dma") == 0) a.kind = kPrefillDirect;
-    if (k && strcmp(k, "w8") == 0) a.kind = kPrefillWide;
-  }
-  // Grid: 8 XCDs x ranks per XCD.  In the tile order (split launches, or
-  // more than 64 * kLptPerLane items per XCD) rank r names an item, a row
-  // tile and a partition: ceil(items / 8) x row tiles of max_query_len x
-  // partitions.  In the longest-first order rank k is the XCD's k-th longest
-  // walk and ranks past the XCD's last walk exit at once, so the grid need
-  // only cover the walks that can exist.  Since query_start is non-decreasing
-  // from 0 to num_tokens, the sequences' chunks hold num_tokens tokens in
-  // all, one XCD holds at most m = ceil(Hkv / 8) KV heads of a sequence, and
-  // each of its items rounds up to whole row tiles once: at most
-  // ceil(m * num_tokens * g / R) + ceil(items / 8) walks per XCD.  A step
-  // of mostly single-token sequences beside a few long chunks then launches
-  // about as many workgroups as it has walks instead of max_query_len's
-  // tiles for every sequence.
-  const int64_t rows_per_wg = a.kind == kPrefillWide ? kWideRows : kPrefillRows;
-  const int64_t tiles = ((int64_t)max_query_len * a.g + rows_per_wg - 1) / rows_per_wg;
-  const int64_t items = (int64_t)num_kv_heads * num_seqs;
-  const int64_t per_xcd = (items + 7) / 8;
-  int64_t ranks = per_xcd * tiles * sp.P;
-  if (sp.P == 1 && per_xcd <= 64 * kLptPerLane) {
-    const int64_t m = (num_kv_heads + 7) / 8;
-    const int64_t walks = (m * num_tokens * a.g + rows_per_wg - 1) / rows_per_wg + per_xcd;
-    if (walks < ranks) ranks = walks;
-  }
-  const int64_t grid = 8 * ranks;
-  if (grid > 0x7fffffffLL)
-    return fail(PA_ERR_SHAPE, "pa_prefill: launch of %lld workgroups is too large", (long long)grid);
-  a.tiles = (int)tiles;
-  a.grid = (int)grid;
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  take_main_kernel_events(&a.ev_start, &a.ev_stop);
-  launch_prefill_mfma(a, st);
-  launch_prefill_reduce(a, st);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "pa_prefill: launch failed: %s", hipGetErrorString(e));
-  return PA_OK;
+  return launch_rows("pa_prefill", out, q, k_pool, v_pool, block_tables, context_lens, query_start, num_seqs,
+                     num_tokens, num_q_heads, num_kv_heads, head_dim, lbs, num_blocks, max_blocks_per_seq,
+                     max_query_len, max_context_len, scale, dtype, sp, wl, workspace, stream);
 }
+
+namespace pa {
+
+size_t decode_rows_workspace(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int max_context_len,
+                             int partition_size) {
+  const Split sp = choose_split(num_seqs, num_q_heads, num_kv_heads, 1, max_context_len, partition_size);
+  return prefill_workspace(num_seqs, num_q_heads, head_dim, sp.P).total;
+}
+
+pa_status_t decode_rows(const char* who, void* out, const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads,
+                        int num_kv_heads, int head_dim, int lbs, int num_blocks, int max_blocks_per_seq,
+                        int max_context_len, int partition_size, float scale, pa_dtype_t dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  const Split sp = choose_split(num_seqs, num_q_heads, num_kv_heads, 1, max_context_len, partition_size);
+  const PrefillWorkspace wl = prefill_workspace(num_seqs, num_q_heads, head_dim, sp.P);
+  if (wl.total > 0) {
+    if (!workspace) return fail(PA_ERR_WORKSPACE, "%s: needs %zu bytes of workspace, got NULL", who, wl.total);
+    if (workspace_bytes < wl.total)
+      return fail(PA_ERR_WORKSPACE, "%s: needs %zu bytes of workspace, got %zu", who, wl.total, workspace_bytes);
+    if (!aligned(workspace, 256)) return fail(PA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", who);
+  }
+  return launch_rows(who, out, q, k_pool, v_pool, block_tables, context_lens, nullptr, num_seqs, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, lbs, num_blocks, max_blocks_per_seq, 1, max_context_len,
+                     scale, dtype, sp, wl, workspace, stream);
+}
+
+}  // namespace pa

@@ -29,7 +29,7 @@ struct PrefillArgs {
   const char* vp;
   const int32_t* bt;
   const int32_t* cl;
-  const int32_t* qs;  // query_start [B + 1]
+  const int32_t* qs;  // query_start [B + 1], or NULL: row s is sequence s's one query row
   int B, N, Hq, Hkv, g, D;
   int num_blocks, maxb, max_q;
   int tiles;      // row tiles per (sequence, KV head) in the launch
@@ -73,6 +73,17 @@ inline PrefillWorkspace prefill_workspace(size_t N, size_t Hq, size_t D, size_t 
 }
 
 void launch_prefill_mfma(const PrefillArgs& a, hipStream_t st);    // fp16 / bf16, main kernel only
+
+// Decode attention (one query row per sequence) through the prefill kernel:
+// pa_decode's route for blocks of 8 slots, which its 16-slot tiles cannot
+// walk.  Arguments checked by the caller except the workspace.
+size_t decode_rows_workspace(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int max_context_len,
+                             int partition_size);
+pa_status_t decode_rows(const char* who, void* out, const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads,
+                        int num_kv_heads, int head_dim, int lbs, int num_blocks, int max_blocks_per_seq,
+                        int max_context_len, int partition_size, float scale, pa_dtype_t dtype, void* workspace,
+                        size_t workspace_bytes, void* stream);
 void launch_prefill_reduce(const PrefillArgs& a, hipStream_t st);  // the merge (nothing when P == 1)
 
 }  // namespace pa

@@ -198,8 +198,10 @@ def test_decode_noalloc_host_validation():
     p = 4096  # never dereferenced: every call below fails on the host
     st = LIB.pa_decode_noalloc(p, p, p, p, p, p, 4096, 64, 8, 128, 16, 1, 512, 8192, ctypes.c_float(0.1), 0, 512, None)
     assert st == 4 and "scratch" in LIB.pa_last_error().decode()
-    st = LIB.pa_decode_noalloc(p, p, p, p, p, p, 4, 8, 2, 128, 8, 1, 8, 64, ctypes.c_float(0.1), 2, 0, None)
-    assert st == 3  # block size 8
+    st = LIB.pa_decode_noalloc(p, p, p, p, p, p, 4, 8, 2, 128, 4, 1, 8, 64, ctypes.c_float(0.1), 2, 0, None)
+    assert st == 3  # block size 4
+    st = LIB.pa_decode_noalloc(p, p, p, p, p, p, 4, 8, 2, 128, 8, 1, 8, 64, ctypes.c_float(0.1), 0, 0, None)
+    assert st == 3  # block size 8 with fp32 KV
     st = LIB.pa_decode_noalloc(None, p, p, p, p, p, 4, 8, 2, 128, 16, 1, 8, 64, ctypes.c_float(0.1), 2, 0, None)
     assert st == 1
     assert LIB.pa_decode_noalloc(p, p, p, p, p, p, 0, 8, 2, 128, 16, 1, 8, 64, ctypes.c_float(0.1), 2, 0, None) == 0

@@ -1,9 +1,11 @@
 """Block sizes other than 16 (PagedAttention and vLLM: Paging the KV Cache
 Like an OS, "Why 16 tokens"; PagedAttention: Virtual Memory for the KV Cache,
 "Block size: why 16").  The decode kernels walk 16-slot tiles, so pa_decode
-takes blocks of 16, 32, 64 or 128 slots; pa_prefill also takes 8; the data
-movement (write, copy, swap) any power of two up to 128.  Every case is the
-whole step against the oracle, whose gather follows the pool's block size."""
+runs blocks of 16, 32, 64 or 128 slots on them and blocks of 8 (16-bit KV)
+through the prefill kernel, which walks token rows; pa_prefill takes 8 to
+128; the data movement (write, copy, swap) any power of two up to 128.  Every
+case is the whole step against the oracle, whose gather follows the pool's
+block size."""
 
 import numpy as np
 import pytest
@@ -21,9 +23,11 @@ def _bits(a):
     return a.view(np.uint16) if a.dtype.itemsize == 2 else a.view(np.uint32)
 
 
-@pytest.mark.parametrize("bs", [16, 32, 64, 128])
-@pytest.mark.parametrize("dtype,hq,hkv,d,psize", [("bf16", 32, 8, 128, 0), ("fp16", 16, 2, 64, 256),
-                                                   ("fp16", 8, 8, 128, 2048), ("fp32", 4, 2, 64, 0)])
+SHAPES = [("bf16", 32, 8, 128, 0), ("fp16", 16, 2, 64, 256), ("fp16", 8, 8, 128, 2048), ("fp32", 4, 2, 64, 0)]
+
+
+@pytest.mark.parametrize("bs,dtype,hq,hkv,d,psize",
+                         [(bs,) + sh for bs in (8, 16, 32, 64, 128) for sh in SHAPES if not (bs == 8 and sh[0] == "fp32")])
 def test_decode_and_write(bs, dtype, hq, hkv, d, psize):
     lens = [1, 15, 16, 17, 33, 127, 128, 129, 300, 1000, 2049]
     w = make_custom(f"bs{bs}", dtype, lens, hq, hkv, d, seed=500 + bs, block_size=bs)
@@ -37,13 +41,74 @@ def test_decode_and_write(bs, dtype, hq, hkv, d, psize):
     assert np.abs(out - want).max() <= TOL[dtype]
 
 
-def test_decode_refuses_blocks_below_16():
+def test_decode_refuses_fp32_blocks_of_8_and_blocks_below_8():
     import paged_kv_cache_117_amd as pa
 
-    w = make_custom("bs8", "bf16", [20, 40], 8, 2, 64, seed=7, block_size=8)
-    g = GpuStep(w)
+    g = GpuStep(make_custom("bs8f32", "fp32", [20, 40], 8, 2, 64, seed=7, block_size=8))
     with pytest.raises(pa.PaError):
         g.run()
+    g = GpuStep(make_custom("bs4", "bf16", [20, 40], 8, 2, 64, seed=7, block_size=4))
+    with pytest.raises(pa.PaError):
+        g.run()
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 32, 8, 128), ("fp16", 64, 8, 128), ("fp16", 40, 40, 64)])
+def test_decode_blocks_of_8_edges_fused_and_noalloc(dtype, hq, hkv, d):
+    """Blocks of 8 slots: L = 0 gives a zero row, L beyond max_context_len
+    and a bad block id NaN rows (as with larger blocks); pa_write_kv_decode
+    equals pa_write_kv + pa_decode bit for bit; pa_decode_noalloc equals
+    pa_decode bit for bit; and the split launch (a short batch, long
+    contexts) and the unsplit one both match the oracle on every row."""
+    import torch
+
+    import paged_kv_cache_117_amd as pa
+
+    lens = [1, 7, 8, 9, 40, 600, 2500, 41]
+    w = make_custom(f"bs8{dtype}{hq}", dtype, lens, hq, hkv, d, seed=31 + hq, block_size=8)
+    print(f"case decode bs=8 {dtype} hq={hq} hkv={hkv} d={d}", flush=True)
+    g = GpuStep(w)
+    kf, vf = g.k.clone(), g.v.clone()
+    for psize in (0, 512):
+        out = to_f64(g.run(partition_size=psize), dtype)
+        st, k, v, want = oracle_step(w)
+        assert np.isfinite(out).all()
+        assert np.abs(out - want).max() <= TOL[dtype]
+    ref = g.out.clone()
+    # the fused step from the same pre-step pools
+    if len(g.st.pairs):
+        pa.copy_blocks(kf, vf, g.pairs)
+    of = pa.write_kv_decode(g.q, kf, vf, g.k_new, g.v_new, g.tables, g.lens, w.scale, w.max_context_len,
+                            partition_size=512)
+    torch.cuda.synchronize()
+    assert torch.equal(of.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(kf.view(torch.int16), g.k.view(torch.int16))
+    assert torch.equal(vf.view(torch.int16), g.v.view(torch.int16))
+    # the allocation-free entry point, twice
+    import ctypes
+
+    from paged_kv_cache_117_amd._lib import LIB
+
+    for _ in range(2):
+        on = torch.full_like(ref, float("nan"))
+        st = LIB.pa_decode_noalloc(on.data_ptr(), g.q.data_ptr(), g.k.data_ptr(), g.v.data_ptr(), g.tables.data_ptr(),
+                                   g.lens.data_ptr(), w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, 8,
+                                   w.num_blocks, g.tables.shape[1], w.max_context_len, ctypes.c_float(w.scale),
+                                   {"fp16": 1, "bf16": 2}[dtype], 512, torch.cuda.current_stream().cuda_stream)
+        assert st == 0, LIB.pa_last_error().decode()
+        torch.cuda.synchronize()
+        assert torch.equal(on.view(torch.int16), ref.view(torch.int16))
+    # edges: zero length, a length past max_context_len, a bad block id
+    lens2 = g.lens.clone()
+    lens2[0] = 0
+    lens2[1] = w.max_context_len + 1
+    tables2 = g.tables.clone()
+    tables2[2, 0] = w.num_blocks + 3
+    o = pa.decode(g.q, g.k, g.v, tables2, lens2, w.scale, w.max_context_len).float().cpu().numpy()
+    assert np.all(o[0] == 0)
+    assert np.all(np.isnan(o[1]))
+    assert np.all(np.isnan(o[2]))
+    keep = list(range(3, len(lens)))
+    assert np.abs(o[keep] - want[keep]).max() <= TOL[dtype]
 
 
 @pytest.mark.parametrize("bs", [8, 32, 128])
