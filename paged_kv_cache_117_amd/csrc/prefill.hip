@@ -116,15 +116,17 @@ __device__ __forceinline__ float max_groups(float x, int x16, int x32) {
 // writes their NaN rows.
 // (kLptPerLane items per lane: the in-kernel order covers up to 256 items per XCD)
 
-// Sequence s's query rows [q0, q1): query_start's entries, or with no
-// query_start one row per sequence (row s), the decode layout.
+// Sequence s's query rows [q0, q1): query_start's entries, or (kRows, the
+// decode layout, no query_start) one row per sequence, row s.  A template
+// argument, so that the prefill instances compile exactly as without it.
+template <bool kRows>
 __device__ __forceinline__ void seq_range(const PrefillArgs& a, int s, int& q0, int& q1) {
-  if (a.qs) {
-    q0 = a.qs[s];
-    q1 = a.qs[s + 1];
-  } else {
+  if constexpr (kRows) {
     q0 = s;
     q1 = s + 1;
+  } else {
+    q0 = a.qs[s];
+    q1 = a.qs[s + 1];
   }
 }
 
@@ -182,8 +184,8 @@ __device__ __forceinline__ int lpt_count(const LptItem& it, int v, int R, int g)
 
 // Rank k of XCD xcd -> (item, tile) and the item's sequence's query_start
 // entries and length as read here; false past the XCD's last workgroup.
-__device__ bool lpt_pick(const PrefillArgs& a, int xcd, int k, int per_xcd, int R, int& item_out, int& tile_out,
-                         int& q0_out, int& q1_out, int& L_out) {
+__device__ bool lpt_pick(const PrefillArgs& a, int xcd, int k, int per_xcd, int R, bool rows, int& item_out,
+                         int& tile_out, int& q0_out, int& q1_out, int& L_out) {
   const int lane = (int)threadIdx.x & 63;
   const int items = a.B * a.Hkv;
   const int c = (per_xcd + 63) >> 6;  // items per lane, lane-major
@@ -196,9 +198,7 @@ __device__ bool lpt_pick(const PrefillArgs& a, int xcd, int k, int per_xcd, int 
     const int item = j * 8 + xcd;
     if (item >= items) continue;
     const int s = item / a.Hkv;
-    int q0, q1;
-    seq_range(a, s, q0, q1);
-    const int L = a.cl[s];
+    const int q0 = rows ? s : a.qs[s], q1 = rows ? s + 1 : a.qs[s + 1], L = a.cl[s];
     const int T = q1 - q0;
     it[e].q0 = q0;
     it[e].q1 = q1;
@@ -265,14 +265,15 @@ __device__ bool lpt_pick(const PrefillArgs& a, int xcd, int k, int per_xcd, int 
   return true;
 }
 
-// `v` into every element of query heads [h0, h0 + nh) of rows [r0, r1).
-template <int DT>
-__device__ void fill_rows(void* out, int r0, int r1, int Hq, int h0, int nh, int D, float v) {
+// NaN (kZero: zero) into every element of query heads [h0, h0 + nh) of rows [r0, r1).
+template <int DT, bool kZero = false>
+__device__ void nan_rows(void* out, int r0, int r1, int Hq, int h0, int nh, int D) {
+  const float nan = kZero ? 0.f : __builtin_nanf("");
   const int per_row = nh * D;
   for (long i = threadIdx.x; i < (long)(r1 - r0) * per_row; i += blockDim.x) {
     const int r = r0 + (int)(i / per_row);
     const int e = (int)(i % per_row);
-    store_elem<DT>(out, ((size_t)r * Hq + h0) * D + e, v);
+    store_elem<DT>(out, ((size_t)r * Hq + h0) * D + e, nan);
   }
 }
 
@@ -453,7 +454,7 @@ __device__ __forceinline__ void short_rows(const PrefillArgs& a, int s, int kvh,
 // lane i of an instruction filling bytes 16 i of its 1 KiB), and the PV
 // operand is read with the transposing LDS read; no staging registers, no
 // staging ALU work.
-template <int DT, int D, int NC, bool kDma, int W>
+template <int DT, int D, int NC, bool kDma, int W, bool kRows>
 __global__ __launch_bounds__(64 * W) void prefill_mfma(PrefillArgs a) {
   constexpr int ROW = D;                     // LDS row of K, elements (16-byte chunks XOR-swizzled)
   constexpr int KS = D / 32;                 // QK k-steps over the head dim
@@ -510,7 +511,7 @@ __global__ __launch_bounds__(64 * W) void prefill_mfma(PrefillArgs a) {
   int q0 = 0, q1 = 0, L = 0;
   const bool picked = a.P == 1 && per_xcd <= 64 * kLptPerLane;
   if (picked) {
-    if (!lpt_pick(a, xcd, local, per_xcd, R, item, tile, q0, q1, L)) return;
+    if (!lpt_pick(a, xcd, local, per_xcd, R, kRows, item, tile, q0, q1, L)) return;
   } else {
     item = (local % per_xcd) * 8 + xcd;
     const int tp = local / per_xcd;
@@ -523,18 +524,21 @@ __global__ __launch_bounds__(64 * W) void prefill_mfma(PrefillArgs a) {
   if (s >= a.B) return;
 
   if (!picked) {  // (the pick read these already)
-    seq_range(a, s, q0, q1);
+    seq_range<kRows>(a, s, q0, q1);
     L = a.cl[s];
   }
   const int T = q1 - q0;
   const int g = a.g;
   if (q0 < 0 || q1 < q0 || q1 > a.N || T > L || (int64_t)L > ((int64_t)a.maxb << a.lbs) || T > a.max_q ||
-      ((a.P > 1 || !a.qs) && L > a.max_ctx)) {
+      ((a.P > 1 || kRows) && L > a.max_ctx)) {
     // Unservable sequence: NaN over whatever part of its row range exists
     // (in the decode layout an empty context gives a zero row instead).
     if (tile == a.tiles - 1 && part == 0) {
       const int r0 = min(max(q0, 0), a.N), r1 = min(max(q1, r0), a.N);
-      fill_rows<DT>(a.out, r0, r1, a.Hq, kvh * g, g, D, !a.qs && L == 0 ? 0.f : __builtin_nanf(""));
+      if (kRows && L == 0)
+        nan_rows<DT, true>(a.out, r0, r1, a.Hq, kvh * g, g, D);
+      else
+        nan_rows<DT>(a.out, r0, r1, a.Hq, kvh * g, g, D);
     }
     return;
   }
@@ -1029,13 +1033,13 @@ __global__ __launch_bounds__(64 * W) void prefill_mfma(PrefillArgs a) {
 // left alone.
 constexpr int kMergeBatch = 8;
 
-template <int DT, int D>
+template <int DT, int D, bool kRows>
 __global__ __launch_bounds__(256) void prefill_reduce(PrefillArgs a) {
   constexpr int HPB = 256 / (D / 4);  // heads per workgroup
   const int n = blockIdx.x;
   // the token's sequence: the last s with query_start[s] <= n (row n's own
   // sequence in the decode layout)
-  int lo = a.qs ? 0 : n, hi = a.qs ? a.B - 1 : n;
+  int lo = kRows ? n : 0, hi = kRows ? n : a.B - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (a.qs[mid] <= n)
@@ -1045,7 +1049,7 @@ __global__ __launch_bounds__(256) void prefill_reduce(PrefillArgs a) {
   }
   const int s = lo;
   int q0, q1;
-  seq_range(a, s, q0, q1);
+  seq_range<kRows>(a, s, q0, q1);
   const int L = a.cl[s];
   const int T = q1 - q0;
   if (n < q0 || n >= q1 || q0 < 0 || q1 > a.N || T > L || (int64_t)L > ((int64_t)a.maxb << a.lbs) ||
@@ -1100,17 +1104,25 @@ __global__ __launch_bounds__(256) void prefill_reduce(PrefillArgs a) {
 template <int DT, int D, bool kMerge>
 void launch_nc(const PrefillArgs& a, hipStream_t st) {
   constexpr int HPB = 256 / (D / 4);
-  if (!kMerge && a.kind == kPrefillWide)
-    hipExtLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC, true, kWideWaves>), dim3(a.grid), dim3(64 * kWideWaves), 0,
+  // (no query_start: the decode layout, on the 4-wavefront direct-load kernel only)
+  const bool rows = a.qs == nullptr;
+  if (!kMerge && rows)
+    hipExtLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC, true, kWaves, true>), dim3(a.grid), dim3(64 * kWaves), 0,
                           st, static_cast<hipEvent_t>(a.ev_start), static_cast<hipEvent_t>(a.ev_stop), 0, a);
+  else if (!kMerge && a.kind == kPrefillWide)
+    hipExtLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC, true, kWideWaves, false>), dim3(a.grid),
+                          dim3(64 * kWideWaves), 0, st, static_cast<hipEvent_t>(a.ev_start),
+                          static_cast<hipEvent_t>(a.ev_stop), 0, a);
   else if (!kMerge && a.kind == kPrefillDirect)
-    hipExtLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC, true, kWaves>), dim3(a.grid), dim3(64 * kWaves), 0, st,
-                          static_cast<hipEvent_t>(a.ev_start), static_cast<hipEvent_t>(a.ev_stop), 0, a);
+    hipExtLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC, true, kWaves, false>), dim3(a.grid), dim3(64 * kWaves), 0,
+                          st, static_cast<hipEvent_t>(a.ev_start), static_cast<hipEvent_t>(a.ev_stop), 0, a);
   else if (!kMerge)
-    hipExtLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC, false, kWaves>), dim3(a.grid), dim3(64 * kWaves), 0, st,
-                          static_cast<hipEvent_t>(a.ev_start), static_cast<hipEvent_t>(a.ev_stop), 0, a);
+    hipExtLaunchKernelGGL((prefill_mfma<DT, D, kPrefillNC, false, kWaves, false>), dim3(a.grid), dim3(64 * kWaves), 0,
+                          st, static_cast<hipEvent_t>(a.ev_start), static_cast<hipEvent_t>(a.ev_stop), 0, a);
+  else if (a.P > 1 && rows)
+    hipLaunchKernelGGL((prefill_reduce<DT, D, true>), dim3(a.N, (a.Hq + HPB - 1) / HPB), dim3(256), 0, st, a);
   else if (a.P > 1)
-    hipLaunchKernelGGL((prefill_reduce<DT, D>), dim3(a.N, (a.Hq + HPB - 1) / HPB), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_reduce<DT, D, false>), dim3(a.N, (a.Hq + HPB - 1) / HPB), dim3(256), 0, st, a);
 }
 
 template <int DT, bool kMerge>

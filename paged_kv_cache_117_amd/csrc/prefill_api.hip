@@ -127,6 +127,7 @@ pa_status_t launch_rows(const char* who, void* out, const void* q, const void* k
     if (k && strcmp(k, "dma") == 0) a.kind = kPrefillDirect;
     if (k && strcmp(k, "w8") == 0) a.kind = kPrefillWide;
   }
+  if (!query_start) a.kind = kPrefillDirect;  // the decode layout has one instance
   // Grid: 8 XCDs x ranks per XCD.  In the tile order (split launches, or
   // more than 64 * kLptPerLane items per XCD) rank r names an item, a row
   // tile and a partition: ceil(items / 8) x row tiles of max_query_len x
